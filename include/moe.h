@@ -1,0 +1,302 @@
+/*
+ * moe.h - C ABI of the routed Mixture-of-Experts layer for MI355X (gfx950).
+ *
+ * The layer this library computes is the sparse expert execution the
+ * FreeToken pages describe: each token is routed to a few of many experts,
+ * only those experts run, and the layer output is the sum of their weighted
+ * partial results ("FreeToken 753b Model Explained", section of the same
+ * name).  Expert weights are reached through an expert-cache slot table; a
+ * global LRU cache in GPU memory is filled from a pinned host expert pool;
+ * the partial sums of two disjoint expert subsets merge exactly
+ * (explainx.ai guide, "Decode: decide whether to move an expert or compute
+ * where it lives"; futuresignalnews.com article, "1. Bandwidth-Adaptive
+ * Execution (The q* Policy)" and "2. Semantic-Aware Caching").
+ *
+ * Conventions for every call
+ *   - Return value: MOE_OK (0) or a negative MOE_E* status; nothing aborts or
+ *     throws across this boundary.  moe_last_error() returns a thread-local
+ *     text for the last failing call on the calling thread.
+ *   - Pointers named d_* or documented "device" are device memory of the
+ *     current HIP device; "host" pointers are CPU memory.  The caller owns
+ *     every buffer; no call keeps a pointer past its return except the cache
+ *     object (see moe_cache_create).
+ *   - Device work is enqueued on the caller's stream (a hipStream_t passed as
+ *     void*; NULL = the null stream) and the call returns without
+ *     synchronising.  A fault inside a kernel surfaces at the caller's next
+ *     synchronisation, not as this call's status.
+ *   - No call allocates device memory.  Scratch comes from a caller-provided
+ *     workspace sized by moe_workspace_bytes().
+ *   - Stateless calls are reentrant; a moe_planner / moe_cache object must
+ *     not be used from two threads at once.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ------------------------------------------------------ */
+#define MOE_OK 0
+#define MOE_EINVAL (-1)       /* bad argument: null pointer, size, shape     */
+#define MOE_EUNSUPPORTED (-2) /* weight type / shape / device not supported  */
+#define MOE_EHIP (-3)         /* HIP runtime error (text in moe_last_error)  */
+#define MOE_EWORKSPACE (-4)   /* workspace missing or too small              */
+#define MOE_ECACHE (-5)       /* cache: invalid plan or not enough slots     */
+
+/* ---- formats ----------------------------------------------------------- */
+/* Expert / router weight formats.
+ *   F32   : IEEE binary32 (router only).
+ *   BF16  : bfloat16 (upper half of binary32), round-to-nearest-even.
+ *   MXFP4 : OCP MX FP4: 4-bit e2m1 codes, two per byte (element 2j in the low
+ *           nibble of byte j), plus one e8m0 scale byte (2^(s-127)) per 32
+ *           consecutive elements along the reduction axis K.  The pages list
+ *           MXFP4 among the engine's expert formats ("FreeToken 753b Model
+ *           Explained", "Performance Benchmarks and Model Fit") without its
+ *           bit layout; the OCP MX v1.0 definitions are used. */
+#define MOE_WTYPE_F32 0
+#define MOE_WTYPE_BF16 1
+#define MOE_WTYPE_MXFP4 2
+
+/* Layer description.  hidden (H) and inter (I) must be multiples of 32
+ * (MXFP4 blocks) and of 8 (BF16 16-byte vectors); 1 <= top_k <= n_experts
+ * <= 1024. */
+typedef struct moe_desc {
+  int32_t hidden;       /* H: token width                                    */
+  int32_t inter;        /* I: expert SwiGLU intermediate width               */
+  int32_t n_experts;    /* E: routed experts                                 */
+  int32_t top_k;        /* k: experts per token                              */
+  int32_t has_shared;   /* 1: a shared expert also runs on every token, w=1  */
+  int32_t renorm_topk;  /* 1: divide the k gate weights by their sum         */
+  int32_t wtype;        /* expert weights: MOE_WTYPE_BF16 or MOE_WTYPE_MXFP4 */
+  int32_t router_wtype; /* router weights: MOE_WTYPE_F32 or MOE_WTYPE_BF16   */
+} moe_desc;
+
+/* One expert is one contiguous block of moe_expert_layout()'s *bytes, laid
+ * out identically in the pinned host pool and in a device slot (the pages'
+ * direct host loading into the final layout, "FreeToken 753b Model
+ * Explained", "How MoE Paging and Caching Work").  Sections, in order:
+ *   BF16 : [0] gate [I][H], [1] up [I][H], [2] down [H][I]   (row-major,
+ *          K contiguous); offsets[3..5] = 0.
+ *   MXFP4: [0] gate codes [I][H/2], [1] gate scales [I][H/32],
+ *          [2] up codes [I][H/2],   [3] up scales [I][H/32],
+ *          [4] down codes [H][I/2], [5] down scales [H][I/32].
+ * Section offsets are 16-byte aligned; *bytes is a multiple of 256.
+ * Returns MOE_EINVAL for a bad descriptor. */
+int moe_expert_layout(const moe_desc* desc, size_t offsets[6], size_t* bytes);
+
+/* Workspace bytes a call needs (0 if none).  mode: 0 = moe_route,
+ * 1 = moe_decode, 2 = moe_prefill, for T tokens.  Returns 0 and sets the
+ * error text for an invalid descriptor or T. */
+#define MOE_MODE_ROUTE 0
+#define MOE_MODE_DECODE 1
+#define MOE_MODE_PREFILL 2
+size_t moe_workspace_bytes(const moe_desc* desc, int32_t T, int32_t mode);
+
+/* Largest T moe_decode accepts (larger batches go through moe_prefill). */
+#define MOE_DECODE_MAX_T 64
+
+/* ---- router ------------------------------------------------------------ */
+/* moe_route: z = W_r x (fp32 accumulation of exact products), p = softmax(z)
+ * over all E experts (fp32), ids = the top_k experts by p in descending order
+ * (ties to the lower id), w = p[ids] (divided by their sum if renorm_topk).
+ * Routing picks a few experts per token and layer ("FreeToken 753b Model
+ * Explained"); the gate function is not on the pages, softmax then top-k is
+ * the reading used.
+ *   x        device, [T][H] BF16 row-major
+ *   w_router device, [E][H] in desc->router_wtype
+ *   ids      device out, [T][k] int32
+ *   w        device out, [T][k] float
+ *   ws       device workspace of moe_workspace_bytes(desc, T, MOE_MODE_ROUTE)
+ * T >= 1 (T == 0 is a no-op returning MOE_OK). */
+int moe_route(const moe_desc* desc, const void* x, const void* w_router,
+              int32_t T, int32_t* ids, float* w, void* ws, size_t ws_bytes,
+              void* stream);
+
+/* ---- expert FFNs + weighted combine ------------------------------------ */
+/* moe_decode: y[t] = sum over j of w[t][j] * FFN_{ids[t][j]}(x[t])
+ *                    (+ FFN_shared(x[t]) when desc->has_shared),
+ * FFN_e(x) = W_down (silu(W_gate x) * (W_up x)), silu(z) = z / (1 + e^-z),
+ * fp32 accumulation, x as given (BF16), h in fp32.  Only experts with a slot
+ * contribute: y is the partial sum over the resident subset (the GPU side of
+ * the pages' exact split); non-resident pairs are skipped.  Terms are added
+ * in a fixed order (routed experts in first-appearance order, then shared),
+ * so results are deterministic.
+ *   x              device [T][H] BF16;   1 <= T <= MOE_DECODE_MAX_T
+ *   ids, w         device [T][k] (from moe_route or the caller)
+ *   slot_of_expert device [E] int32: slot holding expert e, -1 = not
+ *                  resident; NULL = identity (expert e in slot e)
+ *   slot_pool      device base; slot s starts at slot_pool + s * bytes
+ *                  (bytes from moe_expert_layout, 256-byte aligned)
+ *   shared_expert  device block in the same layout, or NULL (required iff
+ *                  desc->has_shared)
+ *   y              device out [T][H] float, overwritten
+ *   ws             device workspace, moe_workspace_bytes(.., MOE_MODE_DECODE)
+ * ids outside [0, E) are an error the kernels cannot report: they are
+ * skipped. */
+int moe_decode(const moe_desc* desc, const void* x, int32_t T,
+               const int32_t* ids, const float* w,
+               const int32_t* slot_of_expert, const void* slot_pool,
+               const void* shared_expert, float* y, void* ws, size_t ws_bytes,
+               void* stream);
+
+/* moe_prefill: the same layer for long token batches (MXFP4 weights only).
+ * Pairs are counting-sorted by expert; x and h are quantised to MXFP4 on the
+ * fly (x along H, h along I, same encoder as moe_quantize_mxfp4) and both
+ * expert products run on the scaled FP4 matrix cores with fp32
+ * accumulation.  Prefill routes nearly every expert (explainx.ai guide,
+ * "Prefill: load almost every expert without idling the GPU").  Arguments as
+ * moe_decode; 1 <= T <= 65536; ws of moe_workspace_bytes(.., PREFILL). */
+int moe_prefill(const moe_desc* desc, const void* x, int32_t T,
+                const int32_t* ids, const float* w,
+                const int32_t* slot_of_expert, const void* slot_pool,
+                const void* shared_expert, float* y, void* ws, size_t ws_bytes,
+                void* stream);
+
+/* moe_merge_partials: y = a + b elementwise over n floats (device).  The
+ * exact merge of two partial sums computed over disjoint expert subsets
+ * (explainx.ai guide, "Decode: ..."; ainewsfeed.tech article, third
+ * paragraph).  y may alias a or b. */
+int moe_merge_partials(const float* a, const float* b, float* y, size_t n,
+                       void* stream);
+
+/* ---- formats ----------------------------------------------------------- */
+/* moe_quantize_mxfp4: src [rows][K] float (row stride src_ld floats) ->
+ * codes [rows][K/2], scales [rows][K/32] (device).  Per 32-block: a = max|v|;
+ * a == 0 -> scale 0, codes 0; else X = floor(log2 a) - 2 clamped to
+ * [-127, 127], scale byte X + 127, codes = v / 2^X rounded to e2m1 with
+ * round-to-nearest-even, saturating at 6, sign kept.  K % 32 == 0. */
+int moe_quantize_mxfp4(const float* src, int32_t rows, int32_t K,
+                       int64_t src_ld, uint8_t* codes, uint8_t* scales,
+                       void* stream);
+
+/* moe_debug_dequant_mxfp4: n_blocks MXFP4 blocks (codes 16 B each, one scale
+ * byte each) -> 32 * n_blocks floats, value e2m1(code) * 2^(s-127) computed
+ * by the same in-register decoder the expert kernels use.  Test hook. */
+int moe_debug_dequant_mxfp4(const uint8_t* codes, const uint8_t* scales,
+                            int64_t n_blocks, float* out, void* stream);
+
+/* moe_debug_mfma_fp4_tile: D = A . B^T for one 16 x 128 MXFP4 tile of A
+ * (a_codes [16][64] bytes, a_scales [16][4]) and of B (same shapes), out
+ * [16][16] float row-major, computed by one wave through the fragment
+ * loaders and scaled FP4 matrix instruction that moe_prefill uses.  Test
+ * hook for the operand and result lane layouts. */
+int moe_debug_mfma_fp4_tile(const uint8_t* a_codes, const uint8_t* a_scales,
+                            const uint8_t* b_codes, const uint8_t* b_scales,
+                            float* out, void* stream);
+
+/* ---- q* split ---------------------------------------------------------- */
+/* Number of the m cache misses to fill into GPU slots so that the PCIe fills
+ * (rate b_pcie) and host-side execution of the rest (rate b_host) finish
+ * together: argmin over q in [0, m] of max(q / b_pcie, (m - q) / b_host),
+ * ties to the larger q.  The pages name this policy q* and say it is chosen
+ * from profiled bandwidths so that neither path idles (futuresignalnews.com,
+ * "1. Bandwidth-Adaptive Execution (The q* Policy)"; explainx.ai, "Decode:
+ * ..."); the formula is the reading used.  Returns -1 for m < 0 or
+ * non-positive rates. */
+int32_t moe_qstar(int32_t m, double b_pcie, double b_host);
+
+/* ---- global LRU planner (host only, no HIP calls) ---------------------- */
+/* A global LRU over (layer, expert) keys and n_slots numbered slots: one
+ * cache shared by every layer, following the router ("FreeToken 753b Model
+ * Explained", "How MoE Paging and Caching Work").  Per plan call (one layer,
+ * one step): the step's selected set S is the distinct ids in
+ * first-appearance order; hits refresh recency in S order; misses are ranked
+ * by summed gate weight (descending, ties to the lower id); the first q are
+ * filled, each into the lowest empty slot, else the least recently used slot
+ * whose key is not in S; unfilled misses stay out of the cache.  q is
+ * clamped to [0, min(misses, n_slots - hits)]; q < 0 means q* from the
+ * planner's bandwidths (moe_planner_set_bandwidths). */
+#define MOE_PLAN_MAX 256
+typedef struct moe_plan {
+  int32_t layer;
+  int32_t n_selected;                    /* |S|                              */
+  int32_t n_hits, n_misses;
+  int32_t q;                             /* fills actually planned           */
+  int32_t n_host;                        /* misses left to the host side     */
+  int32_t selected[MOE_PLAN_MAX];        /* S, first-appearance order        */
+  int32_t hits[MOE_PLAN_MAX];            /* S order                          */
+  int32_t misses[MOE_PLAN_MAX];          /* S order                          */
+  int32_t fill_expert[MOE_PLAN_MAX];     /* ranked order, q entries          */
+  int32_t fill_slot[MOE_PLAN_MAX];
+  int32_t victim_layer[MOE_PLAN_MAX];    /* -1 when the slot was empty       */
+  int32_t victim_expert[MOE_PLAN_MAX];
+  int32_t host_expert[MOE_PLAN_MAX];     /* ranked order, n_host entries     */
+  int32_t hit_slot[MOE_PLAN_MAX];        /* slot of each hit                 */
+} moe_plan;
+
+typedef struct moe_planner moe_planner;
+/* n_layers, n_experts >= 1; 1 <= n_slots. The cache starts cold. */
+int moe_planner_create(moe_planner** out, int32_t n_layers, int32_t n_experts,
+                       int32_t n_slots);
+void moe_planner_destroy(moe_planner* p);
+int moe_planner_set_bandwidths(moe_planner* p, double b_pcie, double b_host);
+/* ids/w: host, n entries (a step's T*k pairs); at most MOE_PLAN_MAX distinct
+ * ids (else MOE_ECACHE); ids outside [0, n_experts) -> MOE_EINVAL.  On error
+ * the planner state is unchanged. */
+int moe_planner_plan(moe_planner* p, int32_t layer, const int32_t* ids,
+                     const float* w, int32_t n, int32_t q, moe_plan* plan);
+/* Undo the last successful moe_planner_plan (one level). */
+int moe_planner_rollback(moe_planner* p);
+/* slot of each expert of `layer` (-1 = not resident), host out [n_experts] */
+int moe_planner_slot_table(const moe_planner* p, int32_t layer, int32_t* out);
+
+/* ---- expert cache: planner + async fills from a pinned host pool ------- */
+/* moe_cache_create keeps the caller's pointers until moe_cache_destroy:
+ *   host_pool          pinned host memory, [n_layers][n_experts] blocks of
+ *                      expert_bytes (hipHostMalloc / torch pin_memory)
+ *   dev_slot_pool      device, n_slots blocks of expert_bytes
+ *   dev_slot_of_expert device [n_layers][n_experts] int32, set to -1 here
+ *                      (on the null stream) and kept equal to the planner's
+ *                      table by cache_fill (ordered on the compute stream)
+ * It creates HIP events (one per slot plus one per fill batch). */
+typedef struct moe_cache moe_cache;
+int moe_cache_create(moe_cache** out, const void* host_pool, int32_t n_layers,
+                     int32_t n_experts, size_t expert_bytes,
+                     void* dev_slot_pool, int32_t n_slots,
+                     int32_t* dev_slot_of_expert);
+void moe_cache_destroy(moe_cache* c);
+int moe_cache_set_bandwidths(moe_cache* c, double b_pcie, double b_host);
+/* Plan one step of one layer (see the planner above). */
+int moe_cache_plan(moe_cache* c, int32_t layer, const int32_t* ids_host,
+                   const float* w_host, int32_t n, int32_t q, moe_plan* plan);
+/* cache_fill: for each planned fill, side_stream waits until the victim
+ * slot's last use (recorded by moe_cache_release) has finished, then one
+ * hipMemcpyAsync copies the expert's block from the pinned host pool into its
+ * slot; compute_stream then waits for the copies and the device slot table
+ * is updated on compute_stream (victims -> -1, fills -> slot).  Returns
+ * without waiting.  Miss option "copy over PCIe, run on the GPU, keep
+ * cached" (explainx.ai guide, "Decode: ...").  On failure the planner is
+ * rolled back, slots whose copy may have started are marked empty, and
+ * MOE_EHIP / MOE_ECACHE is returned. */
+int cache_fill(moe_cache* c, const moe_plan* plan, void* side_stream,
+               void* compute_stream);
+/* Record, on compute_stream, the last use of every slot the plan reads
+ * (hits and fills); call after the step's moe_decode is enqueued. */
+int moe_cache_release(moe_cache* c, const moe_plan* plan, void* compute_stream);
+/* Test hook: make the next n cache_fill calls fail before any copy. */
+int moe_cache_debug_fail_fills(moe_cache* c, int32_t n);
+const moe_planner* moe_cache_planner(const moe_cache* c);
+
+/* ---- bandwidth probe --------------------------------------------------- */
+/* Measures pinned host->device copy bandwidth (bytes / s) from `pinned_host`
+ * into `dev` (both >= bytes) on `stream`, and host-memory streaming read
+ * bandwidth over `pinned_host` with `threads` CPU threads (0 = all), best of
+ * `reps`.  Blocks the caller.  The pages profile exactly these two rates
+ * before splitting misses ("FreeToken 753b Model Explained", "Measure System
+ * Bandwidth"). */
+int moe_probe_bandwidths(const void* pinned_host, void* dev, size_t bytes,
+                         int32_t reps, int32_t threads, void* stream,
+                         double* b_pcie, double* b_host);
+
+/* ---- misc -------------------------------------------------------------- */
+const char* moe_last_error(void);
+int32_t moe_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_H */

@@ -105,21 +105,29 @@ def e2m1_round(r):
     sign bit is the sign of r (so -0.0 and small negatives give code 8).
     """
     r = np.asarray(r, dtype=np.float64)
-    grid = np.array(_E2M1_MAGNITUDE, dtype=np.float64)
+    flat = r.reshape(-1)
+    out = np.empty(flat.shape, dtype=np.uint8)
+    step = 1 << 15          # work in cache-sized pieces; no effect on results
+    for lo in range(0, flat.size, step):
+        out[lo:lo + step] = _e2m1_round_piece(flat[lo:lo + step])
+    return out.reshape(r.shape)
+
+
+def _e2m1_round_piece(r):
     mag = np.minimum(np.abs(r), 6.0)
-    # distance to every grid point; pick the closest, ties -> even code
-    dist = np.abs(mag[..., None] - grid)
-    best = np.min(dist, axis=-1, keepdims=True)
-    is_best = dist == best
-    even = (np.arange(8) & 1) == 0
-    # prefer an even code among the tied candidates
-    cand_even = is_best & even
-    pick_even = np.any(cand_even, axis=-1)
-    idx_even = np.argmax(cand_even, axis=-1)
-    idx_any = np.argmax(is_best, axis=-1)
-    idx = np.where(pick_even, idx_even, idx_any)
-    sign = np.signbit(r).astype(np.int64)
-    return (idx | (sign << 3)).astype(np.uint8)
+    # scan the 8 grid magnitudes keeping the closest; on an exact tie the
+    # candidate with the even code (mantissa bit 0) wins
+    best_idx = np.zeros(mag.shape, dtype=np.uint8)
+    best_d = np.abs(mag - _E2M1_MAGNITUDE[0])
+    for g in range(1, 8):
+        d = np.abs(mag - _E2M1_MAGNITUDE[g])
+        take = d < best_d
+        if g % 2 == 0:
+            take |= (d == best_d) & ((best_idx & 1) == 1)
+        best_idx[take] = g
+        best_d[take] = d[take]
+    sign = np.signbit(r).astype(np.uint8)
+    return best_idx | (sign << 3)
 
 
 def mxfp4_encode(v):

@@ -1,0 +1,268 @@
+// api.cpp - C ABI entry points: argument checks, workspace carve-up, and the
+// launches of the gfx950 kernels.  Declarations and contracts: include/moe.h.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "../../include/moe.h"
+#include "error.hpp"
+#include "kernels.hpp"
+
+namespace moe {
+
+int hip_status(hipError_t err, const char* what) {
+  if (err == hipSuccess) return MOE_OK;
+  return set_error(MOE_EHIP, "%s: %s (%s)", what, hipGetErrorName(err), hipGetErrorString(err));
+}
+
+}  // namespace moe
+
+using moe::hip_status;
+using moe::set_error;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t v) { return (v + kAlign - 1) & ~(kAlign - 1); }
+
+int check_desc(const moe_desc* d) {
+  if (!d) return set_error(MOE_EINVAL, "desc is null");
+  if (d->hidden <= 0 || d->inter <= 0 || d->hidden % 32 || d->inter % 32)
+    return set_error(MOE_EINVAL, "hidden (%d) and inter (%d) must be positive multiples of 32",
+                     d->hidden, d->inter);
+  if (d->n_experts < 1 || d->n_experts > 1024)
+    return set_error(MOE_EINVAL, "n_experts %d outside [1, 1024]", d->n_experts);
+  if (d->top_k < 1 || d->top_k > d->n_experts || d->top_k > 64)
+    return set_error(MOE_EINVAL, "top_k %d outside [1, min(E, 64)]", d->top_k);
+  if (d->wtype != MOE_WTYPE_BF16 && d->wtype != MOE_WTYPE_MXFP4)
+    return set_error(MOE_EUNSUPPORTED, "expert weight type %d not supported", d->wtype);
+  if (d->router_wtype != MOE_WTYPE_BF16 && d->router_wtype != MOE_WTYPE_F32)
+    return set_error(MOE_EUNSUPPORTED, "router weight type %d not supported", d->router_wtype);
+  if (d->has_shared != 0 && d->has_shared != 1)
+    return set_error(MOE_EINVAL, "has_shared must be 0 or 1");
+  return MOE_OK;
+}
+
+void layout(const moe_desc* d, size_t off[6], size_t* bytes) {
+  const size_t H = d->hidden, I = d->inter;
+  if (d->wtype == MOE_WTYPE_BF16) {
+    off[0] = 0;
+    off[1] = I * H * 2;
+    off[2] = 2 * I * H * 2;
+    off[3] = off[4] = off[5] = 0;
+    *bytes = align_up(3 * I * H * 2);
+  } else {
+    const size_t cg = I * H / 2, sg = I * H / 32;
+    off[0] = 0;
+    off[1] = cg;
+    off[2] = cg + sg;
+    off[3] = 2 * cg + sg;
+    off[4] = 2 * cg + 2 * sg;
+    off[5] = 3 * cg + 2 * sg;
+    *bytes = align_up(3 * cg + 3 * sg);
+  }
+}
+
+struct PrefillWs {
+  size_t xq_codes, xq_scales, chunk_counts, seg_start, tiles, sorted_pair, hq_codes, hq_scales,
+      partial, total;
+  int n_chunks, max_tiles, n_pairs;
+};
+
+PrefillWs prefill_ws(const moe_desc* d, int T) {
+  PrefillWs w;
+  const size_t H = d->hidden, I = d->inter, E = d->n_experts, k = d->top_k;
+  w.n_pairs = (int)(T * k + (d->has_shared ? T : 0));
+  w.n_chunks = (w.n_pairs + moe::kPrefillChunk - 1) / moe::kPrefillChunk;
+  w.max_tiles = moe::prefill_max_tiles(T, (int)k, (int)E);
+  size_t o = 0;
+  w.xq_codes = o; o = align_up(o + T * H / 2);
+  w.xq_scales = o; o = align_up(o + T * H / 32);
+  w.chunk_counts = o; o = align_up(o + (size_t)w.n_chunks * (E + 1) * 4);
+  w.seg_start = o; o = align_up(o + (E + 2) * 4);
+  w.tiles = o; o = align_up(o + (1 + 2 * (size_t)w.max_tiles) * 4);
+  w.sorted_pair = o; o = align_up(o + (size_t)w.n_pairs * 4);
+  w.hq_codes = o; o = align_up(o + (size_t)w.n_pairs * I / 2);
+  w.hq_scales = o; o = align_up(o + (size_t)w.n_pairs * I / 32);
+  w.partial = o; o = align_up(o + (size_t)T * (k + 1) * H * 4);
+  w.total = o;
+  return w;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+}  // namespace
+
+extern "C" {
+
+int moe_expert_layout(const moe_desc* desc, size_t offsets[6], size_t* bytes) {
+  int st = check_desc(desc);
+  if (st) return st;
+  if (!offsets || !bytes) return set_error(MOE_EINVAL, "null output pointer");
+  layout(desc, offsets, bytes);
+  return MOE_OK;
+}
+
+size_t moe_workspace_bytes(const moe_desc* desc, int32_t T, int32_t mode) {
+  if (check_desc(desc)) return 0;
+  if (T < 0) { set_error(MOE_EINVAL, "T < 0"); return 0; }
+  switch (mode) {
+    case MOE_MODE_ROUTE:
+      return align_up((size_t)T * desc->n_experts * 4);
+    case MOE_MODE_DECODE:
+      return align_up((size_t)(T * desc->top_k + T) * desc->inter * 4);
+    case MOE_MODE_PREFILL:
+      return prefill_ws(desc, T).total;
+    default:
+      set_error(MOE_EINVAL, "unknown mode %d", mode);
+      return 0;
+  }
+}
+
+int moe_route(const moe_desc* desc, const void* x, const void* w_router, int32_t T,
+              int32_t* ids, float* w, void* ws, size_t ws_bytes, void* stream) {
+  int st = check_desc(desc);
+  if (st) return st;
+  if (T == 0) return MOE_OK;
+  if (T < 0) return set_error(MOE_EINVAL, "T < 0");
+  if (!x || !w_router || !ids || !w) return set_error(MOE_EINVAL, "null pointer");
+  const size_t need = moe_workspace_bytes(desc, T, MOE_MODE_ROUTE);
+  if (!ws || ws_bytes < need)
+    return set_error(MOE_EWORKSPACE, "route workspace %zu < %zu bytes", ws_bytes, need);
+  const int rf32 = desc->router_wtype == MOE_WTYPE_F32;
+  if (T <= 64 && desc->hidden / (rf32 ? 4 : 8) > 64 * 16)
+    return set_error(MOE_EUNSUPPORTED, "hidden %d too wide for the decode router", desc->hidden);
+  if (!aligned(x, 16) || !aligned(w_router, 16))
+    return set_error(MOE_EINVAL, "x and w_router must be 16-byte aligned");
+  return hip_status(moe::launch_route(x, w_router, rf32, T, desc->hidden, desc->n_experts,
+                                      desc->top_k, desc->renorm_topk, static_cast<float*>(ws), ids,
+                                      w, as_stream(stream)),
+                    "moe_route");
+}
+
+static int check_ffn_args(const moe_desc* desc, const void* x, int32_t T, const int32_t* ids,
+                          const float* w, const void* slot_pool, const void* shared_expert,
+                          float* y) {
+  int st = check_desc(desc);
+  if (st) return st;
+  if (!x || !ids || !w || !slot_pool || !y) return set_error(MOE_EINVAL, "null pointer");
+  if (desc->has_shared && !shared_expert)
+    return set_error(MOE_EINVAL, "has_shared set but shared_expert is null");
+  if (!desc->has_shared && shared_expert)
+    return set_error(MOE_EINVAL, "shared_expert given but has_shared is 0");
+  if (!aligned(x, 16) || !aligned(slot_pool, 256) || !aligned(y, 16) ||
+      (shared_expert && !aligned(shared_expert, 256)))
+    return set_error(MOE_EINVAL, "x, y need 16-byte and expert blocks 256-byte alignment");
+  (void)T;
+  return MOE_OK;
+}
+
+int moe_decode(const moe_desc* desc, const void* x, int32_t T, const int32_t* ids, const float* w,
+               const int32_t* slot_of_expert, const void* slot_pool, const void* shared_expert,
+               float* y, void* ws, size_t ws_bytes, void* stream) {
+  if (T == 0) return check_desc(desc);
+  int st = check_ffn_args(desc, x, T, ids, w, slot_pool, shared_expert, y);
+  if (st) return st;
+  if (T < 0 || T > MOE_DECODE_MAX_T || T * desc->top_k > 1024)
+    return set_error(MOE_EINVAL, "decode T %d outside [1, %d] or T*k > 1024", T, MOE_DECODE_MAX_T);
+  if (!moe::decode_shape_supported(desc->wtype, desc->hidden, desc->inter))
+    return set_error(MOE_EUNSUPPORTED, "decode shape H=%d I=%d not compiled", desc->hidden,
+                     desc->inter);
+  const size_t need = moe_workspace_bytes(desc, T, MOE_MODE_DECODE);
+  if (!ws || ws_bytes < need || !aligned(ws, 16))
+    return set_error(MOE_EWORKSPACE, "decode workspace %zu < %zu bytes", ws_bytes, need);
+  moe::DecodeLaunch d;
+  size_t off[6], bytes;
+  layout(desc, off, &bytes);
+  d.x = x; d.ids = ids; d.w = w; d.slot_of = slot_of_expert; d.pool = slot_pool;
+  d.shared = shared_expert; d.h = static_cast<float*>(ws); d.y = y;
+  d.expert_bytes = (int64_t)bytes;
+  for (int i = 0; i < 6; ++i) d.off[i] = (int64_t)off[i];
+  d.T = T; d.H = desc->hidden; d.I = desc->inter; d.E = desc->n_experts; d.k = desc->top_k;
+  d.wtype = desc->wtype;
+  return hip_status(moe::launch_decode(d, as_stream(stream)), "moe_decode");
+}
+
+int moe_prefill(const moe_desc* desc, const void* x, int32_t T, const int32_t* ids, const float* w,
+                const int32_t* slot_of_expert, const void* slot_pool, const void* shared_expert,
+                float* y, void* ws, size_t ws_bytes, void* stream) {
+  if (T == 0) return check_desc(desc);
+  int st = check_ffn_args(desc, x, T, ids, w, slot_pool, shared_expert, y);
+  if (st) return st;
+  if (desc->wtype != MOE_WTYPE_MXFP4)
+    return set_error(MOE_EUNSUPPORTED, "moe_prefill runs MXFP4 expert weights only");
+  if (desc->hidden % 128 || desc->inter % 128)
+    return set_error(MOE_EUNSUPPORTED, "moe_prefill needs hidden and inter multiples of 128");
+  if (T < 0 || T > 65536) return set_error(MOE_EINVAL, "prefill T %d outside [1, 65536]", T);
+  const PrefillWs L = prefill_ws(desc, T);
+  if (!ws || ws_bytes < L.total || !aligned(ws, 256))
+    return set_error(MOE_EWORKSPACE, "prefill workspace %zu < %zu bytes", ws_bytes, L.total);
+  uint8_t* b = static_cast<uint8_t*>(ws);
+  moe::PrefillLaunch p;
+  size_t off[6], bytes;
+  layout(desc, off, &bytes);
+  p.x = x; p.ids = ids; p.w = w; p.slot_of = slot_of_expert; p.pool = slot_pool;
+  p.shared = shared_expert; p.y = y; p.expert_bytes = (int64_t)bytes;
+  for (int i = 0; i < 6; ++i) p.off[i] = (int64_t)off[i];
+  p.T = T; p.H = desc->hidden; p.I = desc->inter; p.E = desc->n_experts; p.k = desc->top_k;
+  p.xq_codes = b + L.xq_codes;
+  p.xq_scales = b + L.xq_scales;
+  p.chunk_counts = reinterpret_cast<int32_t*>(b + L.chunk_counts);
+  p.seg_start = reinterpret_cast<int32_t*>(b + L.seg_start);
+  p.tiles = reinterpret_cast<int32_t*>(b + L.tiles);
+  p.sorted_pair = reinterpret_cast<int32_t*>(b + L.sorted_pair);
+  p.hq_codes = b + L.hq_codes;
+  p.hq_scales = b + L.hq_scales;
+  p.partial = reinterpret_cast<float*>(b + L.partial);
+  p.n_chunks = L.n_chunks;
+  p.max_tiles = L.max_tiles;
+  return hip_status(moe::launch_prefill(p, as_stream(stream)), "moe_prefill");
+}
+
+int moe_merge_partials(const float* a, const float* b, float* y, size_t n, void* stream) {
+  if (n == 0) return MOE_OK;
+  if (!a || !b || !y) return set_error(MOE_EINVAL, "null pointer");
+  return hip_status(moe::launch_merge(a, b, y, n, as_stream(stream)), "moe_merge_partials");
+}
+
+int moe_quantize_mxfp4(const float* src, int32_t rows, int32_t K, int64_t src_ld, uint8_t* codes,
+                       uint8_t* scales, void* stream) {
+  if (rows == 0) return MOE_OK;
+  if (!src || !codes || !scales) return set_error(MOE_EINVAL, "null pointer");
+  if (rows < 0 || K <= 0 || K % 32 || src_ld < K || src_ld % 4)
+    return set_error(MOE_EINVAL, "bad shape rows=%d K=%d ld=%lld", rows, K, (long long)src_ld);
+  if (!aligned(src, 16) || !aligned(codes, 16))
+    return set_error(MOE_EINVAL, "src and codes must be 16-byte aligned");
+  return hip_status(moe::launch_quantize_mxfp4(src, rows, K, src_ld, codes, scales,
+                                               as_stream(stream)),
+                    "moe_quantize_mxfp4");
+}
+
+int moe_debug_dequant_mxfp4(const uint8_t* codes, const uint8_t* scales, int64_t n_blocks,
+                            float* out, void* stream) {
+  if (n_blocks == 0) return MOE_OK;
+  if (!codes || !scales || !out || n_blocks < 0) return set_error(MOE_EINVAL, "bad argument");
+  if (!aligned(codes, 16) || !aligned(out, 16))
+    return set_error(MOE_EINVAL, "codes and out must be 16-byte aligned");
+  return hip_status(moe::launch_dequant_mxfp4(codes, scales, n_blocks, out, as_stream(stream)),
+                    "moe_debug_dequant_mxfp4");
+}
+
+int moe_debug_mfma_fp4_tile(const uint8_t* a_codes, const uint8_t* a_scales,
+                            const uint8_t* b_codes, const uint8_t* b_scales, float* out,
+                            void* stream) {
+  if (!a_codes || !a_scales || !b_codes || !b_scales || !out)
+    return set_error(MOE_EINVAL, "null pointer");
+  if (!aligned(a_codes, 16) || !aligned(b_codes, 16))
+    return set_error(MOE_EINVAL, "codes must be 16-byte aligned");
+  return hip_status(moe::launch_mfma_fp4_tile(a_codes, a_scales, b_codes, b_scales, out,
+                                              as_stream(stream)),
+                    "moe_debug_mfma_fp4_tile");
+}
+
+}  // extern "C"

@@ -1,0 +1,162 @@
+// device.hpp - small device-side helpers shared by the gfx950 kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef float v2f __attribute__((ext_vector_type(2)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+typedef int v8i __attribute__((ext_vector_type(8)));
+
+constexpr int kWave = 64;
+
+// ---- bf16 ----------------------------------------------------------------
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+__device__ __forceinline__ v2bf as_v2bf(uint32_t w) { return __builtin_bit_cast(v2bf, w); }
+
+// dot of two packed bf16 pairs accumulated into fp32 (products are exact)
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float acc) {
+  return __builtin_amdgcn_fdot2_f32_bf16(as_v2bf(a), as_v2bf(b), acc, false);
+}
+
+// ---- e2m1 (MXFP4 element) decode ------------------------------------------
+// Two e2m1 codes held in byte SEL of `word` -> two bf16 values (exact: every
+// e2m1 value is a bf16), packed low element first.  Uses the gfx950 scaled
+// FP4 convert with scale 1.0, so the values are the bare e2m1 values.
+template <int SEL>
+__device__ __forceinline__ uint32_t fp4x2_to_bf16x2(uint32_t word) {
+  v2bf r = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, 1.0f, SEL);
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+template <int SEL>
+__device__ __forceinline__ v2f fp4x2_to_f32x2(uint32_t word) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, SEL);
+}
+
+// e8m0 scale byte -> 2^(s-127) as an fp32 (s = 0 is the denormal 2^-127,
+// s = 255 is NaN).
+__device__ __forceinline__ float e8m0_to_f32(uint32_t s) {
+  s &= 0xffu;
+  if (s == 0) return __uint_as_float(0x00400000u);
+  if (s == 255) return __uint_as_float(0x7fc00000u);
+  return __uint_as_float(s << 23);
+}
+
+// sum over the 32 e2m1 values of one 16-byte block times 32 bf16 x values
+// (x given as 16 packed bf16 pairs), fp32 accumulation, no scale applied.
+__device__ __forceinline__ float dot_fp4_bf16_block(const uint4 q, const uint32_t* xp) {
+  float acc = 0.f;
+  const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    acc = dot2_bf16(fp4x2_to_bf16x2<0>(w[i]), xp[4 * i + 0], acc);
+    acc = dot2_bf16(fp4x2_to_bf16x2<1>(w[i]), xp[4 * i + 1], acc);
+    acc = dot2_bf16(fp4x2_to_bf16x2<2>(w[i]), xp[4 * i + 2], acc);
+    acc = dot2_bf16(fp4x2_to_bf16x2<3>(w[i]), xp[4 * i + 3], acc);
+  }
+  return acc;
+}
+
+// sum over the 32 e2m1 values of one block times 32 fp32 h values.
+__device__ __forceinline__ float dot_fp4_f32_block(const uint4 q, const float* h) {
+  float acc = 0.f;
+  const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v2f a = fp4x2_to_f32x2<0>(w[i]);
+    v2f b = fp4x2_to_f32x2<1>(w[i]);
+    v2f c = fp4x2_to_f32x2<2>(w[i]);
+    v2f d = fp4x2_to_f32x2<3>(w[i]);
+    acc = fmaf(a.x, h[8 * i + 0], acc);
+    acc = fmaf(a.y, h[8 * i + 1], acc);
+    acc = fmaf(b.x, h[8 * i + 2], acc);
+    acc = fmaf(b.y, h[8 * i + 3], acc);
+    acc = fmaf(c.x, h[8 * i + 4], acc);
+    acc = fmaf(c.y, h[8 * i + 5], acc);
+    acc = fmaf(d.x, h[8 * i + 6], acc);
+    acc = fmaf(d.y, h[8 * i + 7], acc);
+  }
+  return acc;
+}
+
+// ---- e2m1 encode (round to nearest, ties to the even code, saturate) ------
+// r is the element already divided by its block scale.  The magnitude code
+// is the number of grid thresholds r passes; a threshold that sits exactly
+// half way between two grid points counts only when the upper neighbour has
+// the even code (mantissa bit 0).
+__device__ __forceinline__ uint32_t e2m1_code(float r) {
+  float a = fabsf(r);
+  uint32_t c = (a > 0.25f) + (a >= 0.75f) + (a > 1.25f) + (a >= 1.75f) +
+               (a > 2.5f) + (a >= 3.5f) + (a > 5.0f);
+  return c | ((__float_as_uint(r) >> 28) & 8u);
+}
+
+// block exponent X = floor(log2 amax) - 2, clamped to [-127, 127]; amax > 0.
+__device__ __forceinline__ int mx_block_exponent(float amax) {
+  uint32_t b = __float_as_uint(amax);
+  int e = (int)((b >> 23) & 0xffu);
+  int fl;
+  if (e == 0) {
+    // denormal: value = m * 2^-149, floor(log2) = 31 - clz(m) - 149
+    fl = (31 - __clz((int)(b & 0x7fffffu))) - 149;
+  } else {
+    fl = e - 127;
+  }
+  int X = fl - 2;
+  return X < -127 ? -127 : (X > 127 ? 127 : X);
+}
+
+// 2^-X as an fp32 multiplier is not always representable (X = -127 gives
+// 2^127, fine; X = 127 gives 2^-127, a denormal), so divide in two exact
+// power-of-two steps.
+__device__ __forceinline__ float mx_scale_down(float v, int X) {
+  return ldexpf(v, -X);
+}
+
+// ---- wave reductions --------------------------------------------------------
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
+  return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, kWave));
+  return v;
+}
+
+// exclusive prefix sum over a 256-thread block (4 waves); returns the
+// exclusive prefix of `v` and writes the block total to *total.
+__device__ __forceinline__ int block256_exclusive_scan(int v, int* total, int* lds4) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  int inc = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    int o = __shfl_up(inc, off, kWave);
+    if (lane >= off) inc += o;
+  }
+  if (lane == 63) lds4[wv] = inc;
+  __syncthreads();
+  int base = 0, tot = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    int s = lds4[i];
+    if (i < wv) base += s;
+    tot += s;
+  }
+  __syncthreads();
+  *total = tot;
+  return base + inc - v;
+}
+
+__device__ __forceinline__ uint4 ldg16(const void* p) {
+  return *reinterpret_cast<const uint4*>(p);
+}
+
+}  // namespace moe

@@ -1,0 +1,122 @@
+// formats.hip - MXFP4 quantise / dequantise kernels, the exact partial-sum
+// merge, and small fill kernels used by the expert cache.
+#include "device.hpp"
+#include "kernels.hpp"
+
+namespace moe {
+namespace {
+
+// One thread per 32-element block: amax, shared exponent, 32 e2m1 codes.
+__global__ __launch_bounds__(256) void quantize_kernel(const float* __restrict__ src, int rows,
+                                                       int K, int64_t ld,
+                                                       uint8_t* __restrict__ codes,
+                                                       uint8_t* __restrict__ scales) {
+  const int nb = K / 32;
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid >= (int64_t)rows * nb) return;
+  const int64_t r = gid / nb;
+  const int b = (int)(gid % nb);
+  const float* s = src + r * ld + (int64_t)b * 32;
+  float v[32];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float4 f = reinterpret_cast<const float4*>(s)[i];
+    v[4 * i] = f.x; v[4 * i + 1] = f.y; v[4 * i + 2] = f.z; v[4 * i + 3] = f.w;
+  }
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  uint32_t packed[4] = {0, 0, 0, 0};
+  uint32_t sbyte = 0;
+  if (amax > 0.f) {
+    const int X = mx_block_exponent(amax);
+    sbyte = (uint32_t)(X + 127);
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      const uint32_t c = e2m1_code(mx_scale_down(v[i], X));
+      packed[i / 8] |= c << (4 * (i % 8));
+    }
+  }
+  *reinterpret_cast<uint4*>(codes + r * (K / 2) + (int64_t)b * 16) =
+      make_uint4(packed[0], packed[1], packed[2], packed[3]);
+  scales[r * nb + b] = (uint8_t)sbyte;
+}
+
+// One thread per block: the in-register decoder of the expert kernels times
+// the e8m0 scale.
+__global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict__ codes,
+                                                      const uint8_t* __restrict__ scales,
+                                                      int64_t n_blocks, float* __restrict__ out) {
+  const int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= n_blocks) return;
+  const uint4 q = ldg16(codes + b * 16);
+  const float sc = e8m0_to_f32(scales[b]);
+  const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+  float4* o = reinterpret_cast<float4*>(out + b * 32);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const v2f a = fp4x2_to_f32x2<0>(w[i]);
+    const v2f c = fp4x2_to_f32x2<1>(w[i]);
+    const v2f d = fp4x2_to_f32x2<2>(w[i]);
+    const v2f e = fp4x2_to_f32x2<3>(w[i]);
+    o[2 * i] = make_float4(a.x * sc, a.y * sc, c.x * sc, c.y * sc);
+    o[2 * i + 1] = make_float4(d.x * sc, d.y * sc, e.x * sc, e.y * sc);
+  }
+}
+
+__global__ __launch_bounds__(256) void merge_kernel(const float* a, const float* b, float* y,
+                                                    size_t n, int vec) {
+  const size_t n4 = vec ? n / 4 : 0;
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride) {
+    const float4 u = reinterpret_cast<const float4*>(a)[i];
+    const float4 v = reinterpret_cast<const float4*>(b)[i];
+    reinterpret_cast<float4*>(y)[i] = make_float4(u.x + v.x, u.y + v.y, u.z + v.z, u.w + v.w);
+  }
+  for (size_t i = n4 * 4 + (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride)
+    y[i] = a[i] + b[i];
+}
+
+__global__ void fill_i32_kernel(int32_t* dst, int32_t value, int64_t n) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) dst[i] = value;
+}
+
+}  // namespace
+
+hipError_t launch_quantize_mxfp4(const float* src, int rows, int K, int64_t ld,
+                                 uint8_t* codes, uint8_t* scales, hipStream_t st) {
+  const int64_t n = (int64_t)rows * (K / 32);
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(quantize_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, src,
+                     rows, K, ld, codes, scales);
+  return hipGetLastError();
+}
+
+hipError_t launch_dequant_mxfp4(const uint8_t* codes, const uint8_t* scales, int64_t n_blocks,
+                                float* out, hipStream_t st) {
+  if (n_blocks == 0) return hipSuccess;
+  hipLaunchKernelGGL(dequant_kernel, dim3((unsigned)((n_blocks + 255) / 256)), dim3(256), 0, st,
+                     codes, scales, n_blocks, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_merge(const float* a, const float* b, float* y, size_t n, hipStream_t st) {
+  if (n == 0) return hipSuccess;
+  size_t blocks = (n / 4 + 255) / 256;
+  if (blocks < 1) blocks = 1;
+  if (blocks > 4096) blocks = 4096;
+  const int vec = ((((uintptr_t)a) | ((uintptr_t)b) | ((uintptr_t)y)) & 15) == 0;
+  hipLaunchKernelGGL(merge_kernel, dim3((unsigned)blocks), dim3(256), 0, st, a, b, y, n, vec);
+  return hipGetLastError();
+}
+
+hipError_t launch_fill_i32(int32_t* dst, int32_t value, int64_t n, hipStream_t st) {
+  if (n == 0) return hipSuccess;
+  int64_t blocks = (n + 255) / 256;
+  if (blocks > 1024) blocks = 1024;
+  hipLaunchKernelGGL(fill_i32_kernel, dim3((unsigned)blocks), dim3(256), 0, st, dst, value, n);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,78 @@
+// kernels.hpp - host-side launchers of the gfx950 kernels (internal).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+struct DecodeLaunch {
+  const void* x;
+  const int32_t* ids;
+  const float* w;
+  const int32_t* slot_of;
+  const void* pool;
+  const void* shared;
+  float* h;
+  float* y;
+  int64_t expert_bytes;
+  int64_t off[6];
+  int T, H, I, E, k, wtype;
+};
+
+struct PrefillLaunch {
+  const void* x;
+  const int32_t* ids;
+  const float* w;
+  const int32_t* slot_of;
+  const void* pool;
+  const void* shared;
+  float* y;
+  int64_t expert_bytes;
+  int64_t off[6];
+  int T, H, I, E, k;
+  // workspace carve-up
+  uint8_t* xq_codes;     // [T][H/2]
+  uint8_t* xq_scales;    // [T][H/32]
+  int32_t* chunk_counts; // [n_chunks][E+1]
+  int32_t* seg_start;    // [E+2]
+  int32_t* tiles;        // [2 * max_tiles + 1]: n_tiles, then (bin, row0) pairs
+  int32_t* sorted_pair;  // [n_pairs]
+  uint8_t* hq_codes;     // [n_pairs][I/2]   (sorted order)
+  uint8_t* hq_scales;    // [n_pairs][I/32]
+  float* partial;        // [T][k+1][H]
+  int n_chunks, max_tiles;
+};
+
+// router
+hipError_t launch_route(const void* x, const void* w_router, int router_f32,
+                        int T, int H, int E, int k, int renorm, float* logits,
+                        int32_t* ids, float* w, hipStream_t st);
+
+// decode
+bool decode_shape_supported(int wtype, int H, int I);
+hipError_t launch_decode(const DecodeLaunch& d, hipStream_t st);
+
+// prefill
+constexpr int kPrefillChunk = 256;   // pairs per sort chunk
+constexpr int kPrefillMT = 128;      // rows per M tile
+int prefill_max_tiles(int T, int k, int E);
+hipError_t launch_prefill(const PrefillLaunch& p, hipStream_t st);
+
+// formats / merge
+hipError_t launch_quantize_mxfp4(const float* src, int rows, int K, int64_t ld,
+                                 uint8_t* codes, uint8_t* scales, hipStream_t st);
+hipError_t launch_dequant_mxfp4(const uint8_t* codes, const uint8_t* scales,
+                                int64_t n_blocks, float* out, hipStream_t st);
+hipError_t launch_merge(const float* a, const float* b, float* y, size_t n,
+                        hipStream_t st);
+hipError_t launch_mfma_fp4_tile(const uint8_t* a_codes, const uint8_t* a_scales,
+                                const uint8_t* b_codes, const uint8_t* b_scales,
+                                float* out, hipStream_t st);
+
+// cache
+hipError_t launch_slot_updates(int32_t* table, const int32_t* idx,
+                               const int32_t* val, int n, hipStream_t st);
+hipError_t launch_fill_i32(int32_t* dst, int32_t value, int64_t n, hipStream_t st);
+
+}  // namespace moe

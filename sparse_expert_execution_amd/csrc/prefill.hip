@@ -1,0 +1,493 @@
+// prefill.hip - long-batch expert FFNs on the gfx950 scaled FP4 matrix cores.
+//
+// With thousands of tokens a layer touches nearly every expert (explainx.ai
+// guide, "Prefill: load almost every expert without idling the GPU"), so the
+// work is a grouped GEMM: (token, expert) pairs are counting-sorted by
+// expert, each expert multiplies its token rows once per weight tile, and the
+// per-pair outputs are combined with the gate weights afterwards.
+//
+// Precision contract: x is quantised to MXFP4 along H and h along I with the
+// library's MXFP4 encoder; both products are FP4 x FP4 with e8m0 block scales
+// on v_mfma_scale_f32_16x16x128_f8f6f4 with fp32 accumulation.
+//
+// Pipeline (one stream, no host synchronisation):
+//   1 quantise x rows                 x [T][H] bf16 -> codes/scales
+//   2 per-chunk expert histogram      256 pairs per chunk
+//   3 scan                            segment starts, per-chunk offsets, tiles
+//   4 stable scatter                  sorted_pair[pos] = pair id
+//   5 GEMM1 gate|up + SwiGLU + MXFP4  -> hq (sorted order)
+//   6 GEMM2 down                      -> partial[t][j][H] fp32
+//   7 combine                         y[t] = sum_j w[t][j] partial[t][j] (+ shared)
+#include "device.hpp"
+#include "kernels.hpp"
+
+namespace moe {
+namespace {
+
+constexpr int kChunk = kPrefillChunk;
+constexpr int kMT = kPrefillMT;
+
+// ---- MFMA fragments ----------------------------------------------------------
+// A 16-row x 128-K MXFP4 tile as one lane's operand: lane l supplies row
+// l % 16 and the 32-element K block l / 16 (16 bytes of codes, one scale).
+struct Frag {
+  uint4 q;
+  uint32_t s;
+};
+
+__device__ __forceinline__ Frag load_frag(const uint8_t* codes_row, const uint8_t* scales_row,
+                                          int k0, bool ok) {
+  Frag f;
+  const int kb = threadIdx.x & 63;
+  const int blk = (k0 >> 5) + (kb >> 4);
+  if (ok) {
+    f.q = ldg16(codes_row + (int64_t)blk * 16);
+    f.s = scales_row[blk];
+  } else {
+    f.q = make_uint4(0, 0, 0, 0);
+    f.s = 127;
+  }
+  return f;
+}
+
+__device__ __forceinline__ v4f mfma_fp4(const Frag& a, const Frag& b, v4f c) {
+  v8i av = {(int)a.q.x, (int)a.q.y, (int)a.q.z, (int)a.q.w, 0, 0, 0, 0};
+  v8i bv = {(int)b.q.x, (int)b.q.y, (int)b.q.z, (int)b.q.w, 0, 0, 0, 0};
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, c, 4, 4, 0, (int)a.s, 0,
+                                                          (int)b.s);
+}
+
+// output element (row, col) held by lane l, register i of a 16x16 tile
+__device__ __forceinline__ int d_row(int lane, int i) { return 4 * (lane >> 4) + i; }
+__device__ __forceinline__ int d_col(int lane) { return lane & 15; }
+
+// ---- 1: quantise bf16 rows to MXFP4 -------------------------------------------
+__global__ __launch_bounds__(256) void quant_bf16_kernel(const uint16_t* __restrict__ x, int T,
+                                                         int H, uint8_t* __restrict__ codes,
+                                                         uint8_t* __restrict__ scales) {
+  const int nb = H / 32;
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid >= (int64_t)T * nb) return;
+  const int64_t r = gid / nb;
+  const int b = (int)(gid % nb);
+  const uint4* s = reinterpret_cast<const uint4*>(x + r * H + (int64_t)b * 32);
+  float v[32];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint4 q = s[i];
+    v[8 * i + 0] = bf16_lo(q.x); v[8 * i + 1] = bf16_hi(q.x);
+    v[8 * i + 2] = bf16_lo(q.y); v[8 * i + 3] = bf16_hi(q.y);
+    v[8 * i + 4] = bf16_lo(q.z); v[8 * i + 5] = bf16_hi(q.z);
+    v[8 * i + 6] = bf16_lo(q.w); v[8 * i + 7] = bf16_hi(q.w);
+  }
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  uint32_t packed[4] = {0, 0, 0, 0};
+  uint32_t sbyte = 0;
+  if (amax > 0.f) {
+    const int X = mx_block_exponent(amax);
+    sbyte = (uint32_t)(X + 127);
+#pragma unroll
+    for (int i = 0; i < 32; ++i) packed[i / 8] |= e2m1_code(mx_scale_down(v[i], X)) << (4 * (i % 8));
+  }
+  *reinterpret_cast<uint4*>(codes + r * (H / 2) + (int64_t)b * 16) =
+      make_uint4(packed[0], packed[1], packed[2], packed[3]);
+  scales[r * nb + b] = (uint8_t)sbyte;
+}
+
+// bin of a pair: routed expert (if resident), E for the shared expert, -1 skip
+struct SortArgs {
+  const int32_t* ids;
+  const int32_t* slot_of;
+  int T, k, E, has_shared, n_pairs, n_chunks, max_tiles;
+  int32_t* chunk_counts;
+  int32_t* seg_start;
+  int32_t* tiles;
+  int32_t* sorted_pair;
+};
+
+__device__ __forceinline__ int pair_bin(const SortArgs& a, int p) {
+  const int nr = a.T * a.k;
+  if (p >= nr) return a.E;  // shared
+  const int e = a.ids[p];
+  if (e < 0 || e >= a.E) return -1;
+  if (a.slot_of && a.slot_of[e] < 0) return -1;
+  return e;
+}
+
+// ---- 2: per-chunk histogram ----------------------------------------------------
+__global__ __launch_bounds__(256) void sort_count_kernel(SortArgs a) {
+  extern __shared__ int hist[];
+  const int nb = a.E + 1;
+  for (int b = threadIdx.x; b < nb; b += 256) hist[b] = 0;
+  __syncthreads();
+  const int p = blockIdx.x * kChunk + threadIdx.x;
+  if (p < a.n_pairs) {
+    const int b = pair_bin(a, p);
+    if (b >= 0) atomicAdd(&hist[b], 1);
+  }
+  __syncthreads();
+  for (int b = threadIdx.x; b < nb; b += 256)
+    a.chunk_counts[(int64_t)blockIdx.x * nb + b] = hist[b];
+}
+
+// ---- 3: scan (one workgroup) ----------------------------------------------------
+// seg_start[b] = first sorted position of bin b (seg_start[E+1] = total);
+// chunk_counts[c][b] becomes the first position of chunk c's pairs of bin b;
+// tiles = {n_tiles, (bin, row0) ...} with row0 the absolute sorted position.
+__global__ __launch_bounds__(1024) void sort_scan_kernel(SortArgs a) {
+  extern __shared__ int sh[];
+  const int nb = a.E + 1;
+  int* tot = sh;            // [nb]
+  int* ntile = sh + nb;     // [nb]
+  for (int b = threadIdx.x; b < nb; b += blockDim.x) {
+    int s = 0;
+    for (int c = 0; c < a.n_chunks; ++c) s += a.chunk_counts[(int64_t)c * nb + b];
+    tot[b] = s;
+    ntile[b] = (s + kMT - 1) / kMT;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int pos = 0, tp = 0;
+    for (int b = 0; b < nb; ++b) {
+      const int s = tot[b], n = ntile[b];
+      tot[b] = pos;      // segment start
+      ntile[b] = tp;     // first tile index
+      pos += s;
+      tp += n;
+    }
+    a.seg_start[nb] = pos;
+    a.tiles[0] = tp < a.max_tiles ? tp : a.max_tiles;
+  }
+  __syncthreads();
+  for (int b = threadIdx.x; b < nb; b += blockDim.x) {
+    const int start = tot[b];
+    const int end = (b + 1 < nb) ? tot[b + 1] : a.seg_start[nb];
+    a.seg_start[b] = start;
+    int pos = start;
+    for (int c = 0; c < a.n_chunks; ++c) {
+      const int n = a.chunk_counts[(int64_t)c * nb + b];
+      a.chunk_counts[(int64_t)c * nb + b] = pos;
+      pos += n;
+    }
+    int ti = ntile[b];
+    for (int r0 = start; r0 < end; r0 += kMT, ++ti) {
+      if (ti < a.max_tiles) {
+        a.tiles[1 + 2 * ti] = b;
+        a.tiles[2 + 2 * ti] = r0;
+      }
+    }
+  }
+}
+
+// ---- 4: stable scatter ------------------------------------------------------------
+__global__ __launch_bounds__(256) void sort_scatter_kernel(SortArgs a) {
+  __shared__ int sbin[kChunk];
+  const int nb = a.E + 1;
+  const int p = blockIdx.x * kChunk + threadIdx.x;
+  const int b = p < a.n_pairs ? pair_bin(a, p) : -1;
+  sbin[threadIdx.x] = b;
+  __syncthreads();
+  if (b < 0) return;
+  int rank = 0;
+  for (int q = 0; q < (int)threadIdx.x; ++q) rank += (sbin[q] == b);
+  a.sorted_pair[a.chunk_counts[(int64_t)blockIdx.x * nb + b] + rank] = p;
+}
+
+struct GemmArgs {
+  const int32_t* slot_of;
+  const uint8_t* pool;
+  const uint8_t* shared;
+  int64_t expert_bytes;
+  int64_t off[6];
+  int T, H, I, E, k;
+  const int32_t* seg_start;
+  const int32_t* tiles;
+  const int32_t* sorted_pair;
+  const uint8_t* xq_codes;
+  const uint8_t* xq_scales;
+  uint8_t* hq_codes;
+  uint8_t* hq_scales;
+  float* partial;
+};
+
+__device__ __forceinline__ const uint8_t* bin_base(const GemmArgs& a, int bin) {
+  if (bin >= a.E) return a.shared;
+  const int slot = a.slot_of ? a.slot_of[bin] : bin;
+  return a.pool + (int64_t)slot * a.expert_bytes;
+}
+
+__device__ __forceinline__ int pair_token(const GemmArgs& a, int p) {
+  const int nr = a.T * a.k;
+  return p < nr ? p / a.k : p - nr;
+}
+
+// ---- 5: GEMM1 gate|up + SwiGLU + MXFP4(h) ----------------------------------------
+// grid = (max_tiles, I / 64).  4 waves: wm = wave & 1 picks 64 of the tile's
+// 128 rows, wn = wave >> 1 picks 32 of the workgroup's 64 h columns; a wave
+// holds 4 (rows) x 4 (gate lo, gate hi, up lo, up hi) 16x16 accumulators.
+__global__ __launch_bounds__(256) void gemm1_kernel(GemmArgs a) {
+  const int n_tiles = a.tiles[0];
+  if ((int)blockIdx.x >= n_tiles) return;
+  const int bin = a.tiles[1 + 2 * blockIdx.x];
+  const int row0 = a.tiles[2 + 2 * blockIdx.x];
+  const int seg_end = a.seg_start[bin + 1];
+  const uint8_t* base = bin_base(a, bin);
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int wm = wv & 1, wn = wv >> 1;
+  const int c0 = blockIdx.y * 64 + wn * 32;  // first h column of this wave
+  const int H = a.H;
+
+  // per-lane operand rows
+  const uint8_t* arow_c[4];
+  const uint8_t* arow_s[4];
+  bool a_ok[4];
+#pragma unroll
+  for (int ms = 0; ms < 4; ++ms) {
+    const int r = row0 + wm * 64 + ms * 16 + (lane & 15);
+    a_ok[ms] = r < seg_end;
+    const int t = a_ok[ms] ? pair_token(a, a.sorted_pair[r]) : 0;
+    arow_c[ms] = a.xq_codes + (int64_t)t * (H / 2);
+    arow_s[ms] = a.xq_scales + (int64_t)t * (H / 32);
+  }
+  const uint8_t* brow_c[4];
+  const uint8_t* brow_s[4];
+#pragma unroll
+  for (int ns = 0; ns < 4; ++ns) {
+    const int mat = ns >> 1;  // 0 gate, 1 up
+    const int n = c0 + (ns & 1) * 16 + (lane & 15);
+    brow_c[ns] = base + a.off[2 * mat] + (int64_t)n * (H / 2);
+    brow_s[ns] = base + a.off[2 * mat + 1] + (int64_t)n * (H / 32);
+  }
+
+  v4f acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  for (int k0 = 0; k0 < H; k0 += 128) {
+    Frag fa[4], fb[4];
+#pragma unroll
+    for (int ms = 0; ms < 4; ++ms) fa[ms] = load_frag(arow_c[ms], arow_s[ms], k0, a_ok[ms]);
+#pragma unroll
+    for (int ns = 0; ns < 4; ++ns) fb[ns] = load_frag(brow_c[ns], brow_s[ns], k0, true);
+#pragma unroll
+    for (int ms = 0; ms < 4; ++ms)
+#pragma unroll
+      for (int ns = 0; ns < 4; ++ns) acc[ms][ns] = mfma_fp4(fa[ms], fb[ns], acc[ms][ns]);
+  }
+
+  // epilogue: h = silu(g) * u, quantise each row's 32-column block to MXFP4
+  const int I = a.I;
+#pragma unroll
+  for (int ms = 0; ms < 4; ++ms) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = row0 + wm * 64 + ms * 16 + d_row(lane, i);
+      const float g0 = acc[ms][0][i], g1 = acc[ms][1][i];
+      const float u0 = acc[ms][2][i], u1 = acc[ms][3][i];
+      const float h0 = g0 / (1.0f + expf(-g0)) * u0;
+      const float h1 = g1 / (1.0f + expf(-g1)) * u1;
+      float amax = fmaxf(fabsf(h0), fabsf(h1));
+#pragma unroll
+      for (int off = 1; off < 16; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off, kWave));
+      uint32_t q0 = 0, q1 = 0, sbyte = 0;
+      if (amax > 0.f) {
+        const int X = mx_block_exponent(amax);
+        sbyte = (uint32_t)(X + 127);
+        q0 = e2m1_code(mx_scale_down(h0, X));
+        q1 = e2m1_code(mx_scale_down(h1, X));
+      }
+      const uint32_t n0 = __shfl_xor(q0, 1, kWave);
+      const uint32_t n1 = __shfl_xor(q1, 1, kWave);
+      const int c = d_col(lane);
+      if (r < seg_end) {
+        uint8_t* dst = a.hq_codes + (int64_t)r * (I / 2) + c0 / 2;
+        if ((c & 1) == 0) {
+          dst[c >> 1] = (uint8_t)(q0 | (n0 << 4));
+          dst[8 + (c >> 1)] = (uint8_t)(q1 | (n1 << 4));
+        }
+        if (c == 0) a.hq_scales[(int64_t)r * (I / 32) + c0 / 32] = (uint8_t)sbyte;
+      }
+    }
+  }
+}
+
+// ---- 6: GEMM2 down -> per-pair partial rows ----------------------------------------
+// grid = (max_tiles, H / 128).  4 waves as 2 (rows) x 2 (64 output columns).
+__global__ __launch_bounds__(256) void gemm2_kernel(GemmArgs a) {
+  const int n_tiles = a.tiles[0];
+  if ((int)blockIdx.x >= n_tiles) return;
+  const int bin = a.tiles[1 + 2 * blockIdx.x];
+  const int row0 = a.tiles[2 + 2 * blockIdx.x];
+  const int seg_end = a.seg_start[bin + 1];
+  const uint8_t* base = bin_base(a, bin);
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int wm = wv & 1, wn = wv >> 1;
+  const int n0 = blockIdx.y * 128 + wn * 64;
+  const int I = a.I, H = a.H;
+
+  const uint8_t* arow_c[4];
+  const uint8_t* arow_s[4];
+  bool a_ok[4];
+#pragma unroll
+  for (int ms = 0; ms < 4; ++ms) {
+    const int r = row0 + wm * 64 + ms * 16 + (lane & 15);
+    a_ok[ms] = r < seg_end;
+    arow_c[ms] = a.hq_codes + (int64_t)r * (I / 2);
+    arow_s[ms] = a.hq_scales + (int64_t)r * (I / 32);
+  }
+  const uint8_t* brow_c[4];
+  const uint8_t* brow_s[4];
+#pragma unroll
+  for (int ns = 0; ns < 4; ++ns) {
+    const int n = n0 + ns * 16 + (lane & 15);
+    brow_c[ns] = base + a.off[4] + (int64_t)n * (I / 2);
+    brow_s[ns] = base + a.off[5] + (int64_t)n * (I / 32);
+  }
+  v4f acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  for (int k0 = 0; k0 < I; k0 += 128) {
+    Frag fa[4], fb[4];
+#pragma unroll
+    for (int ms = 0; ms < 4; ++ms) fa[ms] = load_frag(arow_c[ms], arow_s[ms], k0, a_ok[ms]);
+#pragma unroll
+    for (int ns = 0; ns < 4; ++ns) fb[ns] = load_frag(brow_c[ns], brow_s[ns], k0, true);
+#pragma unroll
+    for (int ms = 0; ms < 4; ++ms)
+#pragma unroll
+      for (int ns = 0; ns < 4; ++ns) acc[ms][ns] = mfma_fp4(fa[ms], fb[ns], acc[ms][ns]);
+  }
+
+  const int nr = a.T * a.k;
+#pragma unroll
+  for (int ms = 0; ms < 4; ++ms) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = row0 + wm * 64 + ms * 16 + d_row(lane, i);
+      if (r >= seg_end) continue;
+      const int p = a.sorted_pair[r];
+      int prow;
+      if (p < nr) prow = (p / a.k) * (a.k + 1) + (p % a.k);
+      else prow = (p - nr) * (a.k + 1) + a.k;
+      float* dst = a.partial + (int64_t)prow * H + n0 + d_col(lane);
+#pragma unroll
+      for (int ns = 0; ns < 4; ++ns) dst[ns * 16] = acc[ms][ns][i];
+    }
+  }
+}
+
+// ---- 7: combine ------------------------------------------------------------------
+// y[t][c] = sum_j w[t][j] * partial[t][j][c] over resident pairs, in j order,
+// plus the shared expert's row with weight 1.
+__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ partial,
+                                                      const int32_t* __restrict__ ids,
+                                                      const float* __restrict__ w,
+                                                      const int32_t* __restrict__ slot_of,
+                                                      int T, int H, int E, int k,
+                                                      int has_shared, float* __restrict__ y) {
+  const int nv = H / 4;
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid >= (int64_t)T * nv) return;
+  const int t = (int)(gid / nv), c4 = (int)(gid % nv);
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  const float4* pr = reinterpret_cast<const float4*>(partial) + (int64_t)t * (k + 1) * nv + c4;
+  for (int j = 0; j < k; ++j) {
+    const int e = ids[t * k + j];
+    if (e < 0 || e >= E) continue;
+    if (slot_of && slot_of[e] < 0) continue;
+    const float g = w[t * k + j];
+    const float4 v = pr[(int64_t)j * nv];
+    acc.x = fmaf(g, v.x, acc.x); acc.y = fmaf(g, v.y, acc.y);
+    acc.z = fmaf(g, v.z, acc.z); acc.w = fmaf(g, v.w, acc.w);
+  }
+  if (has_shared) {
+    const float4 v = pr[(int64_t)k * nv];
+    acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+  }
+  reinterpret_cast<float4*>(y)[(int64_t)t * nv + c4] = acc;
+}
+
+// ---- debug: one 16x16 tile of A (16 x 128) . B (16 x 128)^T through the same
+// fragment loaders and MFMA wrapper as the GEMMs; out is [16][16] row-major.
+__global__ __launch_bounds__(64) void mfma_tile_kernel(const uint8_t* ac, const uint8_t* as,
+                                                       const uint8_t* bc, const uint8_t* bs,
+                                                       float* out) {
+  const int lane = threadIdx.x;
+  const int r = lane & 15;
+  const Frag fa = load_frag(ac + r * 64, as + r * 4, 0, true);
+  const Frag fb = load_frag(bc + r * 64, bs + r * 4, 0, true);
+  v4f acc = v4f{0.f, 0.f, 0.f, 0.f};
+  acc = mfma_fp4(fa, fb, acc);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) out[d_row(lane, i) * 16 + d_col(lane)] = acc[i];
+}
+
+}  // namespace
+
+int prefill_max_tiles(int T, int k, int E) {
+  const int64_t pairs = (int64_t)T * (k + 1);
+  return (int)((pairs + kMT - 1) / kMT + E + 1);
+}
+
+hipError_t launch_prefill(const PrefillLaunch& p, hipStream_t st) {
+  hipError_t err;
+  const int nb = p.E + 1;
+  const int has_shared = p.shared != nullptr;
+  const int n_pairs = p.T * p.k + (has_shared ? p.T : 0);
+
+  // 1 quantise x
+  {
+    const int64_t n = (int64_t)p.T * (p.H / 32);
+    hipLaunchKernelGGL(quant_bf16_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
+                       static_cast<const uint16_t*>(p.x), p.T, p.H, p.xq_codes, p.xq_scales);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+  }
+  SortArgs s;
+  s.ids = p.ids; s.slot_of = p.slot_of; s.T = p.T; s.k = p.k; s.E = p.E;
+  s.has_shared = has_shared; s.n_pairs = n_pairs; s.n_chunks = p.n_chunks;
+  s.max_tiles = p.max_tiles; s.chunk_counts = p.chunk_counts; s.seg_start = p.seg_start;
+  s.tiles = p.tiles; s.sorted_pair = p.sorted_pair;
+  hipLaunchKernelGGL(sort_count_kernel, dim3(p.n_chunks), dim3(256), nb * sizeof(int), st, s);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  hipLaunchKernelGGL(sort_scan_kernel, dim3(1), dim3(1024), 2 * nb * sizeof(int), st, s);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  hipLaunchKernelGGL(sort_scatter_kernel, dim3(p.n_chunks), dim3(256), 0, st, s);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+
+  GemmArgs g;
+  g.slot_of = p.slot_of; g.pool = static_cast<const uint8_t*>(p.pool);
+  g.shared = static_cast<const uint8_t*>(p.shared); g.expert_bytes = p.expert_bytes;
+  for (int i = 0; i < 6; ++i) g.off[i] = p.off[i];
+  g.T = p.T; g.H = p.H; g.I = p.I; g.E = p.E; g.k = p.k;
+  g.seg_start = p.seg_start; g.tiles = p.tiles; g.sorted_pair = p.sorted_pair;
+  g.xq_codes = p.xq_codes; g.xq_scales = p.xq_scales; g.hq_codes = p.hq_codes;
+  g.hq_scales = p.hq_scales; g.partial = p.partial;
+  hipLaunchKernelGGL(gemm1_kernel, dim3(p.max_tiles, p.I / 64), dim3(256), 0, st, g);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  hipLaunchKernelGGL(gemm2_kernel, dim3(p.max_tiles, p.H / 128), dim3(256), 0, st, g);
+  if ((err = hipGetLastError()) != hipSuccess) return err;
+  {
+    const int64_t n = (int64_t)p.T * (p.H / 4);
+    hipLaunchKernelGGL(combine_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
+                       p.partial, p.ids, p.w, p.slot_of, p.T, p.H, p.E, p.k, has_shared, p.y);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+  }
+  return hipSuccess;
+}
+
+hipError_t launch_mfma_fp4_tile(const uint8_t* a_codes, const uint8_t* a_scales,
+                                const uint8_t* b_codes, const uint8_t* b_scales, float* out,
+                                hipStream_t st) {
+  hipLaunchKernelGGL(mfma_tile_kernel, dim3(1), dim3(64), 0, st, a_codes, a_scales, b_codes,
+                     b_scales, out);
+  return hipGetLastError();
+}
+
+}  // namespace moe

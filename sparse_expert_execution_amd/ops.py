@@ -1,0 +1,223 @@
+"""PyTorch-facing wrappers over the C ABI (argument marshalling only).
+
+Tensors supply device / pinned memory, torch streams supply hipStream_t.
+Every step of the layer runs in libmoe.so's kernels; nothing here computes.
+"""
+
+import ctypes
+
+import torch
+
+from . import _lib
+from ._lib import MoeDesc, MoePlan, check, lib
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _stream(stream=None):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def make_desc(hidden, inter, n_experts, top_k, has_shared=False, renorm=False,
+              wtype="mxfp4", router_wtype="bf16"):
+    wt = {"bf16": _lib.WTYPE_BF16, "mxfp4": _lib.WTYPE_MXFP4}[wtype]
+    rt = {"f32": _lib.WTYPE_F32, "bf16": _lib.WTYPE_BF16}[router_wtype]
+    return MoeDesc(hidden, inter, n_experts, top_k, int(has_shared), int(renorm), wt, rt)
+
+
+def expert_layout(desc):
+    off = (ctypes.c_size_t * 6)()
+    nbytes = ctypes.c_size_t()
+    check(lib().moe_expert_layout(ctypes.byref(desc), off, ctypes.byref(nbytes)),
+          "moe_expert_layout")
+    return list(off), nbytes.value
+
+
+def workspace_bytes(desc, T, mode):
+    return lib().moe_workspace_bytes(ctypes.byref(desc), T, mode)
+
+
+def workspace(desc, T, mode, device="cuda"):
+    n = max(workspace_bytes(desc, T, mode), 256)
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def route(desc, x, w_router, ids, w, ws, stream=None):
+    T = x.shape[0]
+    check(lib().moe_route(ctypes.byref(desc), _ptr(x), _ptr(w_router), T, _ptr(ids),
+                          _ptr(w), _ptr(ws), ws.numel(), _stream(stream)), "moe_route")
+
+
+def decode(desc, x, ids, w, pool, y, ws, slot_of=None, shared=None, stream=None):
+    check(lib().moe_decode(ctypes.byref(desc), _ptr(x), x.shape[0], _ptr(ids), _ptr(w),
+                           _ptr(slot_of), _ptr(pool), _ptr(shared), _ptr(y), _ptr(ws),
+                           ws.numel(), _stream(stream)), "moe_decode")
+
+
+def prefill(desc, x, ids, w, pool, y, ws, slot_of=None, shared=None, stream=None):
+    check(lib().moe_prefill(ctypes.byref(desc), _ptr(x), x.shape[0], _ptr(ids), _ptr(w),
+                            _ptr(slot_of), _ptr(pool), _ptr(shared), _ptr(y), _ptr(ws),
+                            ws.numel(), _stream(stream)), "moe_prefill")
+
+
+def merge_partials(a, b, y, stream=None):
+    check(lib().moe_merge_partials(_ptr(a), _ptr(b), _ptr(y), a.numel(), _stream(stream)),
+          "moe_merge_partials")
+
+
+def quantize_mxfp4(src, codes, scales, stream=None):
+    """src [rows, K] float32 (device) -> codes [rows, K/2] u8, scales [rows, K/32] u8."""
+    rows, K = src.shape
+    check(lib().moe_quantize_mxfp4(_ptr(src), rows, K, src.stride(0), _ptr(codes),
+                                   _ptr(scales), _stream(stream)), "moe_quantize_mxfp4")
+
+
+def dequant_mxfp4(codes, scales, out, stream=None):
+    check(lib().moe_debug_dequant_mxfp4(_ptr(codes), _ptr(scales), scales.numel(), _ptr(out),
+                                        _stream(stream)), "moe_debug_dequant_mxfp4")
+
+
+def mfma_fp4_tile(a_codes, a_scales, b_codes, b_scales, out, stream=None):
+    check(lib().moe_debug_mfma_fp4_tile(_ptr(a_codes), _ptr(a_scales), _ptr(b_codes),
+                                        _ptr(b_scales), _ptr(out), _stream(stream)),
+          "moe_debug_mfma_fp4_tile")
+
+
+def qstar(m, b_pcie, b_host):
+    return lib().moe_qstar(m, b_pcie, b_host)
+
+
+def pack_expert(desc, block, gate, up, down, stream=None):
+    """Write one expert into its byte block (a uint8 device tensor view).
+
+    BF16: gate/up/down are BF16 tensors copied into their sections.
+    MXFP4: gate/up/down are float32 tensors quantised by moe_quantize_mxfp4.
+    """
+    off, nbytes = expert_layout(desc)
+    H, I = desc.hidden, desc.inter
+    if desc.wtype == _lib.WTYPE_BF16:
+        for sec, m, n in ((0, gate, I * H), (1, up, I * H), (2, down, H * I)):
+            block[off[sec]:off[sec] + 2 * n].view(torch.bfloat16).copy_(m.reshape(-1))
+    else:
+        for mat, m, rows, K in ((0, gate, I, H), (1, up, I, H), (2, down, H, I)):
+            c = block[off[2 * mat]:off[2 * mat] + rows * K // 2]
+            s = block[off[2 * mat + 1]:off[2 * mat + 1] + rows * K // 32]
+            quantize_mxfp4(m.contiguous(), c, s, stream)
+    return nbytes
+
+
+class Planner:
+    """Host-only global LRU planner (moe_planner_*)."""
+
+    def __init__(self, n_layers, n_experts, n_slots):
+        self._h = ctypes.c_void_p()
+        check(lib().moe_planner_create(ctypes.byref(self._h), n_layers, n_experts, n_slots),
+              "moe_planner_create")
+        self.n_experts = n_experts
+
+    def __del__(self):
+        if getattr(self, "_h", None):
+            lib().moe_planner_destroy(self._h)
+            self._h = None
+
+    def set_bandwidths(self, b_pcie, b_host):
+        check(lib().moe_planner_set_bandwidths(self._h, b_pcie, b_host), "set_bandwidths")
+
+    def plan(self, layer, ids, w, q):
+        import numpy as np
+        ids = np.ascontiguousarray(ids, dtype=np.int32).reshape(-1)
+        w = np.ascontiguousarray(w, dtype=np.float32).reshape(-1)
+        p = MoePlan()
+        check(lib().moe_planner_plan(self._h, layer, ids.ctypes.data_as(ctypes.c_void_p),
+                                     w.ctypes.data_as(ctypes.c_void_p), ids.size, q,
+                                     ctypes.byref(p)), "moe_planner_plan")
+        return p
+
+    def rollback(self):
+        check(lib().moe_planner_rollback(self._h), "moe_planner_rollback")
+
+    def slot_table(self, layer):
+        import numpy as np
+        out = np.empty(self.n_experts, dtype=np.int32)
+        check(lib().moe_planner_slot_table(self._h, layer,
+                                           out.ctypes.data_as(ctypes.c_void_p)),
+              "moe_planner_slot_table")
+        return out
+
+
+def plan_dict(p):
+    """A moe_plan as plain Python lists."""
+    return {
+        "layer": p.layer, "q": p.q,
+        "selected": list(p.selected[:p.n_selected]),
+        "hits": list(p.hits[:p.n_hits]), "hit_slot": list(p.hit_slot[:p.n_hits]),
+        "misses": list(p.misses[:p.n_misses]),
+        "fills": list(zip(p.fill_expert[:p.q], p.fill_slot[:p.q])),
+        "victims": [(l, e) for l, e in zip(p.victim_layer[:p.q], p.victim_expert[:p.q])],
+        "host": list(p.host_expert[:p.n_host]),
+    }
+
+
+class ExpertCache:
+    """moe_cache_*: LRU slots in device memory filled from a pinned host pool.
+
+    host_pool  pinned uint8 tensor [n_layers * n_experts * expert_bytes]
+    dev_pool   device uint8 tensor [n_slots * expert_bytes]
+    table      device int32 tensor [n_layers, n_experts] (kept by the cache)
+    """
+
+    def __init__(self, host_pool, n_layers, n_experts, expert_bytes, dev_pool, n_slots, table):
+        self._h = ctypes.c_void_p()
+        self._keep = (host_pool, dev_pool, table)
+        check(lib().moe_cache_create(ctypes.byref(self._h), _ptr(host_pool), n_layers,
+                                     n_experts, expert_bytes, _ptr(dev_pool), n_slots,
+                                     _ptr(table)), "moe_cache_create")
+        self.n_experts = n_experts
+
+    def __del__(self):
+        if getattr(self, "_h", None):
+            lib().moe_cache_destroy(self._h)
+            self._h = None
+
+    def set_bandwidths(self, b_pcie, b_host):
+        check(lib().moe_cache_set_bandwidths(self._h, b_pcie, b_host), "set_bandwidths")
+
+    def plan(self, layer, ids, w, q):
+        import numpy as np
+        ids = np.ascontiguousarray(ids, dtype=np.int32).reshape(-1)
+        w = np.ascontiguousarray(w, dtype=np.float32).reshape(-1)
+        p = MoePlan()
+        check(lib().moe_cache_plan(self._h, layer, ids.ctypes.data_as(ctypes.c_void_p),
+                                   w.ctypes.data_as(ctypes.c_void_p), ids.size, q,
+                                   ctypes.byref(p)), "moe_cache_plan")
+        return p
+
+    def fill(self, plan, side_stream, compute_stream=None):
+        check(lib().cache_fill(self._h, ctypes.byref(plan), _stream(side_stream),
+                               _stream(compute_stream)), "cache_fill")
+
+    def release(self, plan, compute_stream=None):
+        check(lib().moe_cache_release(self._h, ctypes.byref(plan), _stream(compute_stream)),
+              "moe_cache_release")
+
+    def debug_fail_fills(self, n):
+        check(lib().moe_cache_debug_fail_fills(self._h, n), "debug_fail_fills")
+
+    def slot_table(self, layer):
+        import numpy as np
+        out = np.empty(self.n_experts, dtype=np.int32)
+        check(lib().moe_planner_slot_table(lib().moe_cache_planner(self._h), layer,
+                                           out.ctypes.data_as(ctypes.c_void_p)),
+              "moe_planner_slot_table")
+        return out
+
+
+def probe_bandwidths(pinned_host, dev, reps=3, threads=0, stream=None):
+    bp, bh = ctypes.c_double(), ctypes.c_double()
+    check(lib().moe_probe_bandwidths(_ptr(pinned_host), _ptr(dev), pinned_host.numel(), reps,
+                                     threads, _stream(stream), ctypes.byref(bp),
+                                     ctypes.byref(bh)), "moe_probe_bandwidths")
+    return bp.value, bh.value

@@ -37,6 +37,16 @@ SHAPES = {
     "dsv4_mxfp4_prefill": dict(hidden=4096, inter=2048, n_experts=256, top_k=6,
                                shared=True, wtype="mxfp4",
                                tokens=(4096, 8192, 16384), layers=1),
+    # small shapes with ragged tails (fewer than 64 vectors per row, partial
+    # tiles, odd expert counts) used by the parity tests
+    "ragged_decode": dict(hidden=800, inter=96, n_experts=20, top_k=3, shared=True,
+                          wtype="mxfp4", tokens=(1, 5, 33, 64), layers=1),
+    "ragged_prefill": dict(hidden=512, inter=256, n_experts=13, top_k=4,
+                           shared=True, wtype="mxfp4", tokens=(1, 77, 700),
+                           layers=1),
+    "small_cache": dict(hidden=256, inter=128, n_experts=32, top_k=4,
+                        shared=False, wtype="mxfp4", tokens=(1,), layers=2,
+                        slots=8, steps=64, zipf=1.1, drift=16),
     "glm_cache_decode": dict(hidden=6144, inter=2048, n_experts=256, top_k=8,
                              shared=False, wtype="mxfp4", tokens=(1,), layers=1,
                              slots=64, steps=512, zipf=1.1, drift=32),
@@ -75,11 +85,13 @@ def normal(shape, std, seed, device="cpu"):
     return out
 
 
-def router_weights(name, layer, device="cpu", seed=0):
+def router_weights(name, layer, device="cpu", seed=0, as_dtype=None):
+    """W_r [E, H]: fp32 for the tiny layer, else BF16 (or ``as_dtype``)."""
     s = SHAPES[name]
     w = normal((s["n_experts"], s["hidden"]), WEIGHT_STD,
                seed_of(name, seed, layer, _MATRIX["router"]), device)
-    return w if s["wtype"] == "f32" else w.to(torch.bfloat16)
+    dt = as_dtype or (torch.float32 if s["wtype"] == "f32" else torch.bfloat16)
+    return w.to(dt)
 
 
 def expert_weights(name, layer, expert, device="cpu", seed=0, as_dtype=None):

@@ -1,0 +1,92 @@
+"""Shared test plumbing: build one layer's inputs on the GPU, and the same
+draws as fp64 oracle inputs.  The oracle side never reads a value the HIP
+path produced: it takes the generator's fp32 / bf16 draws and applies its own
+format conversion."""
+
+import numpy as np
+import torch
+
+import synth
+from oracle import formats
+
+
+def desc_for(name, wtype=None, renorm=False):
+    from sparse_expert_execution_amd import ops
+    s = synth.SHAPES[name]
+    wt = wtype or s["wtype"]
+    if wt == "f32":
+        wt = "bf16"      # the GPU runs fp32-drawn experts as BF16 or MXFP4
+    rt = "f32" if s["wtype"] == "f32" else "bf16"
+    return ops.make_desc(s["hidden"], s["inter"], s["n_experts"], s["top_k"],
+                         has_shared=s["shared"], renorm=renorm, wtype=wt,
+                         router_wtype=rt)
+
+
+class GpuLayer:
+    """A layer's pool (all experts in slots 0..E-1), shared block and router."""
+
+    def __init__(self, name, layer=0, seed=0, wtype=None, experts=None, renorm=False,
+                 shape=None):
+        from sparse_expert_execution_amd import ops
+        self.name, self.layer, self.seed = name, layer, seed
+        s = dict(synth.SHAPES[name])
+        self.s = s
+        self.wtype = wtype or s["wtype"]
+        self.desc = desc_for(name, self.wtype, renorm)
+        off, eb = ops.expert_layout(self.desc)
+        self.expert_bytes = eb
+        E = s["n_experts"]
+        dev = "cuda"
+        self.pool = torch.zeros(E * eb, dtype=torch.uint8, device=dev)
+        which = range(E) if experts is None else experts
+        for e in which:
+            self._pack(e, self.pool[e * eb:(e + 1) * eb])
+        self.shared = None
+        if s["shared"]:
+            self.shared = torch.zeros(eb, dtype=torch.uint8, device=dev)
+            self._pack(E, self.shared)
+        self.w_router = synth.router_weights(name, layer, device=dev, seed=seed)
+        torch.cuda.synchronize()
+
+    def _pack(self, e, block):
+        from sparse_expert_execution_amd import ops
+        g, u, d = synth.expert_weights(self.name, self.layer, e, device="cuda",
+                                       seed=self.seed, as_dtype=torch.float32)
+        if self.wtype == "bf16":
+            g, u, d = (m.to(torch.bfloat16) for m in (g, u, d))
+        ops.pack_expert(self.desc, block, g, u, d)
+
+    def tokens(self, T, stream=0):
+        return synth.tokens(self.name, self.layer, T, device="cuda", seed=self.seed,
+                            stream=stream)
+
+
+def oracle_weights(name, layer, e, wtype, seed=0):
+    """(gate, up, down) as exact fp64 values of the format the GPU runs."""
+    mats = synth.expert_weights(name, layer, e, device="cuda", seed=seed,
+                                as_dtype=torch.float32)
+    out = []
+    for m in mats:
+        a = m.cpu().numpy()
+        if wtype == "bf16":
+            out.append(formats.bf16_decode(formats.bf16_round(a)))
+        elif wtype == "mxfp4":
+            out.append(formats.mxfp4_decode(*formats.mxfp4_encode(a)))
+        else:
+            out.append(a.astype(np.float64))
+    return tuple(out)
+
+
+def oracle_router(name, layer, seed=0):
+    s = synth.SHAPES[name]
+    w = synth.router_weights(name, layer, device="cuda", seed=seed,
+                             as_dtype=torch.float32).cpu().numpy()
+    if s["wtype"] == "f32":
+        return w.astype(np.float64)
+    return formats.bf16_decode(formats.bf16_round(w))
+
+
+def bf16_to_f64(x):
+    """Exact values of a BF16 generator tensor (device or host)."""
+    bits = x.detach().cpu().view(torch.int16).numpy().view(np.uint16)
+    return formats.bf16_decode(bits)

@@ -1,0 +1,408 @@
+"""GPU parity: every HIP entry point against the fp64 oracle, through the C ABI.
+
+Bars: bit-exact for MXFP4 codes, dequantised values, top-k ids (where the
+oracle's probability gap between ranks k and k+1 exceeds 1e-4), slot tables
+and merges; per-token max-abs error / max-abs reference <= 1e-2 for layer
+outputs (fp32 accumulation on the GPU).
+"""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from helpers import GpuLayer, bf16_to_f64, oracle_router, oracle_weights
+from oracle import cache as ocache
+from oracle import formats, layer as olayer
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-2
+GAP = 1e-4
+
+
+def _say(*a):
+    print("[gpu-parity]", *a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def ops():
+    from sparse_expert_execution_amd import ops as _ops
+    _ops._lib.lib()
+    return _ops
+
+
+# ---------------------------------------------------------------- formats
+def test_dequant_bit_exact_all_codes_and_scales(ops):
+    _say("dequant all bytes x scales")
+    scales = [0, 1, 100, 120, 127, 134, 254]
+    codes = np.tile(np.arange(256, dtype=np.uint8).reshape(16, 16), (len(scales), 1))
+    sc = np.repeat(np.array(scales, dtype=np.uint8), 16)
+    d_codes = torch.from_numpy(codes).cuda()
+    d_sc = torch.from_numpy(sc).cuda()
+    out = torch.empty(codes.shape[0] * 32, dtype=torch.float32, device="cuda")
+    ops.dequant_mxfp4(d_codes, d_sc, out)
+    torch.cuda.synchronize()
+    ref = formats.mxfp4_decode(codes.reshape(-1, 16), sc.reshape(-1, 1)).reshape(-1)
+    with np.errstate(over="ignore"):
+        ref32 = ref.astype(np.float32)
+    got = out.cpu().numpy()
+    assert np.array_equal(got.view(np.uint32), ref32.view(np.uint32))
+
+
+def _encode_cases():
+    rng = np.random.default_rng(1)
+    rows = [rng.standard_normal(256) * 0.02, rng.standard_normal(256),
+            rng.standard_normal(256) * 1e-30, rng.standard_normal(256) * 1e30,
+            np.zeros(256), -np.zeros(256)]
+    ties = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0] * 4) * 2.0 ** -3
+    ties[0] = 4.0 * 2.0 ** -3            # block max at 4 * 2^X pins the scale
+    rows.append(np.concatenate([ties, -ties, ties * 2 ** 20, -ties * 2 ** -100,
+                                ties * 3, ties * 7.9, ties * 1e-3, ties]))
+    sub = rng.standard_normal(256) * 2.0 ** -140   # fp32 denormals
+    rows.append(sub)
+    return np.stack(rows).astype(np.float32)
+
+
+def test_quantize_bit_exact(ops):
+    _say("quantize edge + random rows")
+    src = _encode_cases()
+    rng = np.random.default_rng(2)
+    big = (rng.standard_normal((300, 4096)) * 0.02).astype(np.float32)
+    for a in (src, big):
+        d = torch.from_numpy(a).cuda()
+        c = torch.empty((a.shape[0], a.shape[1] // 2), dtype=torch.uint8, device="cuda")
+        s = torch.empty((a.shape[0], a.shape[1] // 32), dtype=torch.uint8, device="cuda")
+        ops.quantize_mxfp4(d, c, s)
+        torch.cuda.synchronize()
+        rc, rs = formats.mxfp4_encode(a.astype(np.float64))
+        assert np.array_equal(s.cpu().numpy(), rs)
+        assert np.array_equal(c.cpu().numpy(), rc)
+
+
+def test_merge_exact(ops):
+    _say("merge")
+    rng = np.random.default_rng(3)
+    for n in (1, 7, 4096 * 16 + 3):
+        a = rng.standard_normal(n).astype(np.float32)
+        b = rng.standard_normal(n).astype(np.float32)
+        da, db = torch.from_numpy(a).cuda(), torch.from_numpy(b).cuda()
+        y = torch.empty_like(da)
+        ops.merge_partials(da, db, y)
+        ops.merge_partials(da, db, da)          # aliasing y == a
+        torch.cuda.synchronize()
+        assert np.array_equal(y.cpu().numpy(), a + b)
+        assert np.array_equal(da.cpu().numpy(), a + b)
+
+
+# ------------------------------------------------------------ MFMA layout
+@pytest.mark.parametrize("scale_mode", ["unit", "random"])
+def test_mfma_fp4_tile_layout(ops, scale_mode):
+    _say("mfma tile", scale_mode)
+    rng = np.random.default_rng(4)
+    ac = rng.integers(0, 256, size=(16, 64), dtype=np.uint8)
+    bc = rng.integers(0, 256, size=(16, 64), dtype=np.uint8)
+    if scale_mode == "unit":
+        a_s = np.full((16, 4), 127, dtype=np.uint8)
+        b_s = np.full((16, 4), 127, dtype=np.uint8)
+    else:
+        a_s = rng.integers(120, 135, size=(16, 4), dtype=np.uint8)
+        b_s = rng.integers(120, 135, size=(16, 4), dtype=np.uint8)
+    out = torch.empty((16, 16), dtype=torch.float32, device="cuda")
+    ops.mfma_fp4_tile(*(torch.from_numpy(v).cuda() for v in (ac, a_s, bc, b_s)), out)
+    torch.cuda.synchronize()
+    A = formats.mxfp4_decode(ac, a_s)
+    B = formats.mxfp4_decode(bc, b_s)
+    ref = A @ B.T
+    got = out.cpu().numpy().astype(np.float64)
+    scale = np.max(np.abs(ref))
+    err = np.max(np.abs(got - ref)) / scale
+    hint = {"transposed": np.max(np.abs(got - ref.T)) / scale}
+    assert err < 1e-6, f"mfma layout mismatch err={err} hints={hint}"
+
+
+# ----------------------------------------------------------------- router
+def _check_route(ops, name, T, renorm=False, layer=0):
+    s = synth.SHAPES[name]
+    from helpers import desc_for
+    desc = desc_for(name, renorm=renorm)
+    wr = synth.router_weights(name, layer, device="cuda")
+    x = synth.tokens(name, layer, T, device="cuda")
+    ids = torch.empty((T, s["top_k"]), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, s["top_k"]), dtype=torch.float32, device="cuda")
+    ws = ops.workspace(desc, T, 0)
+    ops.route(desc, x, wr, ids, w, ws)
+    torch.cuda.synchronize()
+    r = olayer.route(bf16_to_f64(x), oracle_router(name, layer), s["top_k"], renorm=renorm)
+    gi, gw = ids.cpu().numpy(), w.cpu().numpy()
+    clear = r["gap"] > GAP
+    assert clear.mean() > 0.5
+    assert np.array_equal(gi[clear], r["ids"][clear])
+    assert np.allclose(gw[clear], r["w"][clear], rtol=1e-4, atol=1e-7)
+    # exempt tokens: the GPU's choice must still be a valid top-k set
+    for t in np.nonzero(~clear)[0]:
+        p = r["p"][t]
+        kth = np.sort(p)[::-1][s["top_k"] - 1]
+        assert np.all(p[gi[t]] >= kth - GAP)
+    return gi
+
+
+@pytest.mark.parametrize("name,T", [("tiny", 4), ("tiny", 100), ("qwen_bf16_decode", 1),
+                                    ("qwen_bf16_decode", 8), ("dsv4_mxfp4_decode", 1),
+                                    ("dsv4_mxfp4_decode", 16), ("dsv4_mxfp4_decode", 300),
+                                    ("glm_cache_decode", 3), ("ragged_decode", 64)])
+def test_route_topk_exact(ops, name, T):
+    _say("route", name, T)
+    _check_route(ops, name, T)
+
+
+def test_route_renorm(ops):
+    _say("route renorm")
+    _check_route(ops, "qwen_bf16_decode", 8, renorm=True)
+
+
+# ----------------------------------------------------------------- decode
+def _run_decode(ops, L, x, ids, w, slot_of=None, fn="decode"):
+    T = x.shape[0]
+    y = torch.full((T, L.s["hidden"]), float("nan"), dtype=torch.float32, device="cuda")
+    mode = 1 if fn == "decode" else 2
+    ws = ops.workspace(L.desc, T, mode)
+    getattr(ops, fn)(L.desc, x, ids, w, L.pool, y, ws, slot_of=slot_of, shared=L.shared)
+    torch.cuda.synchronize()
+    return y.cpu().numpy().astype(np.float64)
+
+
+def _oracle_out(L, x, ids, w, tokens=None, include=None, prefill=False, with_shared=True):
+    s = L.s
+    tok = np.arange(x.shape[0]) if tokens is None else np.asarray(tokens)
+    xs = bf16_to_f64(x)[tok]
+    ids_t, w_t = ids[tok], w[tok].astype(np.float64)
+    inc = None if include is None else include[tok]
+    needed = np.unique(ids_t if inc is None else ids_t[inc])
+    experts = {int(e): oracle_weights(L.name, L.layer, int(e), L.wtype) for e in needed}
+    shared = None
+    if s["shared"] and with_shared:
+        shared = oracle_weights(L.name, L.layer, s["n_experts"], L.wtype)
+    return olayer.combine(xs, ids_t, w_t, experts, shared=shared, prefill=prefill,
+                          include=inc)
+
+
+def _route_gpu(ops, L, x):
+    T = x.shape[0]
+    k = L.s["top_k"]
+    ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    ops.route(L.desc, x, L.w_router, ids, w, ops.workspace(L.desc, T, 0))
+    return ids, w
+
+
+@pytest.mark.parametrize("wtype", ["bf16", "mxfp4"])
+@pytest.mark.parametrize("T", [1, 4])
+def test_decode_tiny(ops, wtype, T):
+    _say("decode tiny", wtype, T)
+    L = GpuLayer("tiny", wtype=wtype)
+    x = L.tokens(T)
+    ids, w = _route_gpu(ops, L, x)
+    y = _run_decode(ops, L, x, ids, w)
+    ref = _oracle_out(L, x, ids.cpu().numpy(), w.cpu().numpy())
+    assert olayer.row_rel_error(y, ref) < TOL
+
+
+@pytest.mark.parametrize("T", [1, 5, 33, 64])
+def test_decode_ragged_shapes(ops, T):
+    _say("decode ragged", T)
+    L = GpuLayer("ragged_decode")
+    x = L.tokens(T)
+    ids, w = _route_gpu(ops, L, x)
+    y = _run_decode(ops, L, x, ids, w)
+    ref = _oracle_out(L, x, ids.cpu().numpy(), w.cpu().numpy())
+    assert olayer.row_rel_error(y, ref) < TOL
+
+
+def test_decode_partial_over_resident_subset(ops):
+    """Non-resident experts are skipped; the two partial sums merge exactly."""
+    _say("decode partial + merge")
+    L = GpuLayer("ragged_decode")
+    T, E = 9, L.s["n_experts"]
+    x = L.tokens(T)
+    ids, w = _route_gpu(ops, L, x)
+    rng = np.random.default_rng(5)
+    resident = rng.random(E) < 0.5
+    slot_of = torch.from_numpy(np.where(resident, np.arange(E), -1).astype(np.int32)).cuda()
+    y_gpu = _run_decode(ops, L, x, ids, w, slot_of=slot_of)
+    hi, hw = ids.cpu().numpy(), w.cpu().numpy()
+    inc = resident[hi]
+    ref_gpu = _oracle_out(L, x, hi, hw, include=inc)
+    assert olayer.row_rel_error(y_gpu, ref_gpu) < TOL
+    # host side: the other subset (oracle), merged on the GPU
+    ref_host = _oracle_out(L, x, hi, hw, include=~inc, with_shared=False)
+    a = torch.from_numpy(y_gpu.astype(np.float32)).cuda()
+    b = torch.from_numpy(ref_host.astype(np.float32)).cuda()
+    out = torch.empty_like(a)
+    ops.merge_partials(a, b, out)
+    torch.cuda.synchronize()
+    full = _oracle_out(L, x, hi, hw)
+    assert olayer.row_rel_error(out.cpu().numpy(), full) < TOL
+
+
+@pytest.mark.parametrize("T", [1, 8])
+def test_decode_qwen_full_layer(ops, T):
+    _say("decode qwen full", T)
+    L = GpuLayer("qwen_bf16_decode", layer=3)
+    x = L.tokens(T)
+    ids, w = _route_gpu(ops, L, x)
+    y = _run_decode(ops, L, x, ids, w)
+    ref = _oracle_out(L, x, ids.cpu().numpy(), w.cpu().numpy())
+    assert olayer.row_rel_error(y, ref) < TOL
+
+
+@pytest.mark.parametrize("T,sample", [(1, [0]), (4, [3]), (16, [13])])
+def test_decode_dsv4_full_layer_sampled(ops, T, sample):
+    _say("decode dsv4 full", T)
+    L = GpuLayer("dsv4_mxfp4_decode", layer=7)
+    x = L.tokens(T)
+    ids, w = _route_gpu(ops, L, x)
+    y = _run_decode(ops, L, x, ids, w)
+    assert np.all(np.isfinite(y))
+    ref = _oracle_out(L, x, ids.cpu().numpy(), w.cpu().numpy(), tokens=sample)
+    assert olayer.row_rel_error(y[sample], ref) < TOL
+
+
+# ---------------------------------------------------------------- prefill
+@pytest.mark.parametrize("name,T", [("tiny", 4), ("tiny", 300), ("ragged_prefill", 1),
+                                    ("ragged_prefill", 77), ("ragged_prefill", 700)])
+def test_prefill_small(ops, name, T):
+    _say("prefill", name, T)
+    L = GpuLayer(name, wtype="mxfp4")
+    x = L.tokens(T)
+    ids, w = _route_gpu(ops, L, x)
+    y = _run_decode(ops, L, x, ids, w, fn="prefill")
+    ref = _oracle_out(L, x, ids.cpu().numpy(), w.cpu().numpy(), prefill=True)
+    assert olayer.row_rel_error(y, ref) < TOL
+
+
+def test_prefill_partial_subset(ops):
+    _say("prefill partial")
+    L = GpuLayer("ragged_prefill")
+    T, E = 200, L.s["n_experts"]
+    x = L.tokens(T)
+    ids, w = _route_gpu(ops, L, x)
+    resident = np.arange(E) % 3 != 0
+    slot_of = torch.from_numpy(np.where(resident, np.arange(E), -1).astype(np.int32)).cuda()
+    y = _run_decode(ops, L, x, ids, w, slot_of=slot_of, fn="prefill")
+    hi, hw = ids.cpu().numpy(), w.cpu().numpy()
+    ref = _oracle_out(L, x, hi, hw, include=resident[hi], prefill=True)
+    assert olayer.row_rel_error(y, ref) < TOL
+
+
+def test_prefill_dsv4_full_layer_sampled(ops):
+    _say("prefill dsv4 4096")
+    L = GpuLayer("dsv4_mxfp4_prefill")
+    T = 4096
+    x = L.tokens(T)
+    ids, w = _route_gpu(ops, L, x)
+    y = _run_decode(ops, L, x, ids, w, fn="prefill")
+    assert np.all(np.isfinite(y))
+    sample = [7, 4095]
+    ref = _oracle_out(L, x, ids.cpu().numpy(), w.cpu().numpy(), tokens=sample, prefill=True)
+    assert olayer.row_rel_error(y[sample], ref) < TOL
+
+
+# ------------------------------------------------------------ expert cache
+def test_cache_trace_fills_tables_and_merge(ops):
+    """Zipf trace through the GPU cache: slot tables equal the oracle LRU step
+    by step, and GPU partial (resident + filled) + host partial (oracle) merge
+    to the full layer output."""
+    _say("cache trace")
+    name = "small_cache"
+    s = synth.SHAPES[name]
+    E, k, slots, steps = s["n_experts"], s["top_k"], s["slots"], 40
+    layers = s["layers"]
+    Ls = [GpuLayer(name, layer=l) for l in range(layers)]
+    eb = Ls[0].expert_bytes
+    host_pool = torch.empty(layers * E * eb, dtype=torch.uint8).pin_memory()
+    for l in range(layers):
+        host_pool[l * E * eb:(l + 1) * E * eb].copy_(Ls[l].pool.cpu())
+    dev_pool = torch.zeros(slots * eb, dtype=torch.uint8, device="cuda")
+    table = torch.zeros((layers, E), dtype=torch.int32, device="cuda")
+    cache = ops.ExpertCache(host_pool, layers, E, eb, dev_pool, slots, table)
+    side = torch.cuda.Stream()
+    comp = torch.cuda.current_stream()
+    ids_tr, w_tr = synth.zipf_trace(E, k, steps, s["zipf"], s["drift"])
+    oc = ocache.LRUCache(slots)
+    rng = np.random.default_rng(6)
+    for st in range(steps):
+        layer = int(rng.integers(0, layers))
+        q = int(rng.integers(0, k + 1))
+        ids_np, w_np = ids_tr[st:st + 1], w_tr[st:st + 1]
+        plan = cache.plan(layer, ids_np, w_np, q)
+        ref_plan = oc.step(layer, ids_np, w_np, q)
+        pd = ops.plan_dict(plan)
+        assert pd["fills"] == ref_plan["fills"] and pd["hits"] == ref_plan["hits"], st
+        cache.fill(plan, side, comp)
+        L = Ls[layer]
+        x = L.tokens(1, stream=st)
+        ids = torch.from_numpy(ids_np.astype(np.int32)).cuda()
+        w = torch.from_numpy(w_np.astype(np.float32)).cuda()
+        y = torch.empty((1, s["hidden"]), dtype=torch.float32, device="cuda")
+        ws = ops.workspace(L.desc, 1, 1)
+        ops.decode(L.desc, x, ids, w, dev_pool, y, ws, slot_of=table[layer])
+        cache.release(plan, comp)
+        resident_after = oc.slot_of_expert(layer, E) >= 0
+        inc = resident_after[ids_np]
+        y_host = _oracle_out(L, x, ids_np, w_np, include=~inc)
+        yh = torch.from_numpy(y_host.astype(np.float32)).cuda()
+        ops.merge_partials(y, yh, y)
+        torch.cuda.synchronize()
+        got_table = table.cpu().numpy()
+        for l in range(layers):
+            assert np.array_equal(got_table[l], oc.slot_of_expert(l, E)), (st, l)
+        full = _oracle_out(L, x, ids_np, w_np)
+        assert olayer.row_rel_error(y.cpu().numpy(), full) < TOL, st
+
+
+def test_cache_injected_fill_failure_rolls_back(ops):
+    _say("cache injected failure")
+    name = "small_cache"
+    s = synth.SHAPES[name]
+    E, slots = s["n_experts"], s["slots"]
+    L = GpuLayer(name)
+    eb = L.expert_bytes
+    host_pool = torch.empty(E * eb, dtype=torch.uint8).pin_memory()
+    host_pool.copy_(L.pool.cpu())
+    dev_pool = torch.zeros(slots * eb, dtype=torch.uint8, device="cuda")
+    table = torch.zeros((1, E), dtype=torch.int32, device="cuda")
+    cache = ops.ExpertCache(host_pool, 1, E, eb, dev_pool, slots, table)
+    side = torch.cuda.Stream()
+    p = cache.plan(0, [1, 2, 3], [0.5, 0.3, 0.2], 3)
+    cache.fill(p, side)
+    cache.release(p)
+    before = cache.slot_table(0).copy()
+    cache.debug_fail_fills(1)
+    p = cache.plan(0, [4, 5], [0.6, 0.4], 2)
+    with pytest.raises(ops._lib.MoeError) as ei:
+        cache.fill(p, side)
+    assert ei.value.status == ops._lib.MOE_EHIP
+    assert np.array_equal(cache.slot_table(0), before)
+    torch.cuda.synchronize()
+    assert np.array_equal(table.cpu().numpy()[0], before)
+    # the cache keeps working after the failure
+    p = cache.plan(0, [4, 5], [0.6, 0.4], 2)
+    cache.fill(p, side)
+    cache.release(p)
+    torch.cuda.synchronize()
+    assert np.array_equal(table.cpu().numpy()[0], cache.slot_table(0))
+
+
+def test_bandwidth_probe_and_qstar(ops):
+    _say("probe")
+    host = torch.empty(64 << 20, dtype=torch.uint8).pin_memory()
+    dev = torch.empty(64 << 20, dtype=torch.uint8, device="cuda")
+    bp, bh = ops.probe_bandwidths(host, dev, reps=2)
+    _say(f"B_pcie={bp / 1e9:.1f} GB/s B_host={bh / 1e9:.1f} GB/s")
+    assert 1e9 < bp < 1e12 and 1e9 < bh < 1e13
+    q = ops.qstar(8, bp, bh)
+    assert q == ocache.qstar(8, bp, bh)
