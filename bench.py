@@ -1,0 +1,404 @@
+#!/usr/bin/env python3
+"""Benchmark of the routed MoE layer on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--quick]
+
+A step is one pass of the hot path over one batch: for each of the
+workload's layers, moe_route then moe_decode (or moe_prefill), back to back on
+one stream.  The headline workload is the Qwen3.6-35B-A3B-shaped BF16 decode
+layer (hidden 2048, 128 routed experts, top-8, intermediate 768) at one token,
+48 distinct layers per step; ``value`` is microseconds per token per MoE
+layer.  Inputs are synthetic (seeded N(0, 0.02) weights, N(0, 1) tokens) and
+resident in HBM before timing starts.  Other workloads (MXFP4 decode,
+prefill, expert-cache decode) are reported under ``details``.
+
+One JSON line is printed on stdout; progress goes to stderr.
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+import synth
+from sparse_expert_execution_amd import bytemodel as bm
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+HBM_PEAK = 8.0e12            # bytes/s, MI355X published
+FP4_PEAK = 10.1e15           # dense MXFP4 FLOP/s, MI355X published
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash(files):
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, "sparse_expert_execution_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_record(name, src_files):
+    """HBM traffic per launch from the committed rocprofv3 counter summary,
+    or None when the kernel sources changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"{name}.traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_hash") != kernel_source_hash(src_files):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+# --------------------------------------------------------------------------
+class Layers:
+    """All layers of one workload resident in HBM."""
+
+    def __init__(self, ops, name, n_layers, log_every=8):
+        s = synth.SHAPES[name]
+        self.s = s
+        self.name = name
+        self.desc = ops.make_desc(s["hidden"], s["inter"], s["n_experts"], s["top_k"],
+                                  has_shared=s["shared"], wtype=s["wtype"],
+                                  router_wtype="bf16")
+        _, eb = ops.expert_layout(self.desc)
+        self.expert_bytes = eb
+        E = s["n_experts"]
+        self.pools, self.shared, self.routers = [], [], []
+        t0 = time.time()
+        for l in range(n_layers):
+            pool = torch.empty(E * eb, dtype=torch.uint8, device="cuda")
+            for e in range(E):
+                g, u, d = synth.expert_weights(name, l, e, device="cuda")
+                ops.pack_expert(self.desc, pool[e * eb:(e + 1) * eb], g, u, d)
+            self.pools.append(pool)
+            if s["shared"]:
+                blk = torch.empty(eb, dtype=torch.uint8, device="cuda")
+                g, u, d = synth.expert_weights(name, l, E, device="cuda")
+                ops.pack_expert(self.desc, blk, g, u, d)
+                self.shared.append(blk)
+            else:
+                self.shared.append(None)
+            self.routers.append(synth.router_weights(name, l, device="cuda"))
+            if (l + 1) % log_every == 0:
+                torch.cuda.synchronize()
+                log(f"{name}: {l + 1}/{n_layers} layers built ({time.time() - t0:.1f}s)")
+        torch.cuda.synchronize()
+
+
+def time_decode(ops, Lw, T, steps, warmup, mode="decode"):
+    """Time `steps` passes over all layers; events around every expert call."""
+    s = Lw.s
+    n_layers = len(Lw.pools)
+    H, k = s["hidden"], s["top_k"]
+    xs = [synth.tokens(Lw.name, l, T, device="cuda") for l in range(n_layers)]
+    ids = [torch.empty((T, k), dtype=torch.int32, device="cuda") for _ in range(n_layers)]
+    ws_ = [torch.empty((T, k), dtype=torch.float32, device="cuda") for _ in range(n_layers)]
+    ys = [torch.empty((T, H), dtype=torch.float32, device="cuda") for _ in range(n_layers)]
+    rws = ops.workspace(Lw.desc, T, 0)
+    fmode = 1 if mode == "decode" else 2
+    fws = ops.workspace(Lw.desc, T, fmode)
+    fn = ops.decode if mode == "decode" else ops.prefill
+    stream = torch.cuda.current_stream()
+
+    def one_step(ev=None):
+        for l in range(n_layers):
+            ops.route(Lw.desc, xs[l], Lw.routers[l], ids[l], ws_[l], rws)
+            if ev is not None:
+                ev[l][0].record(stream)
+            fn(Lw.desc, xs[l], ids[l], ws_[l], Lw.pools[l], ys[l], fws, shared=Lw.shared[l])
+            if ev is not None:
+                ev[l][1].record(stream)
+
+    for _ in range(warmup):
+        one_step()
+    torch.cuda.synchronize()
+    # distinct experts actually touched per layer (for the algorithmic bytes)
+    distinct = [int(np.unique(i.cpu().numpy()).size) for i in ids]
+    evs = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
+            for _ in range(n_layers)] for _ in range(steps)]
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for st in range(steps):
+        one_step(evs[st])
+    t1.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t0.elapsed_time(t1)
+    call_ms = np.array([[e[0].elapsed_time(e[1]) for e in row] for row in evs])
+    return {"total_ms": total_ms, "step_ms": total_ms / steps, "call_ms": call_ms,
+            "distinct": distinct, "ids": [i.cpu().numpy() for i in ids]}
+
+
+def decode_record(ops, Lw, T, steps, warmup):
+    s = Lw.s
+    r = time_decode(ops, Lw, T, steps, warmup)
+    n_layers = len(Lw.pools)
+    H, I, E = s["hidden"], s["inter"], s["n_experts"]
+    route_bytes = bm.router_bytes(H, E, "bf16")
+    call_bytes = [bm.decode_call_bytes(H, I, E, s["wtype"], T, d, shared=s["shared"],
+                                       route=False) for d in r["distinct"]]
+    step_bytes = sum(call_bytes) + n_layers * route_bytes
+    step_s = r["step_ms"] * 1e-3
+    mean_call_s = float(np.mean(r["call_ms"])) * 1e-3
+    achieved = float(np.mean(call_bytes)) / mean_call_s
+    return {
+        "tokens": T, "layers": n_layers,
+        "us_per_token_per_layer": step_s * 1e6 / (n_layers * T),
+        "us_per_token_all_layers": step_s * 1e6 / T,
+        "step_ms": r["step_ms"],
+        "hbm_GBps_step": step_bytes / step_s / 1e9,
+        "hbm_frac_step": step_bytes / step_s / HBM_PEAK,
+        "decode_call_us": mean_call_s * 1e6,
+        "decode_call_bytes": float(np.mean(call_bytes)),
+        "decode_call_GBps": achieved / 1e9,
+        "decode_call_frac": achieved / HBM_PEAK,
+        "mean_distinct_experts": float(np.mean(r["distinct"])),
+    }
+
+
+def prefill_record(ops, Lw, T, steps, warmup):
+    s = Lw.s
+    r = time_decode(ops, Lw, T, steps, warmup, mode="prefill")
+    H, I, E, k = s["hidden"], s["inter"], s["n_experts"], s["top_k"]
+    pairs = T * (k + 1)
+    flops = bm.expert_flops(H, I, pairs)
+    distinct = r["distinct"][0] + (1 if s["shared"] else 0)
+    wbytes = distinct * bm.expert_bytes(H, I, "mxfp4")
+    io_bytes = T * H * 2 + T * H * 4
+    call_s = float(np.mean(r["call_ms"])) * 1e-3
+    step_s = r["step_ms"] * 1e-3
+    alg_bytes = wbytes + io_bytes
+    ai = flops / alg_bytes
+    bound = min(FP4_PEAK, ai * HBM_PEAK)
+    return {
+        "tokens": T, "tokens_per_s": T / step_s, "step_ms": r["step_ms"],
+        "prefill_call_us": call_s * 1e6,
+        "expert_tflops": flops / call_s / 1e12,
+        "mfma_frac_of_fp4_peak": flops / call_s / FP4_PEAK,
+        "arithmetic_intensity": ai,
+        "roofline_bound_tflops": bound / 1e12,
+        "roofline_frac": (flops / call_s) / bound,
+        "hbm_GBps_call": alg_bytes / call_s / 1e9,
+    }
+
+
+def cache_record(ops, steps_limit=None):
+    """Expert-cache decode: 64 LRU slots over a 256-expert pinned host pool,
+    Zipf(1.1) trace drifting every 32 steps, q = q* from the measured
+    bandwidths.  Host partial sums are placeholders of the right shape copied
+    from pinned memory and merged (the host-side expert kernel is not part of
+    this path)."""
+    name = "glm_cache_decode"
+    s = synth.SHAPES[name]
+    H, I, E, k, slots = s["hidden"], s["inter"], s["n_experts"], s["top_k"], s["slots"]
+    steps = s["steps"] if steps_limit is None else steps_limit
+    desc = ops.make_desc(H, I, E, k, wtype="mxfp4", router_wtype="bf16")
+    _, eb = ops.expert_layout(desc)
+    host_pool = torch.empty(E * eb, dtype=torch.uint8).pin_memory()
+    stage = torch.empty(eb, dtype=torch.uint8, device="cuda")
+    for e in range(E):
+        g, u, d = synth.expert_weights(name, 0, e, device="cuda")
+        ops.pack_expert(desc, stage, g, u, d)
+        host_pool[e * eb:(e + 1) * eb].copy_(stage)
+    dev_pool = torch.empty(slots * eb, dtype=torch.uint8, device="cuda")
+    table = torch.empty((1, E), dtype=torch.int32, device="cuda")
+    probe_dev = torch.empty(eb * 4, dtype=torch.uint8, device="cuda")
+    bp, bh = ops.probe_bandwidths(host_pool[:eb * 4], probe_dev, reps=3)
+    cache = ops.ExpertCache(host_pool, 1, E, eb, dev_pool, slots, table)
+    cache.set_bandwidths(bp, bh)
+    ids_tr, w_tr = synth.zipf_trace(E, k, steps, s["zipf"], s["drift"])
+    xs = synth.tokens(name, 0, steps, device="cuda")
+    d_ids = torch.from_numpy(ids_tr).cuda()
+    d_w = torch.from_numpy(w_tr).cuda()
+    y = torch.empty((1, H), dtype=torch.float32, device="cuda")
+    host_part = torch.zeros((steps, H), dtype=torch.float32).pin_memory()
+    dev_part = torch.empty((1, H), dtype=torch.float32, device="cuda")
+    ws = ops.workspace(desc, 1, 1)
+    side = torch.cuda.Stream()
+    comp = torch.cuda.current_stream()
+    hits = misses = fills = 0
+    qs = []
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.time()
+    t_start.record(comp)
+    for st in range(steps):
+        plan = cache.plan(0, ids_tr[st], w_tr[st], -1)
+        hits += plan.n_hits
+        misses += plan.n_misses
+        fills += plan.q
+        qs.append(plan.q)
+        cache.fill(plan, side, comp)
+        ops.decode(desc, xs[st:st + 1], d_ids[st:st + 1], d_w[st:st + 1], dev_pool, y, ws,
+                   slot_of=table[0])
+        dev_part.copy_(host_part[st:st + 1], non_blocking=True)
+        ops.merge_partials(y, dev_part, y)
+        cache.release(plan, comp)
+    t_end.record(comp)
+    torch.cuda.synchronize()
+    wall = time.time() - wall0
+    ms = t_start.elapsed_time(t_end)
+    return {
+        "steps": steps, "slots": slots, "us_per_step": ms * 1e3 / steps,
+        "wall_us_per_step": wall * 1e6 / steps,
+        "hits": hits, "misses": misses, "filled": fills,
+        "miss_rate": misses / max(1, hits + misses),
+        "q_hist": np.bincount(np.array(qs), minlength=k + 1).tolist(),
+        "b_pcie_GBps": bp / 1e9, "b_host_GBps": bh / 1e9,
+        "fill_GBps": fills * eb / (ms * 1e-3) / 1e9,
+    }
+
+
+# --------------------------------------------------------------------------
+def cpu_baseline(name, T, n_layers_sample, min_seconds=10.0):
+    """The fp64 oracle on the host cores: route + combine of the first
+    ``n_layers_sample`` layers at T tokens, repeated until min_seconds."""
+    import threadpoolctl
+    from oracle import formats, layer as olayer
+    s = synth.SHAPES[name]
+    prepared = []
+    for l in range(n_layers_sample):
+        x = synth.tokens(name, l, T, device="cuda")
+        bits = x.cpu().view(torch.int16).numpy().view(np.uint16)
+        xf = formats.bf16_decode(bits)
+        wr = synth.router_weights(name, l, device="cuda", as_dtype=torch.float32).cpu().numpy()
+        wr = formats.bf16_decode(formats.bf16_round(wr))
+        r = olayer.route(xf, wr, s["top_k"])
+        experts = {}
+        for e in np.unique(r["ids"]):
+            mats = synth.expert_weights(name, l, int(e), device="cuda", as_dtype=torch.float32)
+            conv = []
+            for m in mats:
+                a = m.cpu().numpy()
+                conv.append(formats.bf16_decode(formats.bf16_round(a)) if s["wtype"] == "bf16"
+                            else formats.mxfp4_decode(*formats.mxfp4_encode(a)))
+            experts[int(e)] = tuple(conv)
+        prepared.append((xf, wr, experts))
+    info = threadpoolctl.threadpool_info()
+    threads = max([i.get("num_threads", 1) for i in info] or [1])
+    reps = 0
+    t0 = time.time()
+    while True:
+        for xf, wr, experts in prepared:
+            y, _ = olayer.moe_layer(xf, wr, experts, s["top_k"])
+        reps += 1
+        if time.time() - t0 >= min_seconds:
+            break
+    el = time.time() - t0
+    per = el / (reps * n_layers_sample * T)
+    return {"value": per * 1e6, "unit": "us/token/layer", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{name} T={T}: route + combine of {n_layers_sample} layers "
+                      f"(fp64 NumPy), repeated {reps}x over {el:.1f}s; weights decoded "
+                      f"to fp64 before timing"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--quick", action="store_true", help="headline workload only")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: the layer runs on a single MI355X; "
+              "multi-GPU sharding is not part of this build (use --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    from sparse_expert_execution_amd import ops
+    ops._lib.lib()
+    torch.cuda.set_device(0)
+
+    details = {}
+    name = "qwen_bf16_decode"
+    s = synth.SHAPES[name]
+    log("building", name)
+    Lq = Layers(ops, name, s["layers"], log_every=16)
+    log("timing", name, "T=1")
+    head = decode_record(ops, Lq, 1, args.steps, args.warmup)
+    log(json.dumps(head))
+    if not args.quick:
+        details["qwen_bf16_decode_T8"] = decode_record(ops, Lq, 8, args.steps, args.warmup)
+        log("T=8", json.dumps(details["qwen_bf16_decode_T8"]))
+    del Lq
+    torch.cuda.empty_cache()
+
+    if not args.quick:
+        try:
+            name2 = "dsv4_mxfp4_decode"
+            log("building", name2)
+            Ld = Layers(ops, name2, synth.SHAPES[name2]["layers"], log_every=8)
+            for T in (1, 4, 16):
+                details[f"dsv4_mxfp4_decode_T{T}"] = decode_record(ops, Ld, T, args.steps,
+                                                                   args.warmup)
+                log(f"dsv4 T={T}", json.dumps(details[f"dsv4_mxfp4_decode_T{T}"]))
+            del Ld
+            torch.cuda.empty_cache()
+        except Exception as ex:  # keep the headline line
+            details["dsv4_mxfp4_decode_error"] = repr(ex)
+        try:
+            name3 = "dsv4_mxfp4_prefill"
+            log("building", name3)
+            Lp = Layers(ops, name3, 1)
+            for T in (4096, 8192, 16384):
+                details[f"prefill_T{T}"] = prefill_record(ops, Lp, T, max(3, args.steps // 4),
+                                                          2)
+                log(f"prefill T={T}", json.dumps(details[f"prefill_T{T}"]))
+            del Lp
+            torch.cuda.empty_cache()
+        except Exception as ex:
+            details["prefill_error"] = repr(ex)
+        try:
+            log("cache decode trace")
+            details["glm_cache_decode"] = cache_record(ops)
+            log(json.dumps(details["glm_cache_decode"]))
+        except Exception as ex:
+            details["glm_cache_decode_error"] = repr(ex)
+
+    cpu = None
+    if not args.no_cpu:
+        log("cpu baseline (oracle)")
+        cpu = cpu_baseline("qwen_bf16_decode", 1, 4)
+        log(json.dumps(cpu))
+
+    traffic = traffic_record("decode_qwen_bf16_T1", ["decode.hip", "device.hpp"])
+    out = {
+        "metric": "MoE layer decode us/token (HBM GB/s %peak); prefill tokens/s (MFMA %peak)",
+        "value": head["us_per_token_per_layer"],
+        "unit": "us/token/layer",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": head["step_ms"],
+        "higher_is_better": False, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "Qwen3.6-35B-A3B-shaped BF16 MoE decode layer, 1 token, "
+                               "48 distinct layers per step (route + expert FFNs + combine)",
+                   "hidden": 2048, "inter": 768, "n_experts": 128, "top_k": 8,
+                   "tokens": 1, "layers": 48},
+        "roofline": {"bound": "hbm", "kernel": "moe_decode (gate/up + down kernels)",
+                     "achieved": head["decode_call_GBps"], "peak": HBM_PEAK / 1e9,
+                     "unit": "GB/s", "frac": head["decode_call_frac"],
+                     "traffic": traffic},
+        "hbm_GBps_whole_step": head["hbm_GBps_step"],
+        "hbm_frac_whole_step": head["hbm_frac_step"],
+        "cpu_baseline": cpu,
+        "details": details,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
