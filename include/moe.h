@@ -85,12 +85,20 @@ typedef struct moe_desc {
  *          [2] up codes [I][H/2],   [3] up scales [I][H/32],
  *          [4] down codes [H][I/2], [5] down scales [H][I/32].
  * Section offsets are 16-byte aligned; *bytes is a multiple of 256.
+ * moe_pack_expert writes this layout.
  * Returns MOE_EINVAL for a bad descriptor. */
 int moe_expert_layout(const moe_desc* desc, size_t offsets[6], size_t* bytes);
 
 /* Workspace bytes a call needs (0 if none).  mode: 0 = moe_route,
- * 1 = moe_decode, 2 = moe_prefill, for T tokens.  Returns 0 and sets the
- * error text for an invalid descriptor or T. */
+ * 1 = moe_decode / moe_route_decode, 2 = moe_prefill, for T tokens.  Returns
+ * 0 and sets the error text for an invalid descriptor or T.  Route and decode
+ * workspaces start with a header of counters (256 bytes for route, 1024 for
+ * decode) that must be zero before a workspace's first use; every call leaves
+ * it zero again.  A workspace must not be used by two calls that can run
+ * concurrently.  Decode header word 128 is set to 1 if a wait inside the
+ * kernel expired (only possible on an oversubscribed device); setting word
+ * 160 to non-zero makes the kernel record phase timestamps (100 MHz clock,
+ * uint64) from word 192 on. */
 #define MOE_MODE_ROUTE 0
 #define MOE_MODE_DECODE 1
 #define MOE_MODE_PREFILL 2
@@ -122,9 +130,10 @@ int moe_route(const moe_desc* desc, const void* x, const void* w_router,
  * FFN_e(x) = W_down (silu(W_gate x) * (W_up x)), silu(z) = z / (1 + e^-z),
  * fp32 accumulation, x as given (BF16), h in fp32.  Only experts with a slot
  * contribute: y is the partial sum over the resident subset (the GPU side of
- * the pages' exact split); non-resident pairs are skipped.  Terms are added
- * in a fixed order (routed experts in first-appearance order, then shared),
- * so results are deterministic.
+ * the pages' exact split); non-resident pairs are skipped.  Each workgroup
+ * handles one expert and a slice of I and adds its share into y with fp32
+ * atomics, so the summation order (and the last bits of y) can differ
+ * between runs.
  *   x              device [T][H] BF16;   1 <= T <= MOE_DECODE_MAX_T
  *   ids, w         device [T][k] (from moe_route or the caller)
  *   slot_of_expert device [E] int32: slot holding expert e, -1 = not
@@ -142,6 +151,19 @@ int moe_decode(const moe_desc* desc, const void* x, int32_t T,
                const int32_t* slot_of_expert, const void* slot_pool,
                const void* shared_expert, float* y, void* ws, size_t ws_bytes,
                void* stream);
+
+/* moe_route_decode: moe_route followed by moe_decode as one call (one
+ * persistent kernel for T <= 4): the router's ids and w are written out as by
+ * moe_route (the host side of a miss split needs them) and y as by
+ * moe_decode.  Same arguments as moe_decode plus w_router (device, [E][H] in
+ * desc->router_wtype); ids and w are outputs.  ws: moe_workspace_bytes(..,
+ * MOE_MODE_DECODE).  Two kernels: the router (its workgroups also clear y)
+ * and the expert kernel. */
+int moe_route_decode(const moe_desc* desc, const void* x, const void* w_router,
+                     int32_t T, int32_t* ids, float* w,
+                     const int32_t* slot_of_expert, const void* slot_pool,
+                     const void* shared_expert, float* y, void* ws,
+                     size_t ws_bytes, void* stream);
 
 /* moe_prefill: the same layer for long token batches (MXFP4 weights only).
  * Pairs are counting-sorted by expert; x and h are quantised to MXFP4 on the
@@ -173,6 +195,16 @@ int moe_quantize_mxfp4(const float* src, int32_t rows, int32_t K,
                        int64_t src_ld, uint8_t* codes, uint8_t* scales,
                        void* stream);
 
+/* moe_pack_expert: write one expert into its block (dst, device, 256-byte
+ * aligned, moe_expert_layout bytes) from gate [I][H], up [I][H], down [H][I]
+ * (device, row-major, src_type MOE_WTYPE_F32 or MOE_WTYPE_BF16).  BF16
+ * experts: values rounded to BF16 (nearest even) if given as fp32.  MXFP4
+ * experts: quantised with the encoder of moe_quantize_mxfp4 (blocks along
+ * K = H for gate/up, K = I for down).  Host and device blocks share this
+ * layout, so the same bytes serve the pinned pool and the slots. */
+int moe_pack_expert(const moe_desc* desc, const void* gate, const void* up,
+                    const void* down, int32_t src_type, void* dst, void* stream);
+
 /* moe_debug_dequant_mxfp4: n_blocks MXFP4 blocks (codes 16 B each, one scale
  * byte each) -> 32 * n_blocks floats, value e2m1(code) * 2^(s-127) computed
  * by the same in-register decoder the expert kernels use.  Test hook. */
@@ -187,6 +219,14 @@ int moe_debug_dequant_mxfp4(const uint8_t* codes, const uint8_t* scales,
 int moe_debug_mfma_fp4_tile(const uint8_t* a_codes, const uint8_t* a_scales,
                             const uint8_t* b_codes, const uint8_t* b_scales,
                             float* out, void* stream);
+
+/* moe_debug_read_probe: read `bytes` (multiple of 16) of device memory with
+ * 16-byte loads from `blocks` workgroups of 256 threads, 8 loads in flight
+ * per thread; writes nothing unless a checksum hits a magic value.  Timed by
+ * the caller to measure the attainable HBM read rate the roofline fractions
+ * can be compared with. */
+int moe_debug_read_probe(const void* buf, size_t bytes, int32_t blocks,
+                         uint32_t* out, void* stream);
 
 /* ---- q* split ---------------------------------------------------------- */
 /* Number of the m cache misses to fill into GPU slots so that the PCIe fills

@@ -31,8 +31,8 @@ PLAN_MAX = 256
 # every symbol include/moe.h declares
 EXPORTS = (
     "moe_expert_layout", "moe_workspace_bytes", "moe_route", "moe_decode",
-    "moe_prefill", "moe_merge_partials", "moe_quantize_mxfp4",
-    "moe_debug_dequant_mxfp4", "moe_debug_mfma_fp4_tile", "moe_qstar",
+    "moe_route_decode", "moe_prefill", "moe_merge_partials", "moe_quantize_mxfp4",
+    "moe_pack_expert", "moe_debug_dequant_mxfp4", "moe_debug_mfma_fp4_tile", "moe_debug_read_probe", "moe_qstar",
     "moe_planner_create", "moe_planner_destroy", "moe_planner_set_bandwidths",
     "moe_planner_plan", "moe_planner_rollback", "moe_planner_slot_table",
     "moe_cache_create", "moe_cache_destroy", "moe_cache_set_bandwidths",
@@ -91,10 +91,13 @@ def lib():
         "moe_route": (ctypes.c_int, [DP, P, P, I32, P, P, P, SZ, P]),
         "moe_decode": (ctypes.c_int, [DP, P, I32, P, P, P, P, P, P, P, SZ, P]),
         "moe_prefill": (ctypes.c_int, [DP, P, I32, P, P, P, P, P, P, P, SZ, P]),
+        "moe_route_decode": (ctypes.c_int, [DP, P, P, I32, P, P, P, P, P, P, P, SZ, P]),
         "moe_merge_partials": (ctypes.c_int, [P, P, P, SZ, P]),
         "moe_quantize_mxfp4": (ctypes.c_int, [P, I32, I32, I64, P, P, P]),
+        "moe_pack_expert": (ctypes.c_int, [DP, P, P, P, I32, P, P]),
         "moe_debug_dequant_mxfp4": (ctypes.c_int, [P, P, I64, P, P]),
         "moe_debug_mfma_fp4_tile": (ctypes.c_int, [P, P, P, P, P, P]),
+        "moe_debug_read_probe": (ctypes.c_int, [P, SZ, I32, P, P]),
         "moe_qstar": (I32, [I32, D, D]),
         "moe_planner_create": (ctypes.c_int, [ctypes.POINTER(P), I32, I32, I32]),
         "moe_planner_destroy": (None, [P]),

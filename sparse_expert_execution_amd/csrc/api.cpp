@@ -11,6 +11,9 @@
 #include "error.hpp"
 #include "kernels.hpp"
 
+// tokens per decode launch (the kernel keeps per-token state in registers)
+#define MOE_DECODE_CHUNK 16
+
 namespace moe {
 
 int hip_status(hipError_t err, const char* what) {
@@ -92,6 +95,22 @@ PrefillWs prefill_ws(const moe_desc* d, int T) {
   return w;
 }
 
+// route workspace: [0, 256) ticket counter, then router logits z [T][E].
+// decode workspace: [0, 1024) counters, then the plan, z and h [T*k + T][I].
+// Counters must be zero before the first use; every call leaves them zero.
+struct RouteWs {
+  size_t plan, z, h, total;
+};
+constexpr size_t kDecodeHeader = 1024;
+RouteWs route_ws(const moe_desc* d, int T, bool decode) {
+  RouteWs w;
+  w.plan = kDecodeHeader;
+  w.z = decode ? align_up(w.plan + moe::decode_plan_bytes()) : kAlign;
+  w.h = align_up(w.z + (size_t)T * d->n_experts * 4);
+  w.total = decode ? align_up(w.h + (size_t)(T * d->top_k + T) * d->inter * 4) : w.h;
+  return w;
+}
+
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
 hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
@@ -113,9 +132,9 @@ size_t moe_workspace_bytes(const moe_desc* desc, int32_t T, int32_t mode) {
   if (T < 0) { set_error(MOE_EINVAL, "T < 0"); return 0; }
   switch (mode) {
     case MOE_MODE_ROUTE:
-      return align_up((size_t)T * desc->n_experts * 4);
+      return route_ws(desc, T, false).total;
     case MOE_MODE_DECODE:
-      return align_up((size_t)(T * desc->top_k + T) * desc->inter * 4);
+      return route_ws(desc, T, true).total;
     case MOE_MODE_PREFILL:
       return prefill_ws(desc, T).total;
     default:
@@ -131,17 +150,24 @@ int moe_route(const moe_desc* desc, const void* x, const void* w_router, int32_t
   if (T == 0) return MOE_OK;
   if (T < 0) return set_error(MOE_EINVAL, "T < 0");
   if (!x || !w_router || !ids || !w) return set_error(MOE_EINVAL, "null pointer");
-  const size_t need = moe_workspace_bytes(desc, T, MOE_MODE_ROUTE);
-  if (!ws || ws_bytes < need)
-    return set_error(MOE_EWORKSPACE, "route workspace %zu < %zu bytes", ws_bytes, need);
-  const int rf32 = desc->router_wtype == MOE_WTYPE_F32;
-  if (T <= 64 && desc->hidden / (rf32 ? 4 : 8) > 64 * 16)
-    return set_error(MOE_EUNSUPPORTED, "hidden %d too wide for the decode router", desc->hidden);
+  const RouteWs L = route_ws(desc, T, false);
+  if (!ws || ws_bytes < L.total || !aligned(ws, 256))
+    return set_error(MOE_EWORKSPACE, "route workspace %zu < %zu bytes (or not 256-aligned)",
+                     ws_bytes, L.total);
   if (!aligned(x, 16) || !aligned(w_router, 16))
     return set_error(MOE_EINVAL, "x and w_router must be 16-byte aligned");
-  return hip_status(moe::launch_route(x, w_router, rf32, T, desc->hidden, desc->n_experts,
-                                      desc->top_k, desc->renorm_topk, static_cast<float*>(ws), ids,
-                                      w, as_stream(stream)),
+  const int rf32 = desc->router_wtype == MOE_WTYPE_F32;
+  uint8_t* b = static_cast<uint8_t*>(ws);
+  float* z = reinterpret_cast<float*>(b + L.z);
+  if (T <= MOE_DECODE_MAX_T && moe::route_small_supported(rf32, desc->hidden))
+    return hip_status(moe::launch_route_small(x, w_router, rf32, T, desc->hidden,
+                                              desc->n_experts, desc->top_k, desc->renorm_topk, z,
+                                              reinterpret_cast<unsigned*>(b), ids, w,
+                                              as_stream(stream)),
+                      "moe_route");
+  return hip_status(moe::launch_route_large(x, w_router, rf32, T, desc->hidden, desc->n_experts,
+                                            desc->top_k, desc->renorm_topk, z, ids, w,
+                                            as_stream(stream)),
                     "moe_route");
 }
 
@@ -162,30 +188,72 @@ static int check_ffn_args(const moe_desc* desc, const void* x, int32_t T, const 
   return MOE_OK;
 }
 
+static int decode_impl(const moe_desc* desc, const void* x, const void* w_router, int32_t T,
+                       int32_t* ids, float* w, const int32_t* slot_of_expert,
+                       const void* slot_pool, const void* shared_expert, float* y, void* ws,
+                       size_t ws_bytes, void* stream) {
+  if (T < 0 || T > MOE_DECODE_MAX_T || T * desc->top_k > 1024)
+    return set_error(MOE_EINVAL, "decode T %d outside [1, %d] or T*k > 1024", T, MOE_DECODE_MAX_T);
+  if (!moe::decode_shape_supported(desc->wtype, desc->hidden, desc->inter))
+    return set_error(MOE_EUNSUPPORTED, "decode shape H=%d I=%d not compiled", desc->hidden,
+                     desc->inter);
+  const RouteWs L = route_ws(desc, T, true);
+  if (!ws || ws_bytes < L.total || !aligned(ws, 256))
+    return set_error(MOE_EWORKSPACE, "decode workspace %zu < %zu bytes (or not 256-aligned)",
+                     ws_bytes, L.total);
+  uint8_t* b = static_cast<uint8_t*>(ws);
+  size_t off[6], bytes;
+  layout(desc, off, &bytes);
+  moe::FlowLaunch f;
+  f.x = x; f.w_router = w_router; f.router_f32 = desc->router_wtype == MOE_WTYPE_F32;
+  f.renorm = desc->renorm_topk; f.ids = ids; f.w = w; f.slot_of = slot_of_expert;
+  f.pool = slot_pool; f.shared = shared_expert;
+  f.hdr = reinterpret_cast<unsigned*>(b);
+  f.plan = b + L.plan;
+  f.z = reinterpret_cast<float*>(b + L.z);
+  f.h = reinterpret_cast<float*>(b + L.h);
+  f.y = y; f.expert_bytes = (int64_t)bytes;
+  for (int i = 0; i < 6; ++i) f.off[i] = (int64_t)off[i];
+  f.H = desc->hidden; f.I = desc->inter; f.E = desc->n_experts; f.k = desc->top_k;
+  f.wtype = desc->wtype;
+  // one launch per group of at most MOE_DECODE_CHUNK tokens, in stream order
+  const int H = desc->hidden, k = desc->top_k;
+  for (int t0 = 0; t0 < T; t0 += MOE_DECODE_CHUNK) {
+    f.T = T - t0 < MOE_DECODE_CHUNK ? T - t0 : MOE_DECODE_CHUNK;
+    f.x = static_cast<const uint16_t*>(x) + (size_t)t0 * H;
+    f.ids = ids + (size_t)t0 * k;
+    f.w = w + (size_t)t0 * k;
+    f.y = y + (size_t)t0 * H;
+    const int st = hip_status(moe::launch_decode_flow(f, as_stream(stream)),
+                              w_router ? "moe_route_decode" : "moe_decode");
+    if (st) return st;
+  }
+  return MOE_OK;
+}
+
 int moe_decode(const moe_desc* desc, const void* x, int32_t T, const int32_t* ids, const float* w,
                const int32_t* slot_of_expert, const void* slot_pool, const void* shared_expert,
                float* y, void* ws, size_t ws_bytes, void* stream) {
   if (T == 0) return check_desc(desc);
   int st = check_ffn_args(desc, x, T, ids, w, slot_pool, shared_expert, y);
   if (st) return st;
-  if (T < 0 || T > MOE_DECODE_MAX_T || T * desc->top_k > 1024)
-    return set_error(MOE_EINVAL, "decode T %d outside [1, %d] or T*k > 1024", T, MOE_DECODE_MAX_T);
-  if (!moe::decode_shape_supported(desc->wtype, desc->hidden, desc->inter))
-    return set_error(MOE_EUNSUPPORTED, "decode shape H=%d I=%d not compiled", desc->hidden,
-                     desc->inter);
-  const size_t need = moe_workspace_bytes(desc, T, MOE_MODE_DECODE);
-  if (!ws || ws_bytes < need || !aligned(ws, 16))
-    return set_error(MOE_EWORKSPACE, "decode workspace %zu < %zu bytes", ws_bytes, need);
-  moe::DecodeLaunch d;
-  size_t off[6], bytes;
-  layout(desc, off, &bytes);
-  d.x = x; d.ids = ids; d.w = w; d.slot_of = slot_of_expert; d.pool = slot_pool;
-  d.shared = shared_expert; d.h = static_cast<float*>(ws); d.y = y;
-  d.expert_bytes = (int64_t)bytes;
-  for (int i = 0; i < 6; ++i) d.off[i] = (int64_t)off[i];
-  d.T = T; d.H = desc->hidden; d.I = desc->inter; d.E = desc->n_experts; d.k = desc->top_k;
-  d.wtype = desc->wtype;
-  return hip_status(moe::launch_decode(d, as_stream(stream)), "moe_decode");
+  return decode_impl(desc, x, nullptr, T, const_cast<int32_t*>(ids), const_cast<float*>(w),
+                     slot_of_expert, slot_pool, shared_expert, y, ws, ws_bytes, stream);
+}
+
+int moe_route_decode(const moe_desc* desc, const void* x, const void* w_router, int32_t T,
+                     int32_t* ids, float* w, const int32_t* slot_of_expert,
+                     const void* slot_pool, const void* shared_expert, float* y, void* ws,
+                     size_t ws_bytes, void* stream) {
+  if (T == 0) return check_desc(desc);
+  int st = check_ffn_args(desc, x, T, ids, w, slot_pool, shared_expert, y);
+  if (st) return st;
+  if (!w_router) return set_error(MOE_EINVAL, "w_router is null");
+  if (!aligned(w_router, 16)) return set_error(MOE_EINVAL, "w_router must be 16-byte aligned");
+  if (!moe::route_small_supported(desc->router_wtype == MOE_WTYPE_F32, desc->hidden))
+    return set_error(MOE_EUNSUPPORTED, "hidden %d too wide for the decode router", desc->hidden);
+  return decode_impl(desc, x, w_router, T, ids, w, slot_of_expert, slot_pool, shared_expert, y,
+                     ws, ws_bytes, stream);
 }
 
 int moe_prefill(const moe_desc* desc, const void* x, int32_t T, const int32_t* ids, const float* w,
@@ -238,9 +306,41 @@ int moe_quantize_mxfp4(const float* src, int32_t rows, int32_t K, int64_t src_ld
     return set_error(MOE_EINVAL, "bad shape rows=%d K=%d ld=%lld", rows, K, (long long)src_ld);
   if (!aligned(src, 16) || !aligned(codes, 16))
     return set_error(MOE_EINVAL, "src and codes must be 16-byte aligned");
-  return hip_status(moe::launch_quantize_mxfp4(src, rows, K, src_ld, codes, scales,
+  return hip_status(moe::launch_quantize_mxfp4(src, 0, rows, K, src_ld, codes, scales,
                                                as_stream(stream)),
                     "moe_quantize_mxfp4");
+}
+
+int moe_pack_expert(const moe_desc* desc, const void* gate, const void* up, const void* down,
+                    int32_t src_type, void* dst, void* stream) {
+  int st = check_desc(desc);
+  if (st) return st;
+  if (!gate || !up || !down || !dst) return set_error(MOE_EINVAL, "null pointer");
+  if (src_type != MOE_WTYPE_F32 && src_type != MOE_WTYPE_BF16)
+    return set_error(MOE_EUNSUPPORTED, "source type %d not supported", src_type);
+  if (!aligned(gate, 16) || !aligned(up, 16) || !aligned(down, 16) || !aligned(dst, 256))
+    return set_error(MOE_EINVAL, "sources need 16-byte and dst 256-byte alignment");
+  size_t off[6], bytes;
+  layout(desc, off, &bytes);
+  const int H = desc->hidden, I = desc->inter;
+  const int sb = src_type == MOE_WTYPE_BF16;
+  uint8_t* b = static_cast<uint8_t*>(dst);
+  hipStream_t s = as_stream(stream);
+  hipError_t err;
+  if (desc->wtype == MOE_WTYPE_BF16) {
+    err = moe::launch_pack_bf16(gate, sb, I, H, reinterpret_cast<uint16_t*>(b + off[0]), s);
+    if (err == hipSuccess)
+      err = moe::launch_pack_bf16(up, sb, I, H, reinterpret_cast<uint16_t*>(b + off[1]), s);
+    if (err == hipSuccess)
+      err = moe::launch_pack_bf16(down, sb, H, I, reinterpret_cast<uint16_t*>(b + off[2]), s);
+  } else {
+    err = moe::launch_quantize_mxfp4(gate, sb, I, H, H, b + off[0], b + off[1], s);
+    if (err == hipSuccess)
+      err = moe::launch_quantize_mxfp4(up, sb, I, H, H, b + off[2], b + off[3], s);
+    if (err == hipSuccess)
+      err = moe::launch_quantize_mxfp4(down, sb, H, I, I, b + off[4], b + off[5], s);
+  }
+  return hip_status(err, "moe_pack_expert");
 }
 
 int moe_debug_dequant_mxfp4(const uint8_t* codes, const uint8_t* scales, int64_t n_blocks,
@@ -263,6 +363,14 @@ int moe_debug_mfma_fp4_tile(const uint8_t* a_codes, const uint8_t* a_scales,
   return hip_status(moe::launch_mfma_fp4_tile(a_codes, a_scales, b_codes, b_scales, out,
                                               as_stream(stream)),
                     "moe_debug_mfma_fp4_tile");
+}
+
+int moe_debug_read_probe(const void* buf, size_t bytes, int32_t blocks, uint32_t* out,
+                         void* stream) {
+  if (!buf || !out || blocks < 1 || !aligned(buf, 16))
+    return set_error(MOE_EINVAL, "bad read-probe arguments");
+  return hip_status(moe::launch_read_probe(buf, bytes, blocks, out, as_stream(stream)),
+                    "moe_debug_read_probe");
 }
 
 }  // extern "C"

@@ -160,3 +160,137 @@ __device__ __forceinline__ uint4 ldg16(const void* p) {
 }
 
 }  // namespace moe
+
+namespace moe {
+
+// ---- DPP wave reductions (results identical in every lane) ----------------
+// Butterflies inside each 16-lane row (quad_perm xor 1, xor 2, half-row
+// mirror, row mirror), then the four row results combined through readlane.
+constexpr int kDppXor1 = 0xB1;       // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;       // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;
+constexpr int kDppMirror = 0x140;
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+  v += dpp_f<kDppXor1>(v);
+  v += dpp_f<kDppXor2>(v);
+  v += dpp_f<kDppHalfMirror>(v);
+  v += dpp_f<kDppMirror>(v);
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return (r0 + r1) + (r2 + r3);
+}
+
+__device__ __forceinline__ float wave_max_dpp(float v) {
+  v = fmaxf(v, dpp_f<kDppXor1>(v));
+  v = fmaxf(v, dpp_f<kDppXor2>(v));
+  v = fmaxf(v, dpp_f<kDppHalfMirror>(v));
+  v = fmaxf(v, dpp_f<kDppMirror>(v));
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+}
+
+// Order-preserving key of a (value, expert id) pair: larger value first,
+// lower id first among equal values.  The wave maximum of the keys is the
+// arg-max with the lower-id tie-break.
+__device__ __forceinline__ uint64_t topk_key(float v, int id) {
+  uint32_t b = __float_as_uint(v);
+  b = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+  return ((uint64_t)b << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)id);
+}
+__device__ __forceinline__ int topk_key_id(uint64_t k) {
+  return (int)(0xFFFFFFFFu - (uint32_t)(k & 0xFFFFFFFFu));
+}
+
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_max_u64(uint64_t v) {
+  const uint32_t lo = dpp_u<CTRL>((uint32_t)v);
+  const uint32_t hi = dpp_u<CTRL>((uint32_t)(v >> 32));
+  const uint64_t o = ((uint64_t)hi << 32) | lo;
+  return o > v ? o : v;
+}
+
+__device__ __forceinline__ uint64_t wave_max_u64_dpp(uint64_t v) {
+  v = dpp_max_u64<kDppXor1>(v);
+  v = dpp_max_u64<kDppXor2>(v);
+  v = dpp_max_u64<kDppHalfMirror>(v);
+  v = dpp_max_u64<kDppMirror>(v);
+  uint64_t best = 0;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, 16 * r);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), 16 * r);
+    const uint64_t k = ((uint64_t)hi << 32) | lo;
+    best = k > best ? k : best;
+  }
+  return best;
+}
+
+// Top-k of one token's logits by one wave: k rounds of a DPP arg-max over
+// order-preserving (value, lower id first) keys; probabilities from a
+// max-subtracted softmax over all E logits.
+// M = ceil(E / 64) logits per lane (E <= 64 * M).
+template <int M>
+__device__ inline void topk_one_token(const float* zt, int E, int k, int renorm, int32_t* ids_out,
+                                      float* w_out) {
+  const int lane = threadIdx.x & 63;
+  float v[M];
+  bool live[M];
+  float m = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < M; ++i) {
+    const int e = lane + 64 * i;
+    live[i] = e < E;
+    v[i] = live[i] ? zt[e] : -INFINITY;
+    m = fmaxf(m, v[i]);
+  }
+  m = wave_max_dpp(m);
+  float ps = 0.f;
+#pragma unroll
+  for (int i = 0; i < M; ++i)
+    if (live[i]) ps += expf(v[i] - m);
+  const float inv = 1.0f / wave_sum_dpp(ps);
+  float wsum = 0.f, my_w = 0.f;
+  int my_id = 0;
+  for (int j = 0; j < k; ++j) {
+    uint64_t best = 0;
+#pragma unroll
+    for (int i = 0; i < M; ++i) {
+      if (live[i]) {
+        const uint64_t key = topk_key(v[i], lane + 64 * i);
+        best = key > best ? key : best;
+      }
+    }
+    best = wave_max_u64_dpp(best);
+    const int id = topk_key_id(best);
+    float zv = 0.f;
+#pragma unroll
+    for (int i = 0; i < M; ++i)
+      if (lane + 64 * i == id) { live[i] = false; zv = v[i]; }
+    // the winner's logit, from the lane that held it
+    zv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(zv), id & 63));
+    const float p = expf(zv - m) * inv;
+    wsum += p;
+    if (lane == j) { my_w = p; my_id = id; }
+  }
+  if (lane < k) {
+    ids_out[lane] = my_id;
+    w_out[lane] = renorm ? my_w / wsum : my_w;
+  }
+}
+
+}  // namespace moe

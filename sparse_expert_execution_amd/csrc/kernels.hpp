@@ -6,14 +6,19 @@
 
 namespace moe {
 
-struct DecodeLaunch {
+struct FlowLaunch {
   const void* x;
-  const int32_t* ids;
-  const float* w;
+  const void* w_router;   // null: ids / w are inputs
+  int router_f32, renorm;
+  int32_t* ids;
+  float* w;
   const int32_t* slot_of;
   const void* pool;
   const void* shared;
-  float* h;
+  unsigned* hdr;          // 256-byte header (zero before first use)
+  void* plan;             // decode_plan_bytes()
+  float* z;               // [T][E]
+  float* h;               // [T*k + T][I]
   float* y;
   int64_t expert_bytes;
   int64_t off[6];
@@ -44,14 +49,20 @@ struct PrefillLaunch {
   int n_chunks, max_tiles;
 };
 
-// router
-hipError_t launch_route(const void* x, const void* w_router, int router_f32,
-                        int T, int H, int E, int k, int renorm, float* logits,
-                        int32_t* ids, float* w, hipStream_t st);
+// router alone: small T (one wave per expert row, the last workgroup ranks),
+// large T (tiled logits + one wave per token)
+bool route_small_supported(int router_f32, int H);
+hipError_t launch_route_small(const void* x, const void* w_router, int router_f32, int T, int H,
+                              int E, int k, int renorm, float* z, unsigned* ticket, int32_t* ids,
+                              float* w, hipStream_t st);
+hipError_t launch_route_large(const void* x, const void* w_router, int router_f32, int T,
+                              int H, int E, int k, int renorm, float* logits, int32_t* ids,
+                              float* w, hipStream_t st);
 
-// decode
+// decode: router (optional) + experts + combine in one kernel
 bool decode_shape_supported(int wtype, int H, int I);
-hipError_t launch_decode(const DecodeLaunch& d, hipStream_t st);
+size_t decode_plan_bytes();
+hipError_t launch_decode_flow(const FlowLaunch& f, hipStream_t st);
 
 // prefill
 constexpr int kPrefillChunk = 256;   // pairs per sort chunk
@@ -60,8 +71,10 @@ int prefill_max_tiles(int T, int k, int E);
 hipError_t launch_prefill(const PrefillLaunch& p, hipStream_t st);
 
 // formats / merge
-hipError_t launch_quantize_mxfp4(const float* src, int rows, int K, int64_t ld,
+hipError_t launch_quantize_mxfp4(const void* src, int src_bf16, int rows, int K, int64_t ld,
                                  uint8_t* codes, uint8_t* scales, hipStream_t st);
+hipError_t launch_pack_bf16(const void* src, int src_bf16, int rows, int K, uint16_t* dst,
+                            hipStream_t st);
 hipError_t launch_dequant_mxfp4(const uint8_t* codes, const uint8_t* scales,
                                 int64_t n_blocks, float* out, hipStream_t st);
 hipError_t launch_merge(const float* a, const float* b, float* y, size_t n,
@@ -70,9 +83,10 @@ hipError_t launch_mfma_fp4_tile(const uint8_t* a_codes, const uint8_t* a_scales,
                                 const uint8_t* b_codes, const uint8_t* b_scales,
                                 float* out, hipStream_t st);
 
+hipError_t launch_read_probe(const void* src, size_t bytes, int blocks, uint32_t* out,
+                             hipStream_t st);
+
 // cache
-hipError_t launch_slot_updates(int32_t* table, const int32_t* idx,
-                               const int32_t* val, int n, hipStream_t st);
 hipError_t launch_fill_i32(int32_t* dst, int32_t value, int64_t n, hipStream_t st);
 
 }  // namespace moe

@@ -41,8 +41,9 @@ def workspace_bytes(desc, T, mode):
 
 
 def workspace(desc, T, mode, device="cuda"):
+    """Zero-filled workspace (decode workspaces need a zero header once)."""
     n = max(workspace_bytes(desc, T, mode), 256)
-    return torch.empty(n, dtype=torch.uint8, device=device)
+    return torch.zeros(n, dtype=torch.uint8, device=device)
 
 
 def route(desc, x, w_router, ids, w, ws, stream=None):
@@ -55,6 +56,14 @@ def decode(desc, x, ids, w, pool, y, ws, slot_of=None, shared=None, stream=None)
     check(lib().moe_decode(ctypes.byref(desc), _ptr(x), x.shape[0], _ptr(ids), _ptr(w),
                            _ptr(slot_of), _ptr(pool), _ptr(shared), _ptr(y), _ptr(ws),
                            ws.numel(), _stream(stream)), "moe_decode")
+
+
+def route_decode(desc, x, w_router, ids, w, pool, y, ws, slot_of=None, shared=None,
+                 stream=None):
+    check(lib().moe_route_decode(ctypes.byref(desc), _ptr(x), _ptr(w_router), x.shape[0],
+                                 _ptr(ids), _ptr(w), _ptr(slot_of), _ptr(pool), _ptr(shared),
+                                 _ptr(y), _ptr(ws), ws.numel(), _stream(stream)),
+          "moe_route_decode")
 
 
 def prefill(desc, x, ids, w, pool, y, ws, slot_of=None, shared=None, stream=None):
@@ -86,27 +95,26 @@ def mfma_fp4_tile(a_codes, a_scales, b_codes, b_scales, out, stream=None):
           "moe_debug_mfma_fp4_tile")
 
 
+def read_probe(buf, blocks, out, stream=None):
+    check(lib().moe_debug_read_probe(_ptr(buf), buf.numel() * buf.element_size(), blocks,
+                                     _ptr(out), _stream(stream)), "moe_debug_read_probe")
+
+
 def qstar(m, b_pcie, b_host):
     return lib().moe_qstar(m, b_pcie, b_host)
 
 
 def pack_expert(desc, block, gate, up, down, stream=None):
-    """Write one expert into its byte block (a uint8 device tensor view).
-
-    BF16: gate/up/down are BF16 tensors copied into their sections.
-    MXFP4: gate/up/down are float32 tensors quantised by moe_quantize_mxfp4.
-    """
-    off, nbytes = expert_layout(desc)
-    H, I = desc.hidden, desc.inter
-    if desc.wtype == _lib.WTYPE_BF16:
-        for sec, m, n in ((0, gate, I * H), (1, up, I * H), (2, down, H * I)):
-            block[off[sec]:off[sec] + 2 * n].view(torch.bfloat16).copy_(m.reshape(-1))
-    else:
-        for mat, m, rows, K in ((0, gate, I, H), (1, up, I, H), (2, down, H, I)):
-            c = block[off[2 * mat]:off[2 * mat] + rows * K // 2]
-            s = block[off[2 * mat + 1]:off[2 * mat + 1] + rows * K // 32]
-            quantize_mxfp4(m.contiguous(), c, s, stream)
-    return nbytes
+    """Write one expert into its byte block (a uint8 device tensor view) with
+    moe_pack_expert.  gate/up/down: device fp32 or BF16 tensors, row-major."""
+    dt = gate.dtype
+    if dt not in (torch.float32, torch.bfloat16) or up.dtype != dt or down.dtype != dt:
+        raise TypeError("expert matrices must all be float32 or all bfloat16")
+    src = _lib.WTYPE_F32 if dt == torch.float32 else _lib.WTYPE_BF16
+    g, u, d = (m.contiguous() for m in (gate, up, down))
+    check(lib().moe_pack_expert(ctypes.byref(desc), _ptr(g), _ptr(u), _ptr(d), src, _ptr(block),
+                                _stream(stream)), "moe_pack_expert")
+    return expert_layout(desc)[1]
 
 
 class Planner:

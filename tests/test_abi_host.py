@@ -107,9 +107,9 @@ def test_null_and_size_errors_before_any_device_work(L):
 
 def test_workspace_sizes(L):
     d = _desc(hidden=4096, inter=2048, n_experts=256, top_k=6, has_shared=1)
-    assert L.moe_workspace_bytes(ctypes.byref(d), 16, 1) >= (16 * 6 + 16) * 2048 * 4
+    assert L.moe_workspace_bytes(ctypes.byref(d), 16, 1) >= 256 + 16 * 256 * 4
     assert L.moe_workspace_bytes(ctypes.byref(d), 4096, 2) >= 4096 * 7 * 4096 * 4
-    assert L.moe_workspace_bytes(ctypes.byref(d), 4, 0) >= 4 * 256 * 4
+    assert L.moe_workspace_bytes(ctypes.byref(d), 4, 0) >= 256 + 4 * 256 * 4
     assert L.moe_workspace_bytes(ctypes.byref(d), 4, 9) == 0
 
 

@@ -271,6 +271,77 @@ def test_decode_dsv4_full_layer_sampled(ops, T, sample):
     assert olayer.row_rel_error(y[sample], ref) < TOL
 
 
+def _route_decode(ops, L, x, slot_of=None):
+    T, k, H = x.shape[0], L.s["top_k"], L.s["hidden"]
+    ids = torch.full((T, k), -7, dtype=torch.int32, device="cuda")
+    w = torch.full((T, k), float("nan"), dtype=torch.float32, device="cuda")
+    y = torch.full((T, H), float("nan"), dtype=torch.float32, device="cuda")
+    ws = ops.workspace(L.desc, T, 1)
+    ops.route_decode(L.desc, x, L.w_router, ids, w, L.pool, y, ws, slot_of=slot_of,
+                     shared=L.shared)
+    torch.cuda.synchronize()
+    return ids, w, y, ws
+
+
+def _check_ids(L, x, gi, gw, renorm=False):
+    r = olayer.route(bf16_to_f64(x), oracle_router(L.name, L.layer), L.s["top_k"],
+                     renorm=renorm)
+    clear = r["gap"] > GAP
+    assert np.array_equal(gi[clear], r["ids"][clear])
+    assert np.allclose(gw[clear], r["w"][clear], rtol=1e-4, atol=1e-7)
+
+
+@pytest.mark.parametrize("name,T,wtype", [("tiny", 1, "bf16"), ("tiny", 4, "mxfp4"),
+                                          ("qwen_bf16_decode", 1, None),
+                                          ("qwen_bf16_decode", 4, None),
+                                          ("ragged_decode", 3, None),
+                                          ("ragged_decode", 9, None),
+                                          ("glm_cache_decode", 1, None)])
+def test_route_decode(ops, name, T, wtype):
+    """Router + experts + combine in one call (one persistent kernel for T <= 4)."""
+    _say("route_decode", name, T, wtype)
+    L = GpuLayer(name, wtype=wtype)
+    x = L.tokens(T)
+    ids, w, y, ws = _route_decode(ops, L, x)
+    gi, gw = ids.cpu().numpy(), w.cpu().numpy()
+    _check_ids(L, x, gi, gw)
+    ref = _oracle_out(L, x, gi, gw)
+    assert olayer.row_rel_error(y.cpu().numpy(), ref) < TOL
+    # the ticket counter is re-armed
+    assert torch.count_nonzero(ws[:256]).item() == 0
+    # a second call on the same workspace: same routing, same output up to
+    # the order of the fp32 atomic adds
+    ids2, w2, y2, _ = _route_decode(ops, L, x)
+    assert torch.equal(ids, ids2)
+    assert olayer.row_rel_error(y2.cpu().numpy(), y.cpu().numpy().astype(np.float64)) < 1e-5
+
+
+@pytest.mark.parametrize("T,sample", [(1, [0]), (4, [1])])
+def test_route_decode_dsv4_full_sampled(ops, T, sample):
+    _say("route_decode dsv4", T)
+    L = GpuLayer("dsv4_mxfp4_decode", layer=11)
+    x = L.tokens(T)
+    ids, w, y, ws = _route_decode(ops, L, x)
+    gi, gw = ids.cpu().numpy(), w.cpu().numpy()
+    _check_ids(L, x, gi, gw)
+    ref = _oracle_out(L, x, gi, gw, tokens=sample)
+    assert olayer.row_rel_error(y.cpu().numpy()[sample], ref) < TOL
+    assert torch.count_nonzero(ws[:256]).item() == 0
+
+
+def test_route_decode_partial_subset(ops):
+    _say("route_decode partial")
+    L = GpuLayer("ragged_decode")
+    T, E = 4, L.s["n_experts"]
+    x = L.tokens(T, stream=3)
+    resident = np.arange(E) % 4 != 1
+    slot_of = torch.from_numpy(np.where(resident, np.arange(E), -1).astype(np.int32)).cuda()
+    ids, w, y, _ = _route_decode(ops, L, x, slot_of=slot_of)
+    gi, gw = ids.cpu().numpy(), w.cpu().numpy()
+    ref = _oracle_out(L, x, gi, gw, include=resident[gi])
+    assert olayer.row_rel_error(y.cpu().numpy(), ref) < TOL
+
+
 # ---------------------------------------------------------------- prefill
 @pytest.mark.parametrize("name,T", [("tiny", 4), ("tiny", 300), ("ragged_prefill", 1),
                                     ("ragged_prefill", 77), ("ragged_prefill", 700)])
