@@ -11,9 +11,6 @@
 #include "error.hpp"
 #include "kernels.hpp"
 
-// tokens per decode launch (the kernel keeps per-token state in registers)
-#define MOE_DECODE_CHUNK 16
-
 namespace moe {
 
 int hip_status(hipError_t err, const char* what) {
@@ -96,16 +93,15 @@ PrefillWs prefill_ws(const moe_desc* d, int T) {
 }
 
 // route workspace: [0, 256) ticket counter, then router logits z [T][E].
-// decode workspace: [0, 1024) counters, then the plan, z and h [T*k + T][I].
+// decode workspace: [0, 1024) counters, then z [T][E] and h [T*k + T][I].
 // Counters must be zero before the first use; every call leaves them zero.
 struct RouteWs {
-  size_t plan, z, h, total;
+  size_t z, h, total;
 };
 constexpr size_t kDecodeHeader = 1024;
 RouteWs route_ws(const moe_desc* d, int T, bool decode) {
   RouteWs w;
-  w.plan = kDecodeHeader;
-  w.z = decode ? align_up(w.plan + moe::decode_plan_bytes()) : kAlign;
+  w.z = decode ? kDecodeHeader : kAlign;
   w.h = align_up(w.z + (size_t)T * d->n_experts * 4);
   w.total = decode ? align_up(w.h + (size_t)(T * d->top_k + T) * d->inter * 4) : w.h;
   return w;
@@ -204,27 +200,30 @@ static int decode_impl(const moe_desc* desc, const void* x, const void* w_router
   uint8_t* b = static_cast<uint8_t*>(ws);
   size_t off[6], bytes;
   layout(desc, off, &bytes);
-  moe::FlowLaunch f;
+  moe::DecodeLaunch f;
   f.x = x; f.w_router = w_router; f.router_f32 = desc->router_wtype == MOE_WTYPE_F32;
   f.renorm = desc->renorm_topk; f.ids = ids; f.w = w; f.slot_of = slot_of_expert;
   f.pool = slot_pool; f.shared = shared_expert;
   f.hdr = reinterpret_cast<unsigned*>(b);
-  f.plan = b + L.plan;
   f.z = reinterpret_cast<float*>(b + L.z);
   f.h = reinterpret_cast<float*>(b + L.h);
   f.y = y; f.expert_bytes = (int64_t)bytes;
   for (int i = 0; i < 6; ++i) f.off[i] = (int64_t)off[i];
   f.H = desc->hidden; f.I = desc->inter; f.E = desc->n_experts; f.k = desc->top_k;
   f.wtype = desc->wtype;
-  // one launch per group of at most MOE_DECODE_CHUNK tokens, in stream order
+  // launches of at most decode_max_tokens(H) tokens, in stream order, the
+  // batch split evenly over them
   const int H = desc->hidden, k = desc->top_k;
-  for (int t0 = 0; t0 < T; t0 += MOE_DECODE_CHUNK) {
-    f.T = T - t0 < MOE_DECODE_CHUNK ? T - t0 : MOE_DECODE_CHUNK;
+  const int cap = moe::decode_max_tokens(H);
+  const int n_launch = (T + cap - 1) / cap;
+  const int per = (T + n_launch - 1) / n_launch;
+  for (int t0 = 0; t0 < T; t0 += per) {
+    f.T = T - t0 < per ? T - t0 : per;
     f.x = static_cast<const uint16_t*>(x) + (size_t)t0 * H;
     f.ids = ids + (size_t)t0 * k;
     f.w = w + (size_t)t0 * k;
     f.y = y + (size_t)t0 * H;
-    const int st = hip_status(moe::launch_decode_flow(f, as_stream(stream)),
+    const int st = hip_status(moe::launch_decode(f, as_stream(stream)),
                               w_router ? "moe_route_decode" : "moe_decode");
     if (st) return st;
   }

@@ -1,20 +1,24 @@
-// decode.hip - host-side glue of the small-batch decode kernel and of the
-// standalone router (kernels in decode_impl.hpp).
+// decode.hip - host-side glue of the one-kernel decode and of the standalone
+// small-batch router (kernels in decode_impl.hpp).
 #include "decode_impl.hpp"
 
 namespace moe {
-namespace flow {
-hipError_t launch_flow_bf16(FlowArgs& a, hipStream_t st);
-hipError_t launch_flow_mxfp4(FlowArgs& a, hipStream_t st);
-}  // namespace flow
+namespace dec {
+hipError_t launch_bf16(DecArgs& a, hipStream_t st);
+hipError_t launch_mxfp4(DecArgs& a, hipStream_t st);
+}  // namespace dec
 
-using namespace flow;
+using namespace dec;
 
-size_t decode_plan_bytes() { return sizeof(Plan); }
+namespace {
+int elems_per_vector(int wtype) { return wtype == 1 ? 8 : 32; }
+}  // namespace
 
 bool decode_shape_supported(int wtype, int H, int I) {
-  (void)I;
-  return round_lg(H / (wtype == 1 ? 8 : 32)) > 0;
+  const int epv = elems_per_vector(wtype);
+  if (H % epv || I % epv || I > kMaxI) return false;
+  int lr, nv;
+  return lx_cap((H / epv + 63) / 64) > 0 && down_map(I / epv, &lr, &nv);
 }
 
 bool route_small_supported(int router_f32, int H) { return H / (router_f32 ? 4 : 8) <= 64 * 16; }
@@ -30,8 +34,11 @@ hipError_t launch_route_small(const void* x, const void* w_router, int router_f3
   return router_f32 ? launch_route_r<true>(a, st) : launch_route_r<false>(a, st);
 }
 
-hipError_t launch_decode_flow(const FlowLaunch& f, hipStream_t st) {
-  FlowArgs a;
+int decode_max_tokens(int H) { return max_tokens(H); }
+
+hipError_t launch_decode(const DecodeLaunch& f, hipStream_t st) {
+  if (f.T < 1 || f.T > max_tokens(f.H) || f.k > kMaxK || f.E > kMaxE) return hipErrorInvalidValue;
+  DecArgs a;
   a.x = static_cast<const uint16_t*>(f.x);
   a.wr = f.w_router;
   a.router_f32 = f.router_f32;
@@ -41,15 +48,18 @@ hipError_t launch_decode_flow(const FlowLaunch& f, hipStream_t st) {
   a.pool = static_cast<const uint8_t*>(f.pool);
   a.shared = static_cast<const uint8_t*>(f.shared);
   a.hdr = f.hdr;
-  a.plan = static_cast<Plan*>(f.plan);
   a.z = f.z;
   a.h = f.h;
   a.y = f.y;
   a.expert_bytes = f.expert_bytes;
   for (int i = 0; i < 6; ++i) a.off[i] = f.off[i];
   a.T = f.T; a.H = f.H; a.I = f.I; a.E = f.E; a.k = f.k; a.renorm = f.renorm;
-  a.NR = f.w_router ? (f.E + kFW - 1) / kFW : 1;
-  return f.wtype == 1 ? launch_flow_bf16(a, st) : launch_flow_mxfp4(a, st);
+  a.NRW = f.w_router ? (f.E + kW - 1) / kW : 0;
+  const int epv = elems_per_vector(f.wtype);
+  a.lx = (f.H / epv + 63) / 64;
+  if (!down_map(f.I / epv, &a.lr, &a.nv)) return hipErrorInvalidValue;
+  a.G = 0;
+  return f.wtype == 1 ? launch_bf16(a, st) : launch_mxfp4(a, st);
 }
 
 }  // namespace moe

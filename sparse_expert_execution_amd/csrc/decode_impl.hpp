@@ -9,232 +9,599 @@
 // (explainx.ai guide, "Decode: decide whether to move an expert or compute
 // where it lives").
 //
-// Decode is bound by reading the selected experts' weights once from HBM.
-// The kernel's workgroups take one of three roles, by block index:
-//   router   [0, NR)        one wave per router row forms z[t][e]; the last
-//                           router to finish ranks every token (DPP arg-max)
-//                           and publishes the plan: distinct resident
-//                           experts in first-appearance order (then the
-//                           shared expert), each with its (pair, token, gate
-//                           weight) list.  Without a router (ids given) one
-//                           workgroup builds the plan.
-//   gate/up  [NR, +NGU)     one (expert, block of RG rows of I) each: waits
-//                           for the plan, streams its gate and up rows once,
-//                           writes h = silu(g) * u for the expert's tokens
-//   down     [.., +ND)      one block of RD rows of H each: waits for the
-//                           plan, loads its down rows of every selected
-//                           expert into registers while gate/up streams,
-//                           waits for all h, then forms
-//                           y[t][r] = sum_e w[t][e] * (W_down[e][r] . h[t][e])
-//                           in a fixed order and overwrites y (no atomics).
-// Waits are on counters with release/acquire fences and are bounded (an
-// expired wait sets an error word instead of spinning forever).  Every wait
-// is on workgroups with lower block indices, which the dispatcher starts
-// first, so the roles cannot deadlock.
+// Decode is bound by reading the selected experts' weights once from HBM, so
+// the kernel is a persistent grid (every workgroup resident at once) that
+// keeps as many of those reads in flight as it can:
+//   1. router workgroups form z[t][e] = W_r[e] . x[t] (one wave per expert
+//      row) and count themselves done; every workgroup clears its slice of y
+//      and starts on its share of the shared expert's gate/up rows, which
+//      need no routing.
+//   2. every workgroup waits for the router count, ranks the tokens itself
+//      (softmax + DPP arg-max top-k, the same result in every workgroup) and
+//      lists the distinct resident experts in first-appearance order with
+//      their (pair, token, weight) entries.
+//   3. gate/up: the rows of I of all selected experts are split evenly over
+//      the grid; a wave streams one gate row and one up row at a time (two in
+//      flight), dots them with each of the expert's tokens and writes
+//      h = silu(g) * u to the workspace.
+//   4. each workgroup counts itself done with gate/up, issues the loads of
+//      its first down rows and waits for the whole grid (the only grid-wide
+//      wait).
+//   5. down: the rows of H of all selected experts are split evenly over the
+//      grid; each row is dotted with h of each of the expert's tokens and the
+//      gate-weighted result added into y[t][row] with an fp32 atomic.
+// Waits are bounded: an expired wait sets an error word and lets the kernel
+// finish with wrong results instead of hanging.
 #pragma once
 #include "device.hpp"
 #include "kernels.hpp"
 
 namespace moe {
-namespace flow {
+namespace dec {
 
-constexpr int kFT = 256;            // threads per workgroup
-constexpr int kFW = kFT / 64;       // waves per workgroup
+constexpr int kT = 512;             // threads per workgroup (one workgroup per CU)
+constexpr int kW = kT / 64;         // waves per workgroup
 constexpr int kMaxE = 1024;
-constexpr int kMaxPairs = 256;      // T * k per launch
-constexpr int kMaxUnits = kMaxPairs + 1;
 constexpr int kMaxT = 16;           // tokens per launch (larger batches are split)
+constexpr int kMaxK = 8;
+constexpr int kMaxPairs = kMaxT * kMaxK;
+constexpr int kMaxUnits = kMaxPairs + 1;
 constexpr int kMaxEntries = kMaxPairs + kMaxT;
-constexpr int kHStage = 8192;       // floats of h staged in LDS per down pass
-constexpr unsigned kSpinLimit = 1u << 20;
+constexpr int kXStage16 = 7680;     // 16-byte words of staged x (120 KB)
+constexpr int kHStage4 = 1536;      // float4s of staged h (24 KB)
+constexpr int kRankMaxE = 256;      // the rank top-k handles E up to this
+constexpr unsigned kSpinLimit = 1u << 21;
 
-// header words of the workspace: every counter on its own 128-byte line, so
-// polls of one do not queue behind updates of another
-enum {
-  kHRouted = 0, kHPlan = 32, kHGateUp = 64, kHExit = 96, kHError = 128, kHTiming = 160,
-  kHStamps = 192
-};
+// header words of the workspace: every counter on its own 128-byte line
+enum { kHRouted = 0, kHGateUp = 32, kHExit = 64, kHError = 128, kHTiming = 160, kHStamps = 192 };
 
-struct Plan {
-  int n_units;                      // routed + shared
-  int n_routed;
-  int unit_slot[kMaxUnits];         // slot of each routed unit (shared: unused)
-  int unit_start[kMaxUnits + 1];    // entries [start, start_next) per unit
-  int ent_pair[kMaxEntries];        // pair id: t*k + j, or T*k + t for shared
-  int ent_tok[kMaxEntries];
-  float ent_gw[kMaxEntries];
-};
-
-struct FlowArgs {
-  const uint16_t* x;
+struct DecArgs {
+  const uint16_t* x;       // [T][H] bf16
   const void* wr;          // router weights, null when ids/w are given
   int router_f32;
   int32_t* ids;            // [T][k]: out when routing, else in
   float* w;
-  const int32_t* slot_of;
+  const int32_t* slot_of;  // null: expert e sits in slot e
   const uint8_t* pool;
   const uint8_t* shared;
   unsigned* hdr;
-  Plan* plan;
   float* z;                // [T][E]
   float* h;                // [T*k + T][I]
   float* y;                // [T][H]
   int64_t expert_bytes;
   int64_t off[6];
   int T, H, I, E, k, renorm;
-  int NR, NGU, gu_blocks, rg, ND, rd;
+  int G;                   // workgroups in the grid, all resident at once
+  int NRW;                 // router workgroups (0: ids and w are inputs)
+  int lx;                  // 16-byte vectors per lane per gate/up row
+  int lr;                  // lanes per down row (a power of two <= 64)
+  int nv;                  // 16-byte vectors per lane per down row
 };
 
-// phase timing (header word kHTiming non-zero): 100 MHz wall clock at
-// workgroup 0's start (slot 0) and exit (3), the planner's start (1) and
-// publish (2), and the last workgroup's exit (4), as uint64 from word kHStamps
-__device__ __forceinline__ void stamp(const FlowArgs& a, int i, bool any_block = false) {
-  if ((any_block || blockIdx.x == 0) && threadIdx.x == 0 && a.hdr[kHTiming])
-    reinterpret_cast<unsigned long long*>(a.hdr + kHStamps)[i] = wall_clock64();
+// phase timing (header word kHTiming non-zero): 100 MHz wall clock of
+// workgroup 0 at start (0), expert list ready (1), past the grid-wide wait
+// (2), exit (3), router rows done (5), past the router wait (6), gate/up done
+// (7), h staged (11), first down segment done (12), and of the last
+// workgroup's exit (4), as uint64 from kHStamps; the same stamps of the
+// grid's last workgroup 16 slots further
+__device__ __forceinline__ void stamp(bool on, const DecArgs& a, int i) {
+  if (on && threadIdx.x == 0 && (blockIdx.x == 0 || blockIdx.x == gridDim.x - 1))
+    reinterpret_cast<unsigned long long*>(a.hdr + kHStamps)[i + (blockIdx.x ? 16 : 0)] =
+        wall_clock64();
 }
 
-// thread 0 only: wait until *p >= target, then acquire.  Polls back off
-// (64 to 1024 cycles) so that a thousand waiting workgroups do not flood the
-// line the counter sits on.
-__device__ void wait_geq(const FlowArgs& a, unsigned* p, unsigned target) {
+// Data that one workgroup hands to others (z, h, the cleared y) is written
+// with agent-coherent stores and read with agent-coherent loads, so a hand-off
+// needs no cache write-back or invalidation: the writer waits for its stores
+// to complete before it is counted, the reader polls the count before it
+// loads.
+__device__ __forceinline__ void coherent_store(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float coherent_load(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+// 16 bytes at a byte offset of a buffer, agent-coherent (sc1)
+__device__ __forceinline__ float4 coherent_load16(__amdgpu_buffer_rsrc_t r, int byte_off) {
+  const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 16);
+  return make_float4(__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z),
+                     __uint_as_float(v.w));
+}
+
+// thread 0 only: wait until *p >= target.  Polls back off (64 to 512
+// cycles) so that the waiting workgroups do not flood the line the counter
+// sits on.
+__device__ void wait_geq(const DecArgs& a, unsigned* p, unsigned target) {
   unsigned spins = 0;
   int nap = 1;
   while (__hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
     if (nap == 1) __builtin_amdgcn_s_sleep(1);
     else if (nap == 2) __builtin_amdgcn_s_sleep(2);
     else if (nap == 4) __builtin_amdgcn_s_sleep(4);
-    else if (nap == 8) __builtin_amdgcn_s_sleep(8);
-    else __builtin_amdgcn_s_sleep(16);
-    if (nap < 16) nap <<= 1;
+    else __builtin_amdgcn_s_sleep(8);
+    if (nap < 8) nap <<= 1;
     if (++spins > kSpinLimit) {
       __hip_atomic_store(a.hdr + kHError, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       break;
     }
   }
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
 }
 
-// thread 0 only: make this workgroup's writes visible, then count it
-__device__ unsigned signal_add(unsigned* p) {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-  return __hip_atomic_fetch_add(p, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// every wave waits for its coherent stores, then thread 0 counts the
+// workgroup
+__device__ void signal_done(unsigned* p) {
+  wait_stores();
+  __syncthreads();
+  if (threadIdx.x == 0) __hip_atomic_fetch_add(p, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+
+// [lo, hi) of an even split of n items over G parts
+__device__ __forceinline__ void split(int64_t n, int G, int j, int64_t& lo, int64_t& hi) {
+  lo = n * j / G;
+  hi = n * (j + 1) / G;
+}
+
+// Per-wave list of (index, value) results in LDS, written to memory in one
+// burst.  Waits on vector memory count loads and stores together, in issue
+// order, so a store or atomic issued between a load and the use of its data
+// would make that use wait for the store as well; results are therefore
+// collected here and written out when the list fills or the phase ends.
+struct WaveOut {
+  int2* buf;
+  int cap, n;                    // n is the same in every lane
+};
 
 // ---------------------------------------------------------------------------
-// plan: top-k (or the given ids) -> units and their token lists
+// LDS
 // ---------------------------------------------------------------------------
 struct PlanLds {
   int ids[kMaxPairs];
   float w[kMaxPairs];
-  int first[kMaxE];            // lowest pair per expert, then its unit
+  float zsel[kMaxPairs];         // logit of each selected pair
+  float mx[kMaxT], inv[kMaxT];   // softmax max and 1 / sum per token
+  int first[kMaxE];              // lowest pair per expert, then its unit
   int unit_expert[kMaxUnits];
+  int unit_slot[kMaxUnits];      // -1: the shared expert
+  int unit_start[kMaxUnits + 1]; // entries [start, next start) per unit
   int cnt[kMaxUnits];
-  int n_routed;
-  int shared_base;
+  int ent_pair[kMaxEntries];     // t*k + j, or T*k + t for the shared expert
+  int ent_tok[kMaxEntries];
+  float ent_gw[kMaxEntries];
+  int n_routed, n_units;
 };
 
-template <int M>
-__device__ void build_plan(const FlowArgs& a, PlanLds& S, bool route) {
+struct DecLds {
+  PlanLds p;
+  // x of every token: 16-byte word (t * CPV + c) * NV + v holds elements
+  // 8c..8c+7 of weight vector v (CPV = elements per vector / 8, NV vectors
+  // per row), so the lanes of a wave read consecutive words
+  uint4 xs[kXStage16];
+  union {
+    float zs[4 * kHStage4];      // logits of every token, rows padded to float4s
+    // h of the entries of one down pass; an entry's I values as float4s at
+    // (c * V + v) for elements 4c..4c+3 of 16-byte weight vector v (V vectors
+    // per row), so the lanes of a row group read consecutive float4s
+    float4 hs[kHStage4];
+  };
+};
+
+// ---------------------------------------------------------------------------
+// routing: z rows (router workgroups) and the per-workgroup expert list
+// ---------------------------------------------------------------------------
+__device__ void router_rows(const DecArgs& a) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int T = a.T, k = a.k, E = a.E, P = T * k;
-  if (route) {
-    for (int t = wave; t < T; t += kFW)
-      topk_one_token<M>(a.z + (int64_t)t * E, E, k, a.renorm, &S.ids[t * k], &S.w[t * k]);
-    __syncthreads();
-    for (int p = threadIdx.x; p < P; p += kFT) {
-      a.ids[p] = S.ids[p];
-      a.w[p] = S.w[p];
+  const int T = a.T, H = a.H, E = a.E;
+  const int e = blockIdx.x * kW + wave;
+  if (e >= E) return;
+  const int epv = a.router_f32 ? 4 : 8;
+  const int nvr = H / epv;
+  const uint8_t* row = static_cast<const uint8_t*>(a.wr) + (int64_t)e * H * (a.router_f32 ? 4 : 2);
+  for (int t0 = 0; t0 < T; t0 += 4) {
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int i0 = 0; i0 * 64 < nvr; i0 += 4) {
+      uint4 wv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int v = lane + 64 * (i0 + i);
+        wv[i] = v < nvr ? ldg16(row + (int64_t)v * 16) : make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int v = lane + 64 * (i0 + i);
+        if (v >= nvr) continue;
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt) {
+          if (t0 + tt >= T) break;
+          const uint16_t* xt = a.x + (int64_t)(t0 + tt) * H;
+          float s = acc[tt];
+          if (a.router_f32) {
+            const uint2 xx = *reinterpret_cast<const uint2*>(xt + v * 4);
+            s = fmaf(__uint_as_float(wv[i].x), bf16_lo(xx.x), s);
+            s = fmaf(__uint_as_float(wv[i].y), bf16_hi(xx.x), s);
+            s = fmaf(__uint_as_float(wv[i].z), bf16_lo(xx.y), s);
+            s = fmaf(__uint_as_float(wv[i].w), bf16_hi(xx.y), s);
+          } else {
+            const uint4 xx = ldg16(xt + v * 8);
+            s = dot2_bf16(wv[i].x, xx.x, s);
+            s = dot2_bf16(wv[i].y, xx.y, s);
+            s = dot2_bf16(wv[i].z, xx.z, s);
+            s = dot2_bf16(wv[i].w, xx.w, s);
+          }
+          acc[tt] = s;
+        }
+      }
     }
-  } else {
-    for (int p = threadIdx.x; p < P; p += kFT) {
-      S.ids[p] = a.ids[p];
-      S.w[p] = a.w[p];
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+      if (t0 + tt >= T) break;
+      const float s = wave_sum_dpp(acc[tt]);
+      if (lane == 0) coherent_store(a.z + (int64_t)(t0 + tt) * E + e, s);
     }
   }
-  for (int e = threadIdx.x; e < E; e += kFT) S.first[e] = 0x7fffffff;
+}
+
+// sum over aligned groups of lr lanes (a power of two <= 64), result in every
+// lane of the group
+__device__ __forceinline__ float group_sum(float v, int lr) {
+  if (lr == 64) return wave_sum_dpp(v);
+  if (lr >= 2) v += dpp_f<kDppXor1>(v);
+  if (lr >= 4) v += dpp_f<kDppXor2>(v);
+  if (lr >= 8) v += dpp_f<kDppHalfMirror>(v);
+  if (lr >= 16) v += dpp_f<kDppMirror>(v);
+  if (lr == 32) {
+    const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+    const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+    const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+    const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+    v = (threadIdx.x & 32) ? r2 + r3 : r0 + r1;
+  }
+  return v;
+}
+
+// Top-k of every token for E <= kRankMaxE: the logits go to LDS; an expert's
+// rank is the number of experts ahead of it (larger logit, or equal logit and
+// lower id), so the k experts of rank < k land directly in descending order.
+// Weights are the softmax probabilities max-subtracted in fp32 (renormalised
+// over the k when asked).
+__device__ void rank_topk(const DecArgs& a, DecLds& S) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int T = a.T, E = a.E, k = a.k, n = T * E;
+  const int E4 = (E + 3) & ~3;             // rows padded to whole float4s with -inf
+  for (int i = threadIdx.x; i < T * E4; i += kT) {
+    const int t = i / E4, e = i - t * E4;
+    S.zs[i] = e < E ? coherent_load(a.z + (int64_t)t * E + e) : -INFINITY;
+  }
   __syncthreads();
-  for (int p = threadIdx.x; p < P; p += kFT) {
-    const int e = S.ids[p];
+  for (int t = wave; t < T; t += kW) {
+    const float* zt = S.zs + t * E4;
+    float m = -INFINITY;
+    for (int e = lane; e < E; e += 64) m = fmaxf(m, zt[e]);
+    m = wave_max_dpp(m);
+    float ps = 0.f;
+    for (int e = lane; e < E; e += 64) ps += expf(zt[e] - m);
+    ps = wave_sum_dpp(ps);
+    if (lane == 0) {
+      S.p.mx[t] = m;
+      S.p.inv[t] = 1.0f / ps;
+    }
+  }
+  // sp threads per expert, each counting over every sp-th float4 of the row
+  int sp = 1;
+  while (sp < 8 && n * sp * 2 <= kT) sp <<= 1;
+  for (int i = threadIdx.x; i < n * sp; i += kT) {
+    const int item = i / sp, part = i - item * sp;
+    const int t = item / E, e = item - t * E;
+    const float4* zt4 = reinterpret_cast<const float4*>(S.zs + t * E4);
+    const float my = S.zs[t * E4 + e];
+    int rank = 0;
+#pragma unroll 4
+    for (int c = part; c < E4 / 4; c += sp) {
+      const float4 z4 = zt4[c];
+      const int e2 = 4 * c;
+      rank += (z4.x > my) | ((z4.x == my) & (e2 < e));
+      rank += (z4.y > my) | ((z4.y == my) & (e2 + 1 < e));
+      rank += (z4.z > my) | ((z4.z == my) & (e2 + 2 < e));
+      rank += (z4.w > my) | ((z4.w == my) & (e2 + 3 < e));
+    }
+    rank = (int)group_sum((float)rank, sp);
+    if (part == 0 && rank < k) {
+      S.p.ids[t * k + rank] = e;
+      S.p.zsel[t * k + rank] = my;
+    }
+  }
+  __syncthreads();
+  for (int p = threadIdx.x; p < T * k; p += kT) {
+    const int t = p / k;
+    S.p.w[p] = expf(S.p.zsel[p] - S.p.mx[t]) * S.p.inv[t];
+  }
+  __syncthreads();
+  if (a.renorm) {
+    for (int t = threadIdx.x; t < T; t += kT) {
+      float s = 0.f;
+      for (int j = 0; j < k; ++j) s += S.p.w[t * k + j];
+      for (int j = 0; j < k; ++j) S.p.w[t * k + j] /= s;
+    }
+    __syncthreads();
+  }
+}
+
+// Expert list of this launch, built the same way in every workgroup: the
+// distinct resident experts in order of first appearance over the (token,
+// rank) pairs, each with its pairs in order, then the shared expert.
+template <int M>
+__device__ void build_units(const DecArgs& a, DecLds& S, bool route) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int T = a.T, k = a.k, E = a.E, P = T * k;
+  PlanLds& L = S.p;
+  if (route) {
+    if (E <= kRankMaxE) {
+      rank_topk(a, S);
+    } else {
+      for (int t = wave; t < T; t += kW)
+        topk_one_token<M, true>(a.z + (int64_t)t * E, E, k, a.renorm, &L.ids[t * k], &L.w[t * k]);
+    }
+  } else {
+    for (int p = threadIdx.x; p < P; p += kT) {
+      L.ids[p] = a.ids[p];
+      L.w[p] = a.w[p];
+    }
+  }
+  for (int e = threadIdx.x; e < E; e += kT) L.first[e] = 0x7fffffff;
+  __syncthreads();
+  if (route && blockIdx.x == 0) {
+    for (int p = threadIdx.x; p < P; p += kT) {
+      a.ids[p] = L.ids[p];
+      a.w[p] = L.w[p];
+    }
+  }
+  for (int p = threadIdx.x; p < P; p += kT) {
+    const int e = L.ids[p];
     bool ok = e >= 0 && e < E;
     if (ok && a.slot_of) ok = a.slot_of[e] >= 0;
-    S.ids[p] = ok ? e : -1;
-    if (ok) atomicMin(&S.first[e], p);
+    if (ok) atomicMin(&L.first[e], p);
   }
   __syncthreads();
   if (wave == 0) {
     int base = 0;
     for (int c = 0; c < P; c += 64) {
       const int p = c + lane;
-      const int e = p < P ? S.ids[p] : -1;
-      const bool isfirst = e >= 0 && S.first[e] == p;
+      const int e = p < P ? L.ids[p] : -1;
+      const bool isfirst = e >= 0 && e < E && L.first[e] == p;
       const uint64_t mask = __ballot(isfirst);
       const int rank = base + __popcll(mask & ((1ull << lane) - 1ull));
       if (isfirst) {
-        S.unit_expert[rank] = e;
-        a.plan->unit_slot[rank] = a.slot_of ? a.slot_of[e] : e;
-        S.first[e] = rank;
+        L.unit_expert[rank] = e;
+        L.unit_slot[rank] = a.slot_of ? a.slot_of[e] : e;
       }
       base += __popcll(mask);
     }
-    if (lane == 0) S.n_routed = base;
+    if (lane == 0) L.n_routed = base;
   }
   __syncthreads();
-  const int n_routed = S.n_routed;
-  // entries per routed unit, in pair order (one thread per unit)
-  for (int u = threadIdx.x; u < n_routed; u += kFT) {
-    const int e = S.unit_expert[u];
+  const int n_routed = L.n_routed;
+  for (int u = threadIdx.x; u < n_routed; u += kT) {
+    const int e = L.unit_expert[u];
     int c = 0;
-    for (int p = 0; p < P; ++p) c += S.ids[p] == e;
-    S.cnt[u] = c;
+    for (int p = 0; p < P; ++p) c += L.ids[p] == e;
+    L.cnt[u] = c;
   }
   __syncthreads();
   if (threadIdx.x == 0) {
     int pos = 0;
     for (int u = 0; u < n_routed; ++u) {
-      a.plan->unit_start[u] = pos;
-      const int c = S.cnt[u];
-      S.cnt[u] = pos;
-      pos += c;
+      L.unit_start[u] = pos;
+      pos += L.cnt[u];
     }
-    const int n_units = n_routed + (a.shared ? 1 : 0);
-    S.shared_base = pos;
+    int n_units = n_routed;
     if (a.shared) {
-      a.plan->unit_start[n_routed] = pos;
+      L.unit_start[n_routed] = pos;
+      L.unit_slot[n_routed] = -1;
       pos += T;
+      ++n_units;
     }
-    a.plan->unit_start[n_units] = pos;
-    a.plan->n_units = n_units;
-    a.plan->n_routed = n_routed;
+    L.unit_start[n_units] = pos;
+    L.n_units = n_units;
   }
   __syncthreads();
-  for (int u = threadIdx.x; u < n_routed; u += kFT) {
-    const int e = S.unit_expert[u];
-    int pos = S.cnt[u];
+  for (int u = threadIdx.x; u < n_routed; u += kT) {
+    const int e = L.unit_expert[u];
+    int pos = L.unit_start[u];
     for (int p = 0; p < P; ++p) {
-      if (S.ids[p] == e) {
-        a.plan->ent_pair[pos] = p;
-        a.plan->ent_tok[pos] = p / k;
-        a.plan->ent_gw[pos] = S.w[p];
+      if (L.ids[p] == e) {
+        L.ent_pair[pos] = p;
+        L.ent_tok[pos] = p / k;
+        L.ent_gw[pos] = L.w[p];
         ++pos;
       }
     }
   }
   if (a.shared) {
-    const int base = S.shared_base;
-    for (int t = threadIdx.x; t < T; t += kFT) {
-      a.plan->ent_pair[base + t] = P + t;
-      a.plan->ent_tok[base + t] = t;
-      a.plan->ent_gw[base + t] = 1.f;
+    const int base = L.unit_start[n_routed];
+    for (int t = threadIdx.x; t < T; t += kT) {
+      L.ent_pair[base + t] = P + t;
+      L.ent_tok[base + t] = t;
+      L.ent_gw[base + t] = 1.f;
+    }
+  }
+  __syncthreads();
+}
+
+__device__ __forceinline__ const uint8_t* unit_base(const DecArgs& a, int slot) {
+  return slot < 0 ? a.shared : a.pool + (int64_t)slot * a.expert_bytes;
+}
+
+// ---------------------------------------------------------------------------
+// gate/up rows
+// ---------------------------------------------------------------------------
+// x of every token into LDS in the layout DecLds::xs describes
+template <int WT>
+__device__ void stage_x(const DecArgs& a, DecLds& S) {
+  constexpr int CPV = WT == 1 ? 1 : 4;
+  const int NV = a.H / (8 * CPV);
+  const int n = a.T * a.H / 8;
+  for (int q = threadIdx.x; q < n; q += kT) {
+    const int t = q / (a.H / 8), w8 = q - t * (a.H / 8);
+    const int v = w8 / CPV, c = w8 - v * CPV;
+    S.xs[(t * CPV + c) * NV + v] = ldg16(a.x + (int64_t)t * a.H + w8 * 8);
+  }
+}
+
+template <int LXC>
+struct GuBuf {
+  uint4 g[LXC], u[LXC];
+  uint32_t gs[LXC], us[LXC];
+};
+
+// row i of the gate and up matrices of the expert at base, this lane's vectors
+template <int WT, int LXC>
+__device__ __forceinline__ void gu_load(const DecArgs& a, const uint8_t* base, int i, int lane,
+                                        GuBuf<LXC>& b) {
+  constexpr int EPV = WT == 1 ? 8 : 32;
+  const int nvh = a.H / EPV;
+#pragma unroll
+  for (int l = 0; l < LXC; ++l) {
+    const int v = lane + 64 * l;
+    b.g[l] = b.u[l] = make_uint4(0, 0, 0, 0);
+    b.gs[l] = b.us[l] = 0;
+    if (l < a.lx && v < nvh) {
+      if (WT == 1) {
+        b.g[l] = ldg16(base + a.off[0] + ((int64_t)i * a.H + (int64_t)v * 8) * 2);
+        b.u[l] = ldg16(base + a.off[1] + ((int64_t)i * a.H + (int64_t)v * 8) * 2);
+      } else {
+        b.g[l] = ldg16(base + a.off[0] + (int64_t)i * (a.H / 2) + (int64_t)v * 16);
+        b.u[l] = ldg16(base + a.off[2] + (int64_t)i * (a.H / 2) + (int64_t)v * 16);
+        b.gs[l] = (base + a.off[1])[(int64_t)i * (a.H / 32) + v];
+        b.us[l] = (base + a.off[3])[(int64_t)i * (a.H / 32) + v];
+      }
     }
   }
 }
 
-// dot of one 16-byte weight vector with the matching h (fp32) elements
+// h = silu(g . x_t) * (u . x_t) for entry q of the row's expert (token t);
+// the result is the same in every lane
+template <int WT, int LXC>
+__device__ __forceinline__ float gu_dot(const DecArgs& a, const DecLds& S, const GuBuf<LXC>& b,
+                                        int t, int lane) {
+  constexpr int EPV = WT == 1 ? 8 : 32;
+  constexpr int CPV = EPV / 8;
+  const int nvh = a.H / EPV;
+  float gp = 0.f, up = 0.f;
+#pragma unroll
+  for (int l = 0; l < LXC; ++l) {
+    const int v = lane + 64 * l;
+    if (l >= a.lx || v >= nvh) continue;
+    if (WT == 1) {
+      const uint4 xx = S.xs[t * nvh + v];
+      gp = dot2_bf16(b.g[l].x, xx.x, gp);
+      gp = dot2_bf16(b.g[l].y, xx.y, gp);
+      gp = dot2_bf16(b.g[l].z, xx.z, gp);
+      gp = dot2_bf16(b.g[l].w, xx.w, gp);
+      up = dot2_bf16(b.u[l].x, xx.x, up);
+      up = dot2_bf16(b.u[l].y, xx.y, up);
+      up = dot2_bf16(b.u[l].z, xx.z, up);
+      up = dot2_bf16(b.u[l].w, xx.w, up);
+    } else {
+      uint32_t xp[16];
+#pragma unroll
+      for (int c = 0; c < CPV; ++c) {
+        const uint4 t4 = S.xs[(t * CPV + c) * nvh + v];
+        xp[4 * c] = t4.x; xp[4 * c + 1] = t4.y; xp[4 * c + 2] = t4.z; xp[4 * c + 3] = t4.w;
+      }
+      gp = fmaf(dot_fp4_bf16_block(b.g[l], xp), e8m0_to_f32(b.gs[l]), gp);
+      up = fmaf(dot_fp4_bf16_block(b.u[l], xp), e8m0_to_f32(b.us[l]), up);
+    }
+  }
+  const float gsum = wave_sum_dpp(gp);
+  const float usum = wave_sum_dpp(up);
+  return gsum / (1.0f + expf(-gsum)) * usum;
+}
+
+// h results of a wave to memory (coherent stores)
+__device__ __forceinline__ void flush_h(const DecArgs& a, WaveOut& o) {
+  const int lane = threadIdx.x & 63;
+  for (int q = lane; q < o.n; q += 64) {
+    const int2 p = o.buf[q];
+    coherent_store(a.h + p.x, __int_as_float(p.y));
+  }
+  o.n = 0;
+}
+
+// Rows [q0, q1) of a flattened (unit, row of I) list; wave w takes rows
+// q0 + w, q0 + w + kW, ... with RG rows of loads in flight; after() runs once
+// the first rows' loads are issued (every wave calls it).  h results gather in
+// a per-wave list in the h stage of LDS.  SHARED: the list is the shared
+// expert's I rows and its entries are all T tokens (known before routing).
+template <int WT, int LXC, int RG, bool SHARED, class After>
+__device__ void gateup_range(const DecArgs& a, DecLds& S, int64_t q0, int64_t q1,
+                             After&& after) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int I = a.I;
+  const int64_t first = q0 + wave;
+  const int nq = first < q1 ? (int)((q1 - first + kW - 1) / kW) : 0;
+  auto row_of = [&](int m, int& u, int& i) {
+    const int64_t q = first + (int64_t)m * kW;
+    if (SHARED) { u = -1; i = (int)q; }
+    else { u = (int)(q / I); i = (int)(q - (int64_t)u * I); }
+  };
+  auto load = [&](int m, GuBuf<LXC>& b) {
+    int u, i;
+    row_of(m, u, i);
+    gu_load<WT, LXC>(a, SHARED ? a.shared : unit_base(a, S.p.unit_slot[u]), i, lane, b);
+  };
+  WaveOut out;
+  out.cap = kHStage4 / kW * 2;
+  out.buf = reinterpret_cast<int2*>(S.hs) + wave * out.cap;
+  out.n = 0;
+  GuBuf<LXC> buf[RG];
+#pragma unroll
+  for (int r = 0; r < RG; ++r)
+    if (r < nq) load(r, buf[r]);
+  after();                                 // more loads, behind the first rows
+  for (int m0 = 0; m0 < nq; m0 += RG) {
+#pragma unroll
+    for (int r = 0; r < RG; ++r) {
+      const int m = m0 + r;
+      if (m < nq) {
+        int u, i;
+        row_of(m, u, i);
+        const int e0 = SHARED ? 0 : S.p.unit_start[u];
+        const int ne = SHARED ? a.T : S.p.unit_start[u + 1] - e0;
+        float mine = 0.f;        // lane q keeps entry q's h
+        for (int q = 0; q < ne; ++q) {
+          const int t = SHARED ? q : S.p.ent_tok[e0 + q];
+          const float hv = gu_dot<WT, LXC>(a, S, buf[r], t, lane);
+          if (lane == q) mine = hv;
+        }
+        if (m + RG < nq) load(m + RG, buf[r]);
+        if (out.n + ne > out.cap) flush_h(a, out);
+        if (lane < ne) {
+          const int pair = SHARED ? a.T * a.k + lane : S.p.ent_pair[e0 + lane];
+          out.buf[out.n + lane] = make_int2(pair * I + i, __float_as_int(mine));
+        }
+        out.n += ne;
+      }
+    }
+  }
+  flush_h(a, out);
+}
+
+// ---------------------------------------------------------------------------
+// down rows
+// ---------------------------------------------------------------------------
+template <int NVC>
+struct DnBuf {
+  uint4 q[NVC];
+  uint32_t s[NVC];
+};
+
+// dot of one 16-byte weight vector with its EPV h values (EPV / 4 float4s)
 template <int WT>
-__device__ __forceinline__ float wdot_h(const uint4 q, uint32_t sc, const float* hv) {
+__device__ __forceinline__ float wdot_h(const uint4 q, uint32_t sc, const float4* h4) {
   if (WT == 1) {
-    const float4 h0 = *reinterpret_cast<const float4*>(hv);
-    const float4 h1 = *reinterpret_cast<const float4*>(hv + 4);
+    const float4 h0 = h4[0], h1 = h4[1];
     float s = bf16_lo(q.x) * h0.x;
     s = fmaf(bf16_hi(q.x), h0.y, s);
     s = fmaf(bf16_lo(q.y), h0.z, s);
@@ -244,13 +611,11 @@ __device__ __forceinline__ float wdot_h(const uint4 q, uint32_t sc, const float*
     s = fmaf(bf16_lo(q.w), h1.z, s);
     return fmaf(bf16_hi(q.w), h1.w, s);
   } else {
-    // one 32-bit word (8 codes) at a time keeps few h values live
-    const float4* h4 = reinterpret_cast<const float4*>(hv);
     const uint32_t w[4] = {q.x, q.y, q.z, q.w};
     float acc = 0.f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float4 ha = h4[2 * i], hb = h4[2 * i + 1];
+      const float4 ha = h4[2 * i], hc = h4[2 * i + 1];
       const v2f c0 = fp4x2_to_f32x2<0>(w[i]);
       const v2f c1 = fp4x2_to_f32x2<1>(w[i]);
       const v2f c2 = fp4x2_to_f32x2<2>(w[i]);
@@ -259,372 +624,271 @@ __device__ __forceinline__ float wdot_h(const uint4 q, uint32_t sc, const float*
       acc = fmaf(c0.y, ha.y, acc);
       acc = fmaf(c1.x, ha.z, acc);
       acc = fmaf(c1.y, ha.w, acc);
-      acc = fmaf(c2.x, hb.x, acc);
-      acc = fmaf(c2.y, hb.y, acc);
-      acc = fmaf(c3.x, hb.z, acc);
-      acc = fmaf(c3.y, hb.w, acc);
+      acc = fmaf(c2.x, hc.x, acc);
+      acc = fmaf(c2.y, hc.y, acc);
+      acc = fmaf(c3.x, hc.z, acc);
+      acc = fmaf(c3.y, hc.w, acc);
     }
     return acc * e8m0_to_f32(sc);
   }
 }
 
-union FlowLds {
-  PlanLds plan;
-  struct {
-    int n_units;
-    int slot;
-    int start, end;
-    int pair[kMaxT];
-    int tok[kMaxT];
-  } gu;
-  struct {
-    int n_units;
-    int slot[kMaxUnits];
-    int start[kMaxUnits + 1];
-    int pair[kMaxEntries];
-    int tok[kMaxEntries];
-    float gw[kMaxEntries];
-    float h[kHStage];          // h of the entries of one pass
-  } dn;
+// h values kept in registers per lane for single-entry passes: EPV floats per
+// down vector, as long as that stays within 32 floats
+template <int WT, int NVC>
+struct HRegs {
+  static constexpr int EPV = WT == 1 ? 8 : 32;
+  static constexpr bool kOn = NVC * EPV <= 32;
+  float4 v[kOn ? NVC : 1][EPV / 4];
 };
 
-// WT: 1 BF16, 2 MXFP4.  LG: 16-byte vectors per lane per gate/up row.  RGW:
-// gate/up rows per wave.  RDW: down rows per wave.  PF: down vectors per lane
-// kept in registers across the wait.  TC: tokens per down pass.  M: logits
-// per lane in top-k.
-template <int WT, int LG, int RGW, int RDW, int PF, int TC, int M>
-__global__ __launch_bounds__(kFT, 4) void flow_kernel(FlowArgs a) {
-  __shared__ FlowLds S;
-  __shared__ int s_flag;
+// this lane's h values of one staged entry (hs: the entry's float4s)
+template <int WT, int NVC>
+__device__ __forceinline__ void h_regs(const DecArgs& a, const float4* hs, int j,
+                                       HRegs<WT, NVC>& hv) {
   constexpr int EPV = WT == 1 ? 8 : 32;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int bid = blockIdx.x;
-  const int T = a.T, H = a.H, I = a.I, E = a.E;
-  const bool route = a.wr != nullptr;
-  stamp(a, 0);
-
-  if (bid < a.NR) {
-    // ------------------------------ router ------------------------------
-    if (route) {
-      const int epv_r = a.router_f32 ? 4 : 8;
-      const int nvr = H / epv_r;
-      const int row_bytes = H * (a.router_f32 ? 4 : 2);
-      const int e = bid * kFW + wave;
-      if (e < E) {
-        const uint8_t* row = static_cast<const uint8_t*>(a.wr) + (int64_t)e * row_bytes;
-        float acc[4] = {0.f, 0.f, 0.f, 0.f};
-        for (int t0 = 0; t0 < T; t0 += 4) {
-          for (int i0 = 0; i0 * 64 < nvr; i0 += 4) {
-            uint4 wv[4];
+  if constexpr (HRegs<WT, NVC>::kOn) {
+    const int V = a.I / EPV;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int v = lane + 64 * (i0 + i);
-              wv[i] = v < nvr ? ldg16(row + (int64_t)v * 16) : make_uint4(0, 0, 0, 0);
-            }
+    for (int n = 0; n < NVC; ++n) {
+      if (n >= a.nv) break;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int v = lane + 64 * (i0 + i);
-              if (v >= nvr) continue;
-#pragma unroll
-              for (int tt = 0; tt < 4; ++tt) {
-                if (t0 + tt >= T) break;
-                const uint16_t* xt = a.x + (int64_t)(t0 + tt) * H;
-                float s = acc[tt];
-                if (a.router_f32) {
-                  const uint2 xx = *reinterpret_cast<const uint2*>(xt + v * 4);
-                  s = fmaf(__uint_as_float(wv[i].x), bf16_lo(xx.x), s);
-                  s = fmaf(__uint_as_float(wv[i].y), bf16_hi(xx.x), s);
-                  s = fmaf(__uint_as_float(wv[i].z), bf16_lo(xx.y), s);
-                  s = fmaf(__uint_as_float(wv[i].w), bf16_hi(xx.y), s);
-                } else {
-                  const uint4 xx = ldg16(xt + v * 8);
-                  s = dot2_bf16(wv[i].x, xx.x, s);
-                  s = dot2_bf16(wv[i].y, xx.y, s);
-                  s = dot2_bf16(wv[i].z, xx.z, s);
-                  s = dot2_bf16(wv[i].w, xx.w, s);
-                }
-                acc[tt] = s;
-              }
-            }
-          }
-#pragma unroll
-          for (int tt = 0; tt < 4; ++tt) {
-            if (t0 + tt >= T) break;
-            const float s = wave_sum_dpp(acc[tt]);
-            if (lane == 0) a.z[(int64_t)(t0 + tt) * E + e] = s;
-            acc[tt] = 0.f;
-          }
-        }
-      }
-      __syncthreads();
-      if (threadIdx.x == 0) s_flag = signal_add(a.hdr + kHRouted) == (unsigned)(a.NR - 1);
-      __syncthreads();
-      if (s_flag) {
-        if (threadIdx.x == 0) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-        __syncthreads();
-        stamp(a, 1, true);
-        build_plan<M>(a, S.plan, true);
-        __syncthreads();
-        if (threadIdx.x == 0) {
-          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-          __hip_atomic_store(a.hdr + kHPlan, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-        stamp(a, 2, true);
-      }
-    } else {
-      build_plan<M>(a, S.plan, false);
-      __syncthreads();
-      if (threadIdx.x == 0) {
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-        __hip_atomic_store(a.hdr + kHPlan, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-    }
-  } else if (bid < a.NR + a.NGU) {
-    // ------------------------------ gate / up ----------------------------
-    const int g = bid - a.NR;
-    if (threadIdx.x == 0) {
-      wait_geq(a, a.hdr + kHPlan, 1u);
-      S.gu.n_units = __hip_atomic_load(&a.plan->n_units, __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_AGENT);
-    }
-    __syncthreads();
-    const int n_items = S.gu.n_units * a.gu_blocks;
-    if (g < n_items) {
-      const int u = g / a.gu_blocks;
-      const int i0 = (g - u * a.gu_blocks) * a.rg;
-      if (threadIdx.x == 0) {
-        S.gu.slot = u < a.plan->n_routed ? a.plan->unit_slot[u] : -1;
-        S.gu.start = a.plan->unit_start[u];
-        S.gu.end = a.plan->unit_start[u + 1];
-      }
-      __syncthreads();
-      const int ntok = min(S.gu.end - S.gu.start, kMaxT);
-      for (int q = threadIdx.x; q < ntok; q += kFT) {
-        S.gu.pair[q] = a.plan->ent_pair[S.gu.start + q];
-        S.gu.tok[q] = a.plan->ent_tok[S.gu.start + q];
-      }
-      const uint8_t* base =
-          S.gu.slot < 0 ? a.shared : a.pool + (int64_t)S.gu.slot * a.expert_bytes;
-      const int nvh = H / EPV;
-      uint4 gq[RGW][LG], uq[RGW][LG];
-      uint32_t gs[RGW][LG], us[RGW][LG];
-#pragma unroll
-      for (int rr = 0; rr < RGW; ++rr) {
-        const int i = i0 + wave * RGW + rr;
-#pragma unroll
-        for (int l = 0; l < LG; ++l) {
-          const int v = lane + 64 * l;
-          gq[rr][l] = uq[rr][l] = make_uint4(0, 0, 0, 0);
-          gs[rr][l] = us[rr][l] = 0;
-          if (i < I && v < nvh) {
-            if (WT == 1) {
-              gq[rr][l] = ldg16(base + a.off[0] + ((int64_t)i * H + (int64_t)v * 8) * 2);
-              uq[rr][l] = ldg16(base + a.off[1] + ((int64_t)i * H + (int64_t)v * 8) * 2);
-            } else {
-              gq[rr][l] = ldg16(base + a.off[0] + (int64_t)i * (H / 2) + (int64_t)v * 16);
-              uq[rr][l] = ldg16(base + a.off[2] + (int64_t)i * (H / 2) + (int64_t)v * 16);
-              gs[rr][l] = (base + a.off[1])[(int64_t)i * (H / 32) + v];
-              us[rr][l] = (base + a.off[3])[(int64_t)i * (H / 32) + v];
-            }
-          }
-        }
-      }
-      __syncthreads();
-      for (int q = 0; q < ntok; ++q) {
-        const uint16_t* xt = a.x + (int64_t)S.gu.tok[q] * H;
-        float gp[RGW], up[RGW];
-#pragma unroll
-        for (int rr = 0; rr < RGW; ++rr) gp[rr] = up[rr] = 0.f;
-#pragma unroll
-        for (int l = 0; l < LG; ++l) {
-          const int v = lane + 64 * l;
-          if (v >= nvh) continue;
-          if (WT == 1) {
-            const uint4 xx = ldg16(xt + (int64_t)v * 8);
-#pragma unroll
-            for (int rr = 0; rr < RGW; ++rr) {
-              float g2 = gp[rr], u2 = up[rr];
-              g2 = dot2_bf16(gq[rr][l].x, xx.x, g2);
-              g2 = dot2_bf16(gq[rr][l].y, xx.y, g2);
-              g2 = dot2_bf16(gq[rr][l].z, xx.z, g2);
-              gp[rr] = dot2_bf16(gq[rr][l].w, xx.w, g2);
-              u2 = dot2_bf16(uq[rr][l].x, xx.x, u2);
-              u2 = dot2_bf16(uq[rr][l].y, xx.y, u2);
-              u2 = dot2_bf16(uq[rr][l].z, xx.z, u2);
-              up[rr] = dot2_bf16(uq[rr][l].w, xx.w, u2);
-            }
-          } else {
-            uint32_t xp[16];
-            const uint4* xs = reinterpret_cast<const uint4*>(xt + (int64_t)v * 32);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              const uint4 t4 = xs[j];
-              xp[4 * j] = t4.x; xp[4 * j + 1] = t4.y; xp[4 * j + 2] = t4.z; xp[4 * j + 3] = t4.w;
-            }
-#pragma unroll
-            for (int rr = 0; rr < RGW; ++rr) {
-              gp[rr] = fmaf(dot_fp4_bf16_block(gq[rr][l], xp), e8m0_to_f32(gs[rr][l]), gp[rr]);
-              up[rr] = fmaf(dot_fp4_bf16_block(uq[rr][l], xp), e8m0_to_f32(us[rr][l]), up[rr]);
-            }
-          }
-        }
-#pragma unroll
-        for (int rr = 0; rr < RGW; ++rr) {
-          const float gsum = wave_sum_dpp(gp[rr]);
-          const float usum = wave_sum_dpp(up[rr]);
-          const int i = i0 + wave * RGW + rr;
-          if (lane == 0 && i < I)
-            a.h[(int64_t)S.gu.pair[q] * I + i] = gsum / (1.0f + expf(-gsum)) * usum;
-        }
-      }
-      __syncthreads();
-      if (threadIdx.x == 0) signal_add(a.hdr + kHGateUp);
-    }
-  } else {
-    // ------------------------------ down ---------------------------------
-    const int d = bid - a.NR - a.NGU;
-    if (threadIdx.x == 0) {
-      wait_geq(a, a.hdr + kHPlan, 1u);
-      S.dn.n_units = __hip_atomic_load(&a.plan->n_units, __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_AGENT);
-    }
-    __syncthreads();
-    const int n_units = S.dn.n_units;
-    const int n_routed = a.plan->n_routed;
-    for (int u = threadIdx.x; u <= n_units; u += kFT) {
-      S.dn.start[u] = a.plan->unit_start[u];
-      if (u < n_units) S.dn.slot[u] = u < n_routed ? a.plan->unit_slot[u] : -1;
-    }
-    __syncthreads();
-    const int n_ent = min(S.dn.start[n_units], kMaxEntries);
-    for (int q = threadIdx.x; q < n_ent; q += kFT) {
-      S.dn.pair[q] = a.plan->ent_pair[q];
-      S.dn.tok[q] = a.plan->ent_tok[q];
-      S.dn.gw[q] = a.plan->ent_gw[q];
-    }
-    const int r0 = d * a.rd + wave * RDW;
-    const int nvi = I / EPV;
-    const int per_unit = RDW * nvi;
-    const int n_slots = n_units * per_unit;
-    __syncthreads();
-    auto slot_load = [&](int s, uint4& q, uint32_t& sc) {
-      const int u = s / per_unit;
-      const int rem = s - u * per_unit;
-      const int rr = rem / nvi, v = rem - rr * nvi;
-      const int row = r0 + rr;
-      q = make_uint4(0, 0, 0, 0);
-      sc = 0;
-      if (row < H) {
-        const int slot = S.dn.slot[u];
-        const uint8_t* b = slot < 0 ? a.shared : a.pool + (int64_t)slot * a.expert_bytes;
-        if (WT == 1) {
-          q = ldg16(b + a.off[2] + ((int64_t)row * I + (int64_t)v * 8) * 2);
-        } else {
-          q = ldg16(b + a.off[4] + (int64_t)row * (I / 2) + (int64_t)v * 16);
-          sc = (b + a.off[5])[(int64_t)row * (I / 32) + v];
-        }
-      }
-    };
-    uint4 pre[PF];
-    uint32_t psc[PF];
-#pragma unroll
-    for (int j = 0; j < PF; ++j) {
-      const int s = lane + 64 * j;
-      if (s < n_slots) slot_load(s, pre[j], psc[j]);
-      else { pre[j] = make_uint4(0, 0, 0, 0); psc[j] = 0; }
-    }
-    if (threadIdx.x == 0) wait_geq(a, a.hdr + kHGateUp, (unsigned)(n_units * a.gu_blocks));
-    __syncthreads();
-    // Passes over entry ranges [e0, e1) whose h fits the LDS stage; a slot
-    // contributes in every pass that holds entries of its expert.
-    const int cap = kHStage / I;              // entries per pass (>= 1: I <= kHStage)
-    int u_lo = 0;
-    for (int e0 = 0; e0 < n_ent; e0 += cap) {
-      const int e1 = min(n_ent, e0 + cap);
-      while (S.dn.start[u_lo + 1] <= e0) ++u_lo;
-      int u_hi = u_lo;
-      while (u_hi + 1 < n_units && S.dn.start[u_hi + 1] < e1) ++u_hi;
-      __syncthreads();
-      {
-        const int n4 = (e1 - e0) * (I / 4);
-        for (int q = threadIdx.x; q < n4; q += kFT) {
-          const int en = e0 + q / (I / 4), c4 = q % (I / 4);
-          reinterpret_cast<float4*>(S.dn.h)[q] =
-              reinterpret_cast<const float4*>(a.h + (int64_t)S.dn.pair[en] * I)[c4];
-        }
-      }
-      __syncthreads();
-      const int s_lo = u_lo * per_unit, s_hi = (u_hi + 1) * per_unit;
-      float acc[RDW][kMaxT];
-#pragma unroll
-      for (int r2 = 0; r2 < RDW; ++r2)
-#pragma unroll
-        for (int tt = 0; tt < kMaxT; ++tt) acc[r2][tt] = 0.f;
-      auto consume = [&](int s, const uint4& q, uint32_t sc) {
-        const int u = s / per_unit;
-        const int rem = s - u * per_unit;
-        const int rr = rem / nvi, v = rem - rr * nvi;
-        if (r0 + rr >= H) return;
-        const int ea = max(S.dn.start[u], e0), eb = min(S.dn.start[u + 1], e1);
-        for (int en = ea; en < eb; ++en) {
-          const int t = S.dn.tok[en];
-          const float c = S.dn.gw[en] * wdot_h<WT>(q, sc, &S.dn.h[(en - e0) * I + v * EPV]);
-#pragma unroll
-          for (int r2 = 0; r2 < RDW; ++r2)
-#pragma unroll
-            for (int t2 = 0; t2 < TC; ++t2)
-              if (r2 == rr && t2 == t) acc[r2][t2] += c;
-        }
-      };
-#pragma unroll
-      for (int j = 0; j < PF; ++j) {
-        const int s = lane + 64 * j;
-        if (s >= s_lo && s < s_hi && s < n_slots) consume(s, pre[j], psc[j]);
-      }
-      constexpr int SB = 4;     // streamed slots in flight per lane
-      int s_first = lane + 64 * PF;
-      if (s_first < s_lo) s_first += ((s_lo - s_first + 63) / 64) * 64;
-      for (int s = s_first; s - lane < s_hi; s += 64 * SB) {
-        uint4 q[SB];
-        uint32_t sc[SB];
-#pragma unroll
-        for (int i = 0; i < SB; ++i)
-          if (s + 64 * i < s_hi) slot_load(s + 64 * i, q[i], sc[i]);
-#pragma unroll
-        for (int i = 0; i < SB; ++i)
-          if (s + 64 * i < s_hi) consume(s + 64 * i, q[i], sc[i]);
-      }
-#pragma unroll
-      for (int r2 = 0; r2 < RDW; ++r2) {
-#pragma unroll
-        for (int tt = 0; tt < TC; ++tt) {
-          const float v = wave_sum_dpp(acc[r2][tt]);
-          const int row = r0 + r2;
-          if (lane == 0 && row < H && tt < T) {
-            float* yp = a.y + (int64_t)tt * H + row;
-            *yp = (e0 == 0 ? 0.f : *yp) + v;
-          }
-        }
-      }
-    }
-    if (n_ent == 0) {
-      // nothing resident: y is zero
-#pragma unroll
-      for (int r2 = 0; r2 < RDW; ++r2)
-        for (int t = lane; t < T; t += 64)
-          if (r0 + r2 < H) a.y[(int64_t)t * H + r0 + r2] = 0.f;
+      for (int c = 0; c < EPV / 4; ++c) hv.v[n][c] = hs[c * V + j + a.lr * n];
     }
   }
+}
 
-  // ------------------------------ exit ------------------------------------
-  stamp(a, 3);
+// Down rows of one workgroup: its share [d0, d1) of the flattened (unit, row
+// of H) list is taken one unit segment at a time; a segment's rows are walked
+// in steps of kW * (64 / lr) rows, each wave taking 64 / lr rows per step with
+// lr lanes per row and nv vectors per lane (lane j of a row group holds
+// vectors j, j + lr, ...).
+struct DnMap {
+  int64_t lo, hi;    // rows of the current segment
+  int rpw;           // rows per wave per step
+  int grp, j;        // row group of this lane, lane within it
+  __device__ int64_t row(int step, int wave) const {
+    return lo + (int64_t)step * kW * rpw + wave * rpw + grp;
+  }
+  __device__ int steps() const { return (int)((hi - lo + kW * rpw - 1) / (kW * rpw)); }
+};
+
+// Always NVC loads (rows past the segment read its first row, vectors past nv
+// read vector j; neither is used), so that every step issues the same loads
+// and the waits for a step's data can be counted exactly.
+template <int WT, int NVC>
+__device__ __forceinline__ void dn_load(const DecArgs& a, const DecLds& S, const DnMap& m,
+                                        int u, int64_t row, DnBuf<NVC>& b) {
+  const int r = (int)((row < m.hi ? row : m.lo) - (int64_t)u * a.H);
+  const uint8_t* base = unit_base(a, S.p.unit_slot[u]);
+#pragma unroll
+  for (int n = 0; n < NVC; ++n) {
+    const int v = m.j + (n < a.nv ? a.lr * n : 0);
+    if (WT == 1) {
+      b.q[n] = ldg16(base + a.off[2] + ((int64_t)r * a.I + (int64_t)v * 8) * 2);
+    } else {
+      b.q[n] = ldg16(base + a.off[4] + (int64_t)r * (a.I / 2) + (int64_t)v * 16);
+      b.s[n] = (base + a.off[5])[(int64_t)r * (a.I / 32) + v];
+    }
+  }
+}
+
+// y results of a wave to memory (fp32 atomics; index -1: none)
+__device__ __forceinline__ void flush_y(const DecArgs& a, WaveOut& o) {
+  const int lane = threadIdx.x & 63;
+  for (int q = lane; q < o.n; q += 64) {
+    const int2 p = o.buf[q];
+    if (p.x >= 0) unsafeAtomicAdd(a.y + p.x, __int_as_float(p.y));
+  }
+  o.n = 0;
+}
+
+// row (of unit u) . h for the staged entries [c0, c1), each result times the
+// entry's gate weight listed for y[token][row].  A single entry's h values
+// come in registers when they fit (hv), else from LDS per row.  Rows past the
+// segment (unused weights) list index -1.  The list has room for the pass.
+template <int WT, int NVC>
+__device__ __forceinline__ void dn_compute(const DecArgs& a, const DecLds& S, const DnMap& m,
+                                           int u, int64_t row, int c0, int c1,
+                                           const DnBuf<NVC>& b, const HRegs<WT, NVC>& hv,
+                                           WaveOut& out) {
+  constexpr int EPV = WT == 1 ? 8 : 32;
+  const bool valid = row < m.hi;
+  const int r = (int)(row - (int64_t)u * a.H);
+  const int V = a.I / EPV;
+  for (int en = c0; en < c1; ++en) {
+    float s = 0.f;
+    if (HRegs<WT, NVC>::kOn && c1 - c0 == 1) {
+#pragma unroll
+      for (int n = 0; n < NVC; ++n) {
+        if (n >= a.nv) break;
+        s += wdot_h<WT>(b.q[n], b.s[n], hv.v[HRegs<WT, NVC>::kOn ? n : 0]);
+      }
+    } else {
+      const float4* hs = S.hs + (en - c0) * (a.I / 4);
+#pragma unroll
+      for (int n = 0; n < NVC; ++n) {
+        if (n >= a.nv) break;
+        float4 h4[EPV / 4];
+#pragma unroll
+        for (int c = 0; c < EPV / 4; ++c) h4[c] = hs[c * V + m.j + a.lr * n];
+        s += wdot_h<WT>(b.q[n], b.s[n], h4);
+      }
+    }
+    s = group_sum(s, a.lr);
+    if (m.j == 0)
+      out.buf[out.n + m.grp] =
+          make_int2(valid ? S.p.ent_tok[en] * a.H + r : -1, __float_as_int(S.p.ent_gw[en] * s));
+    out.n += m.rpw;
+  }
+}
+
+// stage h of entries [c0, c1) into LDS (coherent loads, transposed layout)
+template <int WT>
+__device__ __forceinline__ void stage_h(const DecArgs& a, DecLds& S, __amdgpu_buffer_rsrc_t hr,
+                                        int c0, int c1) {
+  constexpr int EPV = WT == 1 ? 8 : 32;
+  const int I4 = a.I / 4, V = a.I / EPV;
+  const int n4 = (c1 - c0) * I4;
+  for (int q = threadIdx.x; q < n4; q += kT) {
+    const int e = q / I4, c4 = q - e * I4;
+    const int v = c4 / (EPV / 4), cc = c4 - v * (EPV / 4);
+    S.hs[e * I4 + cc * V + v] = coherent_load16(hr, (S.p.ent_pair[c0 + e] * a.I + c4 * 4) * 4);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// the kernel.  WT: 1 BF16, 2 MXFP4.  LXC, NVC: register capacity (vectors per
+// lane) of a gate/up row and of a down row.  M: logits per lane in the wave
+// top-k used for E > kRankMaxE (E <= 64 M).  RG gate/up rows and DD steps of
+// down rows are loaded ahead.
+// ---------------------------------------------------------------------------
+template <int WT, int LXC, int NVC, int M>
+__global__ __launch_bounds__(kT) void decode_kernel(DecArgs a) {
+  constexpr int RGV = WT == 1 ? 32 : 16;   // gate/up vectors in flight per lane
+  constexpr int RG = RGV / (2 * LXC) > 0 ? RGV / (2 * LXC) : 1;
+  constexpr int DDV = WT == 1 ? 16 : (LXC >= 4 ? 4 : 8);  // down vectors in flight per lane
+  constexpr int DD = NVC >= DDV ? 1 : DDV / NVC;
+  __shared__ DecLds S;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int bid = blockIdx.x, G = a.G;
+  const bool route = a.NRW > 0;
+  const bool timing = a.hdr[kHTiming] != 0;     // uniform: a scalar load
+  stamp(timing, a, 0);
+
+  // 1. router rows; x into LDS; clear y; the shared expert's gate/up rows
+  if (bid < a.NRW) {
+    router_rows(a);
+    stamp(timing, a, 5);
+    signal_done(a.hdr + kHRouted);
+  }
+  stage_x<WT>(a, S);
+  {
+    int64_t lo, hi;
+    split((int64_t)a.T * a.H, G, bid, lo, hi);
+    for (int64_t i = lo + threadIdx.x; i < hi; i += kT) coherent_store(a.y + i, 0.f);
+  }
+  __syncthreads();
+  if (a.shared) {
+    int64_t lo, hi;
+    split(a.I, G, bid, lo, hi);
+    gateup_range<WT, LXC, RG, true>(a, S, lo, hi, [] {});
+  }
+
+  // 2. the expert list
+  if (route) {
+    if (threadIdx.x == 0) wait_geq(a, a.hdr + kHRouted, (unsigned)a.NRW);
+    __syncthreads();
+    stamp(timing, a, 6);
+  }
+  build_units<M>(a, S, route);
+  stamp(timing, a, 1);
+  const int n_routed = S.p.n_routed, n_units = S.p.n_units;
+
+  // 3. routed gate/up rows
+  int64_t d0, d1;
+  split((int64_t)n_units * a.H, G, bid, d0, d1);
+  DnMap m;
+  m.rpw = 64 / a.lr;
+  m.grp = lane / a.lr;
+  m.j = lane - m.grp * a.lr;
+  m.lo = d0;
+  m.hi = d0 < d1 ? min(d1, (d0 / a.H + 1) * (int64_t)a.H) : d1;
+  DnBuf<NVC> ring[DD];
+  {
+    int64_t lo, hi;
+    split((int64_t)n_routed * a.I, G, bid, lo, hi);
+    gateup_range<WT, LXC, RG, false>(a, S, lo, hi, [] {});
+  }
+
+  // 4. count this workgroup done, issue the first down rows' loads, then the
+  // grid-wide wait for h
+  stamp(timing, a, 7);
+  signal_done(a.hdr + kHGateUp);
+  if (m.lo < d1) {
+    const int u = (int)(m.lo / a.H);
+#pragma unroll
+    for (int d = 0; d < DD; ++d) dn_load<WT, NVC>(a, S, m, u, m.row(d, wave), ring[d]);
+  }
+  if (threadIdx.x == 0) wait_geq(a, a.hdr + kHGateUp, (unsigned)G);
+  __syncthreads();
+  stamp(timing, a, 2);
+
+  // 5. down rows, unit segment by segment; h of up to ce entries staged at a
+  // time (and no more than the per-wave y list holds over a segment); DD
+  // steps of weight loads in flight
+  const __amdgpu_buffer_rsrc_t hr = __builtin_amdgcn_make_buffer_rsrc(
+      a.h, 0, (a.T * a.k + a.T) * a.I * 4, 0x00020000);
+  WaveOut out;                             // y results, in the x stage
+  out.cap = kXStage16 * 2 / kW;
+  out.buf = reinterpret_cast<int2*>(S.xs) + wave * out.cap;
+  out.n = 0;
+  int ce = kHStage4 / (a.I / 4);
+  {
+    const int per_entry = (a.H / (kW * m.rpw) + 1 + DD) * m.rpw;  // list slots per entry
+    if (ce > out.cap / per_entry) ce = out.cap / per_entry;
+    if (ce < 1) ce = 1;
+  }
+  bool loaded = true;                      // ring holds the segment's first steps
+  while (m.lo < d1) {
+    const int u = (int)(m.lo / a.H);
+    const int e0 = S.p.unit_start[u], e1 = S.p.unit_start[u + 1];
+    const int ns = m.steps();
+    for (int c0 = e0; c0 < e1; c0 += ce) {
+      const int c1 = min(e1, c0 + ce);
+      __syncthreads();
+      stage_h<WT>(a, S, hr, c0, c1);
+      if (!loaded) {
+#pragma unroll
+        for (int d = 0; d < DD; ++d) dn_load<WT, NVC>(a, S, m, u, m.row(d, wave), ring[d]);
+      }
+      loaded = false;
+      __syncthreads();
+      stamp(timing, a, 11);
+      HRegs<WT, NVC> hv;
+      if (c1 - c0 == 1) h_regs<WT, NVC>(a, S.hs, m.j, hv);
+      for (int s0 = 0; s0 < ns; s0 += DD) {
+#pragma unroll
+        for (int d = 0; d < DD; ++d) {
+          dn_compute<WT, NVC>(a, S, m, u, m.row(s0 + d, wave), c0, c1, ring[d], hv, out);
+          dn_load<WT, NVC>(a, S, m, u, m.row(s0 + d + DD, wave), ring[d]);
+        }
+      }
+      flush_y(a, out);
+    }
+    stamp(timing, a, 12);
+    m.lo = m.hi;
+    m.hi = min(d1, m.lo + a.H);
+  }
+
+  // exit: the last workgroup out resets the counters for the next call
+  stamp(timing, a, 3);
   __syncthreads();
   if (threadIdx.x == 0) {
     const unsigned old =
         __hip_atomic_fetch_add(a.hdr + kHExit, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (old == gridDim.x - 1) {
+    if (old == (unsigned)G - 1) {
       __hip_atomic_store(a.hdr + kHRouted, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(a.hdr + kHPlan, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       __hip_atomic_store(a.hdr + kHGateUp, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       __hip_atomic_store(a.hdr + kHExit, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       if (a.hdr[kHTiming])
@@ -633,9 +897,36 @@ __global__ __launch_bounds__(kFT, 4) void flow_kernel(FlowArgs a) {
   }
 }
 
+// capacities compiled per weight format
+inline int lx_cap(int lx) { return lx <= 1 ? 1 : lx <= 2 ? 2 : lx <= 4 ? 4 : lx <= 8 ? 8 : -1; }
+inline int nv_cap(int nv) { return nv <= 1 ? 1 : nv <= 2 ? 2 : nv <= 4 ? 4 : nv <= 8 ? 8 : -1; }
+
+// largest I the staged h of one entry fits
+constexpr int kMaxI = 4 * kHStage4;
+
+// tokens one launch can take: x of all of them must fit the LDS stage
+inline int max_tokens(int H) {
+  const int t = kXStage16 * 8 / H;
+  return t < kMaxT ? t : kMaxT;
+}
+
+// Down row mapping of I / EPV vectors per row: lr = the largest power of two
+// <= 64 dividing it, nv = vectors per lane.  False when nv exceeds 8.
+inline bool down_map(int nvec, int* lr, int* nv) {
+  if (nvec <= 0) return false;
+  int l = 64;
+  while (nvec % l) l >>= 1;
+  *lr = l;
+  *nv = nvec / l;
+  return *nv <= 8;
+}
+
 // ---------------------------------------------------------------------------
 // standalone router (moe_route, T <= 64): one wave per row, last workgroup ranks
 // ---------------------------------------------------------------------------
+constexpr int kRT = 256;            // threads per router workgroup
+constexpr int kRW = kRT / 64;
+
 struct RouteArgs {
   const uint16_t* x;
   const void* wr;
@@ -647,10 +938,10 @@ struct RouteArgs {
 };
 
 template <bool RF32, int L, int M>
-__global__ __launch_bounds__(kFT) void route_kernel(RouteArgs a) {
+__global__ __launch_bounds__(kRT) void route_kernel(RouteArgs a) {
   __shared__ int s_last;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int e = blockIdx.x * kFW + wave;
+  const int e = blockIdx.x * kRW + wave;
   const int H = a.H, E = a.E, T = a.T;
   constexpr int EPV = RF32 ? 4 : 8;
   const int nvr = H / EPV;
@@ -687,13 +978,15 @@ __global__ __launch_bounds__(kFT) void route_kernel(RouteArgs a) {
       if (lane == 0) a.z[(int64_t)t * E + e] = acc;
     }
   }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
   __syncthreads();
-  if (threadIdx.x == 0) s_last = signal_add(a.ticket) == gridDim.x - 1;
+  if (threadIdx.x == 0)
+    s_last = __hip_atomic_fetch_add(a.ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+             gridDim.x - 1;
   __syncthreads();
   if (!s_last) return;
-  if (threadIdx.x == 0) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  __syncthreads();
-  for (int t = wave; t < T; t += kFW)
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  for (int t = wave; t < T; t += kRW)
     topk_one_token<M>(a.z + (int64_t)t * E, E, a.k, a.renorm, a.ids + (int64_t)t * a.k,
                       a.w + (int64_t)t * a.k);
   if (threadIdx.x == 0)
@@ -702,8 +995,7 @@ __global__ __launch_bounds__(kFT) void route_kernel(RouteArgs a) {
 
 template <bool RF32, int L, int M>
 hipError_t launch_route_t(const RouteArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL((route_kernel<RF32, L, M>), dim3((a.E + kFW - 1) / kFW), dim3(kFT), 0, st,
-                     a);
+  hipLaunchKernelGGL((route_kernel<RF32, L, M>), dim3((a.E + kRW - 1) / kRW), dim3(kRT), 0, st, a);
   return hipGetLastError();
 }
 
@@ -726,14 +1018,5 @@ hipError_t launch_route_r(const RouteArgs& a, hipStream_t st) {
   return launch_route_l<RF32, 16>(a, st);
 }
 
-// 16-byte vectors per lane per row, rounded up to a compiled variant
-inline int round_lg(int nvec) {
-  const int l = (nvec + 63) / 64;
-  if (l <= 4) return l < 1 ? 1 : l;
-  if (l <= 6) return 6;
-  if (l <= 8) return 8;
-  return -1;
-}
-
-}  // namespace flow
+}  // namespace dec
 }  // namespace moe

@@ -1,0 +1,78 @@
+// decode_launch.hpp - grid sizing and variant choice of the one-kernel decode
+// (kernel in decode_impl.hpp), instantiated once per weight format.
+#pragma once
+#include "decode_impl.hpp"
+
+#ifndef MOE_DECODE_WPC
+#define MOE_DECODE_WPC 2   // workgroups per compute unit (capped by occupancy)
+#endif
+
+namespace moe {
+namespace dec {
+
+// compute units of the current device, cached per device
+inline int device_cus() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (!cus[dev]) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) n = 0;
+    cus[dev] = n;
+  }
+  return cus[dev];
+}
+
+template <int WT, int LXC, int NVC, int M>
+hipError_t launch_t(DecArgs& a, hipStream_t st) {
+  static const int occ = [] {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_kernel<WT, LXC, NVC, M>, kT, 0) !=
+        hipSuccess)
+      n = 0;
+    return n;
+  }();
+  const int cus = device_cus();
+  if (occ <= 0 || cus <= 0) return hipErrorInvalidConfiguration;
+  // every workgroup must be resident at once (they all meet at one wait)
+  const int cap = cus * (occ < MOE_DECODE_WPC ? occ : MOE_DECODE_WPC);
+  // no more workgroups than about two gate/up rows each
+  const int64_t units = (int64_t)(a.T * a.k < a.E ? a.T * a.k : a.E) + (a.shared ? 1 : 0);
+  const int64_t useful = (units * a.I + 1) / 2;
+  int G = (int)(useful < cap ? useful : cap);
+  if (G < a.NRW) G = a.NRW;
+  if (G > cus * occ || G < 1) return hipErrorInvalidConfiguration;
+  a.G = G;
+  hipLaunchKernelGGL((decode_kernel<WT, LXC, NVC, M>), dim3(G), dim3(kT), 0, st, a);
+  return hipGetLastError();
+}
+
+template <int WT, int LXC, int NVC>
+hipError_t launch_m(DecArgs& a, hipStream_t st) {
+  return a.E <= 256 ? launch_t<WT, LXC, NVC, 4>(a, st) : launch_t<WT, LXC, NVC, 16>(a, st);
+}
+
+template <int WT, int LXC>
+hipError_t launch_n(DecArgs& a, hipStream_t st) {
+  switch (nv_cap(a.nv)) {
+    case 1: return launch_m<WT, LXC, 1>(a, st);
+    case 2: return launch_m<WT, LXC, 2>(a, st);
+    case 4: return launch_m<WT, LXC, 4>(a, st);
+    case 8: return launch_m<WT, LXC, 8>(a, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <int WT>
+hipError_t launch_w(DecArgs& a, hipStream_t st) {
+  switch (lx_cap(a.lx)) {
+    case 1: return launch_n<WT, 1>(a, st);
+    case 2: return launch_n<WT, 2>(a, st);
+    case 4: return launch_n<WT, 4>(a, st);
+    case 8: return launch_n<WT, 8>(a, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace dec
+}  // namespace moe

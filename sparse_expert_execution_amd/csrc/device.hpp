@@ -244,7 +244,9 @@ __device__ __forceinline__ uint64_t wave_max_u64_dpp(uint64_t v) {
 // order-preserving (value, lower id first) keys; probabilities from a
 // max-subtracted softmax over all E logits.
 // M = ceil(E / 64) logits per lane (E <= 64 * M).
-template <int M>
+// SC1: read the logits with agent-coherent loads (written by other
+// workgroups of the same kernel).
+template <int M, bool SC1 = false>
 __device__ inline void topk_one_token(const float* zt, int E, int k, int renorm, int32_t* ids_out,
                                       float* w_out) {
   const int lane = threadIdx.x & 63;
@@ -255,7 +257,11 @@ __device__ inline void topk_one_token(const float* zt, int E, int k, int renorm,
   for (int i = 0; i < M; ++i) {
     const int e = lane + 64 * i;
     live[i] = e < E;
-    v[i] = live[i] ? zt[e] : -INFINITY;
+    if (SC1)
+      v[i] = live[i] ? __hip_atomic_load(zt + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                     : -INFINITY;
+    else
+      v[i] = live[i] ? zt[e] : -INFINITY;
     m = fmaxf(m, v[i]);
   }
   m = wave_max_dpp(m);

@@ -6,7 +6,7 @@
 
 namespace moe {
 
-struct FlowLaunch {
+struct DecodeLaunch {
   const void* x;
   const void* w_router;   // null: ids / w are inputs
   int router_f32, renorm;
@@ -15,8 +15,7 @@ struct FlowLaunch {
   const int32_t* slot_of;
   const void* pool;
   const void* shared;
-  unsigned* hdr;          // 256-byte header (zero before first use)
-  void* plan;             // decode_plan_bytes()
+  unsigned* hdr;          // counter header (zero before first use)
   float* z;               // [T][E]
   float* h;               // [T*k + T][I]
   float* y;
@@ -59,10 +58,11 @@ hipError_t launch_route_large(const void* x, const void* w_router, int router_f3
                               int H, int E, int k, int renorm, float* logits, int32_t* ids,
                               float* w, hipStream_t st);
 
-// decode: router (optional) + experts + combine in one kernel
+// decode: router (optional) + experts + combine in one kernel, at most
+// decode_max_tokens(H) tokens per launch
 bool decode_shape_supported(int wtype, int H, int I);
-size_t decode_plan_bytes();
-hipError_t launch_decode_flow(const FlowLaunch& f, hipStream_t st);
+int decode_max_tokens(int H);
+hipError_t launch_decode(const DecodeLaunch& f, hipStream_t st);
 
 // prefill
 constexpr int kPrefillChunk = 256;   // pairs per sort chunk
