@@ -16,7 +16,6 @@ One JSON line is printed on stdout; progress goes to stderr.
 """
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -37,23 +36,16 @@ def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
 
-def kernel_source_hash(files):
-    h = hashlib.sha256()
-    for f in files:
-        with open(os.path.join(ROOT, "sparse_expert_execution_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
-    return h.hexdigest()[:16]
-
-
-def traffic_record(name, src_files):
+def traffic_record(name):
     """HBM traffic per launch from the committed rocprofv3 counter summary,
     or None when the kernel sources changed since the counters were taken."""
+    from sparse_expert_execution_amd import profiling
     path = os.path.join(ROOT, "profiles", f"{name}.traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("source_hash") != kernel_source_hash(src_files):
+    if rec.get("source_hash") != profiling.source_hash():
         return None
     return rec.get("bytes_per_launch")
 
@@ -131,17 +123,23 @@ def time_decode(ops, Lw, T, steps, warmup, mode="decode"):
     torch.cuda.synchronize()
     # distinct experts actually touched per layer (for the algorithmic bytes)
     distinct = [int(np.unique(i.cpu().numpy()).size) for i in ids]
-    evs = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
-            for _ in range(n_layers)] for _ in range(steps)]
+    # the timed steps: calls back to back, events only around the whole run
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0.record(stream)
     for st in range(steps):
-        one_step(evs[st])
+        one_step()
     t1.record(stream)
     torch.cuda.synchronize()
     total_ms = t0.elapsed_time(t1)
+    # a second pass with events around every expert call, on the stream the
+    # kernels run on, for the per-launch duration of the dominant kernel
+    evs = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
+            for _ in range(n_layers)] for _ in range(steps)]
+    for st in range(steps):
+        one_step(evs[st])
+    torch.cuda.synchronize()
     call_ms = np.array([[e[0].elapsed_time(e[1]) for e in row] for row in evs])
     return {"total_ms": total_ms, "step_ms": total_ms / steps, "call_ms": call_ms,
             "distinct": distinct, "ids": [i.cpu().numpy() for i in ids]}
@@ -382,7 +380,7 @@ def main():
         cpu = cpu_baseline("qwen_bf16_decode", 1, 4)
         log(json.dumps(cpu))
 
-    traffic = traffic_record("decode_qwen_bf16_T1", ["decode.hip", "device.hpp"])
+    traffic = traffic_record("decode_qwen_bf16_T1")
     out = {
         "metric": "MoE layer decode us/token (HBM GB/s %peak); prefill tokens/s (MFMA %peak)",
         "value": head["us_per_token_per_layer"],

@@ -1,0 +1,175 @@
+"""Reproducible inputs for rocprofv3 and the summaries kept under profiles/.
+
+    python -m sparse_expert_execution_amd.profiling run <workload> [--tokens T]
+        [--layers L] [--calls N]
+        Builds L synthetic layers of a decode workload and makes N
+        moe_route_decode calls over them, then one HBM read-probe launch of a
+        known size and one plain device copy of a known size; run it under
+        ``rocprofv3 --pmc FETCH_SIZE`` (then WRITE_SIZE) to calibrate the
+        counters against kernels whose traffic is known.
+
+    python -m sparse_expert_execution_amd.profiling summarize --name NAME
+        --stats run_kernel_stats.csv --fetch fetch.csv --write write.csv
+        --alg-bytes B --cmd-stats "..." --cmd-fetch "..." --cmd-write "..."
+        Writes profiles/NAME.md (per-kernel durations, bytes per launch) and
+        profiles/NAME.traffic.json (HBM bytes per decode launch, scaled by the
+        calibration, with a hash of the kernel sources it was taken on).
+
+The traffic is per launch of the decode kernel: FETCH_SIZE and WRITE_SIZE are
+KiB per dispatch summed over the L2 channels; each is multiplied by
+known_bytes / (counter * 1024) of its calibration kernel.
+"""
+
+import argparse
+import csv
+import hashlib
+import json
+import os
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+DECODE_SOURCES = ["decode_impl.hpp", "decode_launch.hpp", "decode.hip", "decode_bf16.hip",
+                  "decode_mxfp4.hip", "device.hpp"]
+PROBE_BYTES = 256 << 20
+COPY_BYTES = 256 << 20
+
+
+def source_hash(files=DECODE_SOURCES):
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, "sparse_expert_execution_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def cmd_run(args):
+    import torch
+    sys.path.insert(0, ROOT)
+    import synth
+    from sparse_expert_execution_amd import ops
+    s = synth.SHAPES[args.workload]
+    desc = ops.make_desc(s["hidden"], s["inter"], s["n_experts"], s["top_k"],
+                         has_shared=s["shared"], wtype=s["wtype"], router_wtype="bf16")
+    _, eb = ops.expert_layout(desc)
+    E, T = s["n_experts"], args.tokens
+    layers = []
+    for l in range(args.layers):
+        pool = torch.empty(E * eb, dtype=torch.uint8, device="cuda")
+        for e in range(E):
+            ops.pack_expert(desc, pool[e * eb:(e + 1) * eb],
+                            *synth.expert_weights(args.workload, l, e, device="cuda"))
+        sh = None
+        if s["shared"]:
+            sh = torch.empty(eb, dtype=torch.uint8, device="cuda")
+            ops.pack_expert(desc, sh, *synth.expert_weights(args.workload, l, E, device="cuda"))
+        layers.append((pool, sh, synth.router_weights(args.workload, l, device="cuda"),
+                       synth.tokens(args.workload, l, T, device="cuda")))
+    ids = torch.empty((T, s["top_k"]), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, s["top_k"]), dtype=torch.float32, device="cuda")
+    y = torch.empty((T, s["hidden"]), dtype=torch.float32, device="cuda")
+    ws = ops.workspace(desc, T, 1)
+    torch.cuda.synchronize()
+    for c in range(args.calls):
+        pool, sh, wr, x = layers[c % len(layers)]
+        ops.route_decode(desc, x, wr, ids, w, pool, y, ws, shared=sh)
+    torch.cuda.synchronize()
+    # calibration: a read of PROBE_BYTES, a copy writing COPY_BYTES
+    buf = torch.empty(PROBE_BYTES, dtype=torch.uint8, device="cuda")
+    buf.fill_(1)
+    out = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ops.read_probe(buf, 8192, out)
+    src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(2.0)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    print(f"profiling run: {args.calls} decode calls of {args.workload} T={T}, probe "
+          f"{PROBE_BYTES} B, copy {COPY_BYTES} B", flush=True)
+
+
+def _counter_rows(path, counter):
+    rows = []
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if r.get("Counter_Name") == counter:
+                rows.append((r["Kernel_Name"], float(r["Counter_Value"])))
+    return rows
+
+
+def _mean(xs):
+    return sum(xs) / len(xs) if xs else None
+
+
+def cmd_summarize(args):
+    stats = list(csv.DictReader(open(args.stats)))
+    fetch = _counter_rows(args.fetch, "FETCH_SIZE")
+    write = _counter_rows(args.write, "WRITE_SIZE")
+    dec = lambda n: "decode_kernel" in n
+    probe = lambda n: "read_probe" in n
+    copy = lambda n: "copy" in n.lower() or "elementwise" in n.lower()
+    f_dec = _mean([v for n, v in fetch if dec(n)])
+    f_probe = _mean([v for n, v in fetch if probe(n)])
+    w_dec = _mean([v for n, v in write if dec(n)])
+    w_copy = max([v for n, v in write if copy(n)] or [0.0]) or None
+    f_scale = PROBE_BYTES / (f_probe * 1024) if f_probe else None
+    w_scale = COPY_BYTES / (w_copy * 1024) if w_copy else None
+    fetch_b = f_dec * 1024 * f_scale if f_dec and f_scale else None
+    write_b = w_dec * 1024 * w_scale if w_dec is not None and w_scale else None
+    total = (fetch_b or 0) + (write_b or 0) if fetch_b is not None else None
+    rec = {"name": args.name, "source_hash": source_hash(),
+           "bytes_per_launch": total, "fetch_bytes_per_launch": fetch_b,
+           "write_bytes_per_launch": write_b, "alg_bytes_per_launch": args.alg_bytes,
+           "fetch_scale": f_scale, "write_scale": w_scale,
+           "fetch_kib_raw": f_dec, "write_kib_raw": w_dec,
+           "probe_fetch_kib": f_probe, "copy_write_kib": w_copy,
+           "cmd_fetch": args.cmd_fetch, "cmd_write": args.cmd_write}
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    with open(os.path.join(ROOT, "profiles", f"{args.name}.traffic.json"), "w") as f:
+        json.dump(rec, f, indent=1)
+    lines = [f"# {args.name}", "", "Kernel trace (rocprofv3 --kernel-trace --stats):", "",
+             f"    {args.cmd_stats}", "", "| kernel | calls | avg us | min us | max us | % |",
+             "|---|---|---|---|---|---|"]
+    for r in sorted(stats, key=lambda r: -float(r["TotalDurationNs"]))[:12]:
+        lines.append(f"| {r['Name'][:80]} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
+                     f"{float(r['Percentage']):.1f} |")
+    lines += ["", "HBM traffic of the decode kernel (rocprofv3 --pmc, one counter per run):", "",
+              f"    {args.cmd_fetch}", f"    {args.cmd_write}", "",
+              f"- FETCH_SIZE per launch: {f_dec} KiB raw; read-probe calibration "
+              f"{f_probe} KiB for {PROBE_BYTES} B -> scale {f_scale}",
+              f"- WRITE_SIZE per launch: {w_dec} KiB raw; copy calibration {w_copy} KiB for "
+              f"{COPY_BYTES} B -> scale {w_scale}",
+              f"- traffic per launch: {total} B (algorithmic {args.alg_bytes} B)",
+              f"- kernel sources hash: {rec['source_hash']}"]
+    with open(os.path.join(ROOT, "profiles", f"{args.name}.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(json.dumps(rec))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    r = sub.add_parser("run")
+    r.add_argument("workload")
+    r.add_argument("--tokens", type=int, default=1)
+    r.add_argument("--layers", type=int, default=8)
+    r.add_argument("--calls", type=int, default=16)
+    s = sub.add_parser("summarize")
+    s.add_argument("--name", required=True)
+    s.add_argument("--stats", required=True)
+    s.add_argument("--fetch", required=True)
+    s.add_argument("--write", required=True)
+    s.add_argument("--alg-bytes", type=float, default=None)
+    s.add_argument("--cmd-stats", default="")
+    s.add_argument("--cmd-fetch", default="")
+    s.add_argument("--cmd-write", default="")
+    a = ap.parse_args()
+    if a.cmd == "run":
+        cmd_run(a)
+    else:
+        cmd_summarize(a)
+
+
+if __name__ == "__main__":
+    main()
