@@ -15,8 +15,8 @@
 //   2 per-chunk expert histogram      256 pairs per chunk
 //   3 scan                            segment starts, per-chunk offsets, tiles
 //   4 stable scatter                  sorted_pair[pos] = pair id
-//   5 GEMM1 gate|up + SwiGLU + MXFP4  -> hq (sorted order)
-//   6 GEMM2 down                      -> partial[t][j][H] fp32
+//   5 GEMM1 gate|up + SwiGLU + MXFP4  -> hq (sorted order)      (LDS-tiled)
+//   6 GEMM2 down                      -> partial[t][j][H] fp32    (LDS-tiled)
 //   7 combine                         y[t] = sum_j w[t][j] partial[t][j] (+ shared)
 #include "device.hpp"
 #include "kernels.hpp"
@@ -223,43 +223,145 @@ __device__ __forceinline__ int pair_token(const GemmArgs& a, int p) {
   return p < nr ? p / a.k : p - nr;
 }
 
-// ---- 5: GEMM1 gate|up + SwiGLU + MXFP4(h) ----------------------------------------
-// grid = (max_tiles, I / 64).  4 waves: wm = wave & 1 picks 64 of the tile's
-// 128 rows, wn = wave >> 1 picks 32 of the workgroup's 64 h columns; a wave
-// holds 4 (rows) x 4 (gate lo, gate hi, up lo, up hi) 16x16 accumulators.
-__global__ __launch_bounds__(256) void gemm1_kernel(GemmArgs a) {
+// ---- 5/6: grouped GEMMs on LDS tiles ----------------------------------------------
+// One workgroup computes a 128-row (sorted pairs of one expert) x 256-column
+// tile of A . B^T, K in steps of 128 (one MFMA deep).  The A tile (128 rows x
+// 64 code bytes) and the B tile (256 weight rows) of a step are copied from
+// global memory straight into LDS (global_load_lds, 16 bytes a lane) in
+// fragment order: for each 16-row slice, lane l's 16 bytes are row l % 16,
+// K block l / 16, exactly what the lane feeds the MFMA, so a fragment is one
+// conflict-free 16-byte LDS read.  Scale bytes go to LDS as one dword (the
+// step's 4 K blocks) per row.  kStages - 1 steps are in flight (about 100 KB
+// per CU, one workgroup per CU); each step lives in its own LDS variable.  8
+// waves (two per SIMD, so one's matrix work covers the other's LDS waits) as
+// 2 (64 rows) x 4 (64 B rows); a wave holds 4 x 4 16x16 accumulators.
+//   GEMM1: A = MXFP4(x) rows gathered by token, B = [gate rows c0..c0+127 ;
+//          up rows c0..c0+127]; epilogue h = silu(g) * u -> MXFP4 along I.
+//   GEMM2: A = MXFP4(h) rows (sorted order), B = down rows n0..n0+255;
+//          epilogue writes the pair's partial output row.
+constexpr int kBM = 128, kBN = 256;
+constexpr int kGemmThreads = 512;   // 8 waves, two per SIMD
+constexpr int kStages = 5;
+
+struct Stage {
+  uint4 a[(kBM / 16) * 64];         // 8 slices x 64 lanes x 16 bytes
+  uint4 b[(kBN / 16) * 64];         // 16 slices
+  uint32_t as[kBM];                 // 4 scale bytes (the step's K blocks) per row
+  uint32_t bs[kBN];
+};
+
+__device__ __forceinline__ void dma16(const void* g, void* lds) {
+  __builtin_amdgcn_global_load_lds(g, lds, 16, 0, 0);
+}
+__device__ __forceinline__ void dma4(const void* g, void* lds) {
+  __builtin_amdgcn_global_load_lds(g, lds, 4, 0, 0);
+}
+
+// Four fragments (16 code bytes each) and their scale dwords from LDS byte
+// addresses.  The reads are written out here, with their wait inside the same
+// block, because LDS reads the compiler can see would make it wait for every
+// copy still in flight into any step's buffer, not just the one being read.
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void lds_frag4(const uint32_t (&qa)[4], const uint32_t (&sa)[4],
+                                          u32x4 (&q)[4], uint32_t (&sc)[4]) {
+  asm volatile(
+      "ds_read_b128 %0, %8\n\t"
+      "ds_read_b128 %1, %9\n\t"
+      "ds_read_b128 %2, %10\n\t"
+      "ds_read_b128 %3, %11\n\t"
+      "ds_read_b32 %4, %12\n\t"
+      "ds_read_b32 %5, %13\n\t"
+      "ds_read_b32 %6, %14\n\t"
+      "ds_read_b32 %7, %15\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(q[0]), "=&v"(q[1]), "=&v"(q[2]), "=&v"(q[3]), "=&v"(sc[0]), "=&v"(sc[1]),
+        "=&v"(sc[2]), "=&v"(sc[3])
+      : "v"(qa[0]), "v"(qa[1]), "v"(qa[2]), "v"(qa[3]), "v"(sa[0]), "v"(sa[1]), "v"(sa[2]),
+        "v"(sa[3])
+      : "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)p;
+}
+
+template <int MODE>
+__global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(GemmArgs a) {
+  __shared__ Stage st0, st1, st2, st3, st4;
+  auto stage = [&](int s) -> Stage& {
+    return s == 0 ? st0 : (s == 1 ? st1 : (s == 2 ? st2 : (s == 3 ? st3 : st4)));
+  };
+  const int H = a.H, I = a.I;
+  const int K = MODE == 1 ? H : I;
+  const int nout = MODE == 1 ? I : H;          // output columns of the whole GEMM
+  const int bn = MODE == 1 ? kBN / 2 : kBN;    // output columns of one workgroup
+  // Workgroup ids go round-robin over the 8 XCDs, each with its own L2.  Ids
+  // are grouped so that the nt column tiles of one row tile run together on
+  // one XCD: the row tile's A operand is then fetched from HBM once and served
+  // from that L2 to the other nt - 1 workgroups.
+  const int nt = (nout + bn - 1) / bn;
+  const int gid = blockIdx.x, per_group = 8 * nt;
+  const int rem = gid % per_group;
+  const int tile = (gid / per_group) * 8 + (rem & 7);
+  const int col0 = (rem >> 3) * bn;
   const int n_tiles = a.tiles[0];
-  if ((int)blockIdx.x >= n_tiles) return;
-  const int bin = a.tiles[1 + 2 * blockIdx.x];
-  const int row0 = a.tiles[2 + 2 * blockIdx.x];
+  if (tile >= n_tiles) return;
+  const int bin = a.tiles[1 + 2 * tile];
+  const int row0 = a.tiles[2 + 2 * tile];
   const int seg_end = a.seg_start[bin + 1];
   const uint8_t* base = bin_base(a, bin);
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int wm = wv & 1, wn = wv >> 1;
-  const int c0 = blockIdx.y * 64 + wn * 32;  // first h column of this wave
-  const int H = a.H;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int wm = wv & 1, wn = wv >> 1;         // 2 (64 rows) x 4 (64 B rows)
+  const int fr = lane & 15, fk = lane >> 4;
 
-  // per-lane operand rows
-  const uint8_t* arow_c[4];
-  const uint8_t* arow_s[4];
-  bool a_ok[4];
+  // copy sources of this lane: A slice wv; B slices 2 wv, 2 wv + 1; scale
+  // dwords of A rows 64 (wv & 1) + lane and of B rows 64 (wv & 3) + lane
+  auto a_row_ptrs = [&](int r, const uint8_t*& c, const uint8_t*& sc) {
+    const bool ok = r < seg_end;
+    const int rr = ok ? r : row0;
+    if (MODE == 1) {
+      const int t = pair_token(a, a.sorted_pair[rr]);
+      c = a.xq_codes + (int64_t)t * (H / 2);
+      sc = a.xq_scales + (int64_t)t * (H / 32);
+    } else {
+      c = a.hq_codes + (int64_t)rr * (I / 2);
+      sc = a.hq_scales + (int64_t)rr * (I / 32);
+    }
+  };
+  auto b_row_ptrs = [&](int rt, const uint8_t*& c, const uint8_t*& sc) {
+    // rt: row of the B tile
+    int mat, n;
+    if (MODE == 1) { mat = rt >> 7; n = col0 + (rt & 127); }
+    else { mat = 2; n = col0 + rt; }
+    const int nn = n < nout ? n : 0;
+    c = base + a.off[2 * mat] + (int64_t)nn * (K / 2);
+    sc = base + a.off[2 * mat + 1] + (int64_t)nn * (K / 32);
+  };
+  const uint8_t* ac[1];
+  const uint8_t* bc[2];
+  const uint8_t* as_src;
+  const uint8_t* bs_src;
+  {
+    const uint8_t* dummy;
+    a_row_ptrs(row0 + wv * 16 + fr, ac[0], dummy);
 #pragma unroll
-  for (int ms = 0; ms < 4; ++ms) {
-    const int r = row0 + wm * 64 + ms * 16 + (lane & 15);
-    a_ok[ms] = r < seg_end;
-    const int t = a_ok[ms] ? pair_token(a, a.sorted_pair[r]) : 0;
-    arow_c[ms] = a.xq_codes + (int64_t)t * (H / 2);
-    arow_s[ms] = a.xq_scales + (int64_t)t * (H / 32);
+    for (int j = 0; j < 2; ++j) b_row_ptrs((2 * wv + j) * 16 + fr, bc[j], dummy);
+    const uint8_t* c;
+    a_row_ptrs(row0 + (wv & 1) * 64 + lane, c, as_src);
+    b_row_ptrs((wv & 3) * 64 + lane, c, bs_src);
   }
-  const uint8_t* brow_c[4];
-  const uint8_t* brow_s[4];
+  // every wave issues the same number of copies per step (5), so one count
+  // covers all: the scale dwords are copied by several waves (the same bytes
+  // to the same place)
+  auto issue = [&](int kt, Stage& S) {
+    const int k0 = kt * 128;
+    dma16(ac[0] + k0 / 2 + fk * 16, &S.a[wv * 64]);
 #pragma unroll
-  for (int ns = 0; ns < 4; ++ns) {
-    const int mat = ns >> 1;  // 0 gate, 1 up
-    const int n = c0 + (ns & 1) * 16 + (lane & 15);
-    brow_c[ns] = base + a.off[2 * mat] + (int64_t)n * (H / 2);
-    brow_s[ns] = base + a.off[2 * mat + 1] + (int64_t)n * (H / 32);
-  }
+    for (int j = 0; j < 2; ++j) dma16(bc[j] + k0 / 2 + fk * 16, &S.b[(2 * wv + j) * 64]);
+    dma4(as_src + k0 / 32, &S.as[(wv & 1) * 64]);
+    dma4(bs_src + k0 / 32, &S.bs[(wv & 3) * 64]);
+  };
+  constexpr int kCopies = 5;                   // copies per wave per step
 
   v4f acc[4][4];
 #pragma unroll
@@ -267,118 +369,125 @@ __global__ __launch_bounds__(256) void gemm1_kernel(GemmArgs a) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  for (int k0 = 0; k0 < H; k0 += 128) {
-    Frag fa[4], fb[4];
+  auto compute = [&](const Stage& S) {
+    Frag fa[4];
+    {
+      uint32_t qa[4], sa[4], sc[4];
+      u32x4 q[4];
 #pragma unroll
-    for (int ms = 0; ms < 4; ++ms) fa[ms] = load_frag(arow_c[ms], arow_s[ms], k0, a_ok[ms]);
-#pragma unroll
-    for (int ns = 0; ns < 4; ++ns) fb[ns] = load_frag(brow_c[ns], brow_s[ns], k0, true);
-#pragma unroll
-    for (int ms = 0; ms < 4; ++ms)
-#pragma unroll
-      for (int ns = 0; ns < 4; ++ns) acc[ms][ns] = mfma_fp4(fa[ms], fb[ns], acc[ms][ns]);
-  }
-
-  // epilogue: h = silu(g) * u, quantise each row's 32-column block to MXFP4
-  const int I = a.I;
-#pragma unroll
-  for (int ms = 0; ms < 4; ++ms) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = row0 + wm * 64 + ms * 16 + d_row(lane, i);
-      const float g0 = acc[ms][0][i], g1 = acc[ms][1][i];
-      const float u0 = acc[ms][2][i], u1 = acc[ms][3][i];
-      const float h0 = g0 / (1.0f + expf(-g0)) * u0;
-      const float h1 = g1 / (1.0f + expf(-g1)) * u1;
-      float amax = fmaxf(fabsf(h0), fabsf(h1));
-#pragma unroll
-      for (int off = 1; off < 16; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off, kWave));
-      uint32_t q0 = 0, q1 = 0, sbyte = 0;
-      if (amax > 0.f) {
-        const int X = mx_block_exponent(amax);
-        sbyte = (uint32_t)(X + 127);
-        q0 = e2m1_code(mx_scale_down(h0, X));
-        q1 = e2m1_code(mx_scale_down(h1, X));
+      for (int ms = 0; ms < 4; ++ms) {
+        const int sl = wm * 4 + ms;
+        qa[ms] = lds_addr(&S.a[sl * 64 + lane]);
+        sa[ms] = lds_addr(&S.as[sl * 16 + fr]);
       }
-      const uint32_t n0 = __shfl_xor(q0, 1, kWave);
-      const uint32_t n1 = __shfl_xor(q1, 1, kWave);
-      const int c = d_col(lane);
-      if (r < seg_end) {
-        uint8_t* dst = a.hq_codes + (int64_t)r * (I / 2) + c0 / 2;
-        if ((c & 1) == 0) {
-          dst[c >> 1] = (uint8_t)(q0 | (n0 << 4));
-          dst[8 + (c >> 1)] = (uint8_t)(q1 | (n1 << 4));
-        }
-        if (c == 0) a.hq_scales[(int64_t)r * (I / 32) + c0 / 32] = (uint8_t)sbyte;
+      lds_frag4(qa, sa, q, sc);
+#pragma unroll
+      for (int ms = 0; ms < 4; ++ms) {
+        fa[ms].q = make_uint4(q[ms].x, q[ms].y, q[ms].z, q[ms].w);
+        fa[ms].s = (sc[ms] >> (8 * fk)) & 0xffu;
+      }
+    }
+    {
+      uint32_t qa[4], sa[4], sc[4];
+      u32x4 q[4];
+#pragma unroll
+      for (int ns = 0; ns < 4; ++ns) {
+        // GEMM1: slices 0..7 gate, 8..15 up; wave wn takes 32 h columns of
+        // each (n-slices 0, 1 gate and 2, 3 up)
+        const int sl = MODE == 1 ? (ns >> 1) * 8 + wn * 2 + (ns & 1) : wn * 4 + ns;
+        qa[ns] = lds_addr(&S.b[sl * 64 + lane]);
+        sa[ns] = lds_addr(&S.bs[sl * 16 + fr]);
+      }
+      lds_frag4(qa, sa, q, sc);
+#pragma unroll
+      for (int ns = 0; ns < 4; ++ns) {
+        Frag fb;
+        fb.q = make_uint4(q[ns].x, q[ns].y, q[ns].z, q[ns].w);
+        fb.s = (sc[ns] >> (8 * fk)) & 0xffu;
+#pragma unroll
+        for (int ms = 0; ms < 4; ++ms) acc[ms][ns] = mfma_fp4(fa[ms], fb, acc[ms][ns]);
+      }
+    }
+  };
+
+  const int nk = K / 128;
+  // prologue: steps 0 .. kStages-2 (a step past the end re-reads the last)
+#pragma unroll
+  for (int s = 0; s < kStages - 1; ++s) issue(s < nk ? s : nk - 1, stage(s));
+  for (int kt0 = 0; kt0 < nk; kt0 += kStages) {
+#pragma unroll
+    for (int s = 0; s < kStages; ++s) {
+      const int kt = kt0 + s;
+      if (kt < nk) {
+        // this wave's copies of step kt are done once at most the later
+        // kStages-2 steps' copies are outstanding; the barrier makes every
+        // wave's copies visible and frees the buffer step kt-1 used
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"((kStages - 2) * kCopies) : "memory");
+        __builtin_amdgcn_s_barrier();
+        const int kn = kt + kStages - 1;
+        issue(kn < nk ? kn : nk - 1, stage((s + kStages - 1) % kStages));
+        compute(stage(s));
       }
     }
   }
-}
 
-// ---- 6: GEMM2 down -> per-pair partial rows ----------------------------------------
-// grid = (max_tiles, H / 128).  4 waves as 2 (rows) x 2 (64 output columns).
-__global__ __launch_bounds__(256) void gemm2_kernel(GemmArgs a) {
-  const int n_tiles = a.tiles[0];
-  if ((int)blockIdx.x >= n_tiles) return;
-  const int bin = a.tiles[1 + 2 * blockIdx.x];
-  const int row0 = a.tiles[2 + 2 * blockIdx.x];
-  const int seg_end = a.seg_start[bin + 1];
-  const uint8_t* base = bin_base(a, bin);
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int wm = wv & 1, wn = wv >> 1;
-  const int n0 = blockIdx.y * 128 + wn * 64;
-  const int I = a.I, H = a.H;
-
-  const uint8_t* arow_c[4];
-  const uint8_t* arow_s[4];
-  bool a_ok[4];
+  if (MODE == 1) {
+    // h = silu(g) * u; each row's 32-column block (gate and up n-slice
+    // pairs) to MXFP4
+    const int c0 = col0 + wn * 32;             // first h column of this wave
 #pragma unroll
-  for (int ms = 0; ms < 4; ++ms) {
-    const int r = row0 + wm * 64 + ms * 16 + (lane & 15);
-    a_ok[ms] = r < seg_end;
-    arow_c[ms] = a.hq_codes + (int64_t)r * (I / 2);
-    arow_s[ms] = a.hq_scales + (int64_t)r * (I / 32);
-  }
-  const uint8_t* brow_c[4];
-  const uint8_t* brow_s[4];
+    for (int ms = 0; ms < 4; ++ms) {
+      {
+        constexpr int blk = 0;
 #pragma unroll
-  for (int ns = 0; ns < 4; ++ns) {
-    const int n = n0 + ns * 16 + (lane & 15);
-    brow_c[ns] = base + a.off[4] + (int64_t)n * (I / 2);
-    brow_s[ns] = base + a.off[5] + (int64_t)n * (I / 32);
-  }
-  v4f acc[4][4];
+        for (int i = 0; i < 4; ++i) {
+          const int r = row0 + wm * 64 + ms * 16 + d_row(lane, i);
+          const float g0 = acc[ms][0][i], g1 = acc[ms][1][i];
+          const float u0 = acc[ms][2][i], u1 = acc[ms][3][i];
+          const float h0 = g0 / (1.0f + expf(-g0)) * u0;
+          const float h1 = g1 / (1.0f + expf(-g1)) * u1;
+          float amax = fmaxf(fabsf(h0), fabsf(h1));
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+          for (int off = 1; off < 16; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off, kWave));
+          uint32_t q0 = 0, q1 = 0, sbyte = 0;
+          if (amax > 0.f) {
+            const int X = mx_block_exponent(amax);
+            sbyte = (uint32_t)(X + 127);
+            q0 = e2m1_code(mx_scale_down(h0, X));
+            q1 = e2m1_code(mx_scale_down(h1, X));
+          }
+          const uint32_t n0 = __shfl_xor(q0, 1, kWave);
+          const uint32_t n1 = __shfl_xor(q1, 1, kWave);
+          const int c = d_col(lane);
+          const int cb = c0 + blk * 32;         // first column of the block
+          if (r < seg_end) {
+            uint8_t* dst = a.hq_codes + (int64_t)r * (I / 2) + cb / 2;
+            if ((c & 1) == 0) {
+              dst[c >> 1] = (uint8_t)(q0 | (n0 << 4));
+              dst[8 + (c >> 1)] = (uint8_t)(q1 | (n1 << 4));
+            }
+            if (c == 0) a.hq_scales[(int64_t)r * (I / 32) + cb / 32] = (uint8_t)sbyte;
+          }
+        }
+      }
+    }
+  } else {
+    const int nr = a.T * a.k;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
-
-  for (int k0 = 0; k0 < I; k0 += 128) {
-    Frag fa[4], fb[4];
+    for (int ms = 0; ms < 4; ++ms) {
 #pragma unroll
-    for (int ms = 0; ms < 4; ++ms) fa[ms] = load_frag(arow_c[ms], arow_s[ms], k0, a_ok[ms]);
+      for (int i = 0; i < 4; ++i) {
+        const int r = row0 + wm * 64 + ms * 16 + d_row(lane, i);
+        if (r >= seg_end) continue;
+        const int p = a.sorted_pair[r];
+        int prow;
+        if (p < nr) prow = (p / a.k) * (a.k + 1) + (p % a.k);
+        else prow = (p - nr) * (a.k + 1) + a.k;
+        float* dst = a.partial + (int64_t)prow * H + col0 + wn * 64 + d_col(lane);
 #pragma unroll
-    for (int ns = 0; ns < 4; ++ns) fb[ns] = load_frag(brow_c[ns], brow_s[ns], k0, true);
-#pragma unroll
-    for (int ms = 0; ms < 4; ++ms)
-#pragma unroll
-      for (int ns = 0; ns < 4; ++ns) acc[ms][ns] = mfma_fp4(fa[ms], fb[ns], acc[ms][ns]);
-  }
-
-  const int nr = a.T * a.k;
-#pragma unroll
-  for (int ms = 0; ms < 4; ++ms) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = row0 + wm * 64 + ms * 16 + d_row(lane, i);
-      if (r >= seg_end) continue;
-      const int p = a.sorted_pair[r];
-      int prow;
-      if (p < nr) prow = (p / a.k) * (a.k + 1) + (p % a.k);
-      else prow = (p - nr) * (a.k + 1) + a.k;
-      float* dst = a.partial + (int64_t)prow * H + n0 + d_col(lane);
-#pragma unroll
-      for (int ns = 0; ns < 4; ++ns) dst[ns * 16] = acc[ms][ns][i];
+        for (int ns = 0; ns < 4; ++ns)
+          if (col0 + wn * 64 + ns * 16 < H) dst[ns * 16] = acc[ms][ns][i];
+      }
     }
   }
 }
@@ -469,9 +578,13 @@ hipError_t launch_prefill(const PrefillLaunch& p, hipStream_t st) {
   g.seg_start = p.seg_start; g.tiles = p.tiles; g.sorted_pair = p.sorted_pair;
   g.xq_codes = p.xq_codes; g.xq_scales = p.xq_scales; g.hq_codes = p.hq_codes;
   g.hq_scales = p.hq_scales; g.partial = p.partial;
-  hipLaunchKernelGGL(gemm1_kernel, dim3(p.max_tiles, p.I / 64), dim3(256), 0, st, g);
-  if ((err = hipGetLastError()) != hipSuccess) return err;
-  hipLaunchKernelGGL(gemm2_kernel, dim3(p.max_tiles, p.H / 128), dim3(256), 0, st, g);
+  {
+    const int groups = (p.max_tiles + 7) / 8;
+    const int nt1 = p.I / (kBN / 2), nt2 = (p.H + kBN - 1) / kBN;
+    hipLaunchKernelGGL(gemm_kernel<1>, dim3(groups * 8 * nt1), dim3(kGemmThreads), 0, st, g);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    hipLaunchKernelGGL(gemm_kernel<2>, dim3(groups * 8 * nt2), dim3(kGemmThreads), 0, st, g);
+  }
   if ((err = hipGetLastError()) != hipSuccess) return err;
   {
     const int64_t n = (int64_t)p.T * (p.H / 4);

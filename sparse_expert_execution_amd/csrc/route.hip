@@ -1,4 +1,5 @@
-// route.hip - router logits, softmax and wavefront top-k.
+// route.hip - router logits (BF16 matrix cores for large batches), softmax and
+// wavefront top-k.
 //
 // Each token in each MoE layer is sent to a few of many experts ("FreeToken
 // 753b Model Explained", section of the same name: six of 256 per layer for
@@ -59,6 +60,78 @@ __global__ __launch_bounds__(256) void logits_tiled_kernel(
     }
 }
 
+// ---- large T, BF16 router: 64 tokens x 64 experts per workgroup on BF16 matrix
+// cores (v_mfma_f32_16x16x32_bf16: exact products, fp32 accumulation).  Wave w
+// takes tokens 16w..16w+15 of the tile against all 64 experts (4 tiles of 16),
+// K in chunks of 128 with the next chunk's loads in flight.  Lane l supplies
+// row l % 16 and K elements 8 (l / 16) .. +7 of each 32-deep step; it gets
+// back rows 4 (l / 16) + i, column l % 16 of the 16 x 16 result.
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ bf16x8 as_bf16x8(const uint4 v) {
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+__global__ __launch_bounds__(256) void logits_mfma_kernel(const uint16_t* __restrict__ x,
+                                                          const uint16_t* __restrict__ wr,
+                                                          int T, int H, int E,
+                                                          float* __restrict__ z) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int t0 = blockIdx.x * 64 + wave * 16, e0 = blockIdx.y * 64;
+  const int r = lane & 15, kq = lane >> 4;
+  const bool tok = t0 + r < T;
+  const uint16_t* xr = x + (int64_t)(tok ? t0 + r : 0) * H + kq * 8;
+  const uint16_t* wrow[4];
+  bool eok[4];
+#pragma unroll
+  for (int n = 0; n < 4; ++n) {
+    const int e = e0 + n * 16 + r;
+    eok[n] = e < E;
+    wrow[n] = wr + (int64_t)(eok[n] ? e : 0) * H + kq * 8;
+  }
+  auto load = [&](int k0, uint4 (&a)[4], uint4 (&b)[4][4]) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      a[s] = tok ? ldg16(xr + k0 + 32 * s) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+      for (int n = 0; n < 4; ++n)
+        b[n][s] = eok[n] ? ldg16(wrow[n] + k0 + 32 * s) : make_uint4(0, 0, 0, 0);
+    }
+  };
+  v4f acc[4];
+#pragma unroll
+  for (int n = 0; n < 4; ++n) acc[n] = v4f{0.f, 0.f, 0.f, 0.f};
+  uint4 ca[4], cb[4][4], na[4], nb[4][4];
+  load(0, ca, cb);
+  for (int k0 = 0; k0 < H; k0 += 128) {
+    const bool more = k0 + 128 < H;
+    if (more) load(k0 + 128, na, nb);
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int n = 0; n < 4; ++n)
+        acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ca[s]), as_bf16x8(cb[n][s]),
+                                                         acc[n], 0, 0, 0);
+    if (more) {
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        ca[s] = na[s];
+#pragma unroll
+        for (int n = 0; n < 4; ++n) cb[n][s] = nb[n][s];
+      }
+    }
+  }
+#pragma unroll
+  for (int n = 0; n < 4; ++n) {
+    const int e = e0 + n * 16 + r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = t0 + 4 * kq + i;
+      if (t < T && e < E) z[(int64_t)t * E + e] = acc[n][i];
+    }
+  }
+}
+
 // ---- softmax + top-k: one wave per token --------------------------------------
 template <int M>
 __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ z, int T, int E,
@@ -76,7 +149,10 @@ hipError_t launch_route_large(const void* x, const void* w_router, int router_f3
                               float* w, hipStream_t st) {
   dim3 grid((T + 63) / 64, (E + 63) / 64);
   const uint16_t* xb = static_cast<const uint16_t*>(x);
-  if (router_f32)
+  if (!router_f32 && H % 128 == 0)
+    hipLaunchKernelGGL(logits_mfma_kernel, grid, dim3(256), 0, st, xb,
+                       static_cast<const uint16_t*>(w_router), T, H, E, logits);
+  else if (router_f32)
     hipLaunchKernelGGL((logits_tiled_kernel<true>), grid, dim3(256), 0, st, xb, w_router, T, H, E,
                        logits);
   else

@@ -153,7 +153,9 @@ def _check_route(ops, name, T, renorm=False, layer=0):
 @pytest.mark.parametrize("name,T", [("tiny", 4), ("tiny", 100), ("qwen_bf16_decode", 1),
                                     ("qwen_bf16_decode", 8), ("dsv4_mxfp4_decode", 1),
                                     ("dsv4_mxfp4_decode", 16), ("dsv4_mxfp4_decode", 300),
-                                    ("glm_cache_decode", 3), ("ragged_decode", 64)])
+                                    ("glm_cache_decode", 3), ("ragged_decode", 64),
+                                    ("qwen_bf16_decode", 130), ("ragged_decode", 200),
+                                    ("dsv4_mxfp4_prefill", 4096)])
 def test_route_topk_exact(ops, name, T):
     _say("route", name, T)
     _check_route(ops, name, T)
