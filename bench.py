@@ -199,10 +199,11 @@ def prefill_record(ops, Lw, T, steps, warmup):
 
 def cache_record(ops, steps_limit=None):
     """Expert-cache decode: 64 LRU slots over a 256-expert pinned host pool,
-    Zipf(1.1) trace drifting every 32 steps, q = q* from the measured
-    bandwidths.  Host partial sums are placeholders of the right shape copied
-    from pinned memory and merged (the host-side expert kernel is not part of
-    this path)."""
+    Zipf(1.1) trace drifting every 32 steps, q = q* from the measured PCIe
+    rate and the measured host expert-kernel rate.  Per step: fills on a side
+    stream, the GPU partial over resident + filled experts, the host partial
+    over the other misses (moe_host_experts on the host cores, while the GPU
+    works), then the exact merge on the GPU."""
     name = "glm_cache_decode"
     s = synth.SHAPES[name]
     H, I, E, k, slots = s["hidden"], s["inter"], s["n_experts"], s["top_k"], s["slots"]
@@ -219,15 +220,20 @@ def cache_record(ops, steps_limit=None):
     table = torch.empty((1, E), dtype=torch.int32, device="cuda")
     probe_dev = torch.empty(eb * 4, dtype=torch.uint8, device="cuda")
     bp, bh = ops.probe_bandwidths(host_pool[:eb * 4], probe_dev, reps=3)
+    bx = ops.host_expert_rate(desc, host_pool, n_experts=8, reps=2)
     cache = ops.ExpertCache(host_pool, 1, E, eb, dev_pool, slots, table)
-    cache.set_bandwidths(bp, bh)
+    cache.set_bandwidths(bp, bx)
     ids_tr, w_tr = synth.zipf_trace(E, k, steps, s["zipf"], s["drift"])
     xs = synth.tokens(name, 0, steps, device="cuda")
+    xs_host = xs.cpu()
     d_ids = torch.from_numpy(ids_tr).cuda()
     d_w = torch.from_numpy(w_tr).cuda()
+    h_ids = torch.from_numpy(ids_tr.astype(np.int32))
+    h_w = torch.from_numpy(w_tr.astype(np.float32))
     y = torch.empty((1, H), dtype=torch.float32, device="cuda")
     host_part = torch.zeros((steps, H), dtype=torch.float32).pin_memory()
     dev_part = torch.empty((1, H), dtype=torch.float32, device="cuda")
+    host_experts = 0
     ws = ops.workspace(desc, 1, 1)
     side = torch.cuda.Stream()
     comp = torch.cuda.current_stream()
@@ -247,9 +253,16 @@ def cache_record(ops, steps_limit=None):
         cache.fill(plan, side, comp)
         ops.decode(desc, xs[st:st + 1], d_ids[st:st + 1], d_w[st:st + 1], dev_pool, y, ws,
                    slot_of=table[0])
+        cache.release(plan, comp)
+        # the host side runs while the GPU works on the fills and the decode
+        host = set(int(e) for e in ops.plan_dict(plan)["host"])
+        if host:
+            inc = torch.tensor([[int(e) in host for e in ids_tr[st]]], dtype=torch.uint8)
+            ops.host_experts(desc, xs_host[st:st + 1], h_ids[st:st + 1], h_w[st:st + 1],
+                             host_pool, host_part[st:st + 1], include=inc)
+            host_experts += len(host)
         dev_part.copy_(host_part[st:st + 1], non_blocking=True)
         ops.merge_partials(y, dev_part, y)
-        cache.release(plan, comp)
     t_end.record(comp)
     torch.cuda.synchronize()
     wall = time.time() - wall0
@@ -260,7 +273,8 @@ def cache_record(ops, steps_limit=None):
         "hits": hits, "misses": misses, "filled": fills,
         "miss_rate": misses / max(1, hits + misses),
         "q_hist": np.bincount(np.array(qs), minlength=k + 1).tolist(),
-        "b_pcie_GBps": bp / 1e9, "b_host_GBps": bh / 1e9,
+        "b_pcie_GBps": bp / 1e9, "b_host_read_GBps": bh / 1e9,
+        "b_host_expert_kernel_GBps": bx / 1e9, "host_experts_run": host_experts,
         "fill_GBps": fills * eb / (ms * 1e-3) / 1e9,
     }
 

@@ -332,6 +332,40 @@ int moe_probe_bandwidths(const void* pinned_host, void* dev, size_t bytes,
                          int32_t reps, int32_t threads, void* stream,
                          double* b_pcie, double* b_host);
 
+/* ---- host side of the split -------------------------------------------- */
+/* moe_host_experts: the expert FFNs of the pairs left to the host, on the
+ * host cores, reading expert blocks straight from a (pinned) host pool:
+ *   y[t] = sum over pairs (t, j) with include[t*k + j] != 0 of
+ *          w[t][j] * FFN_{ids[t][j]}(x[t])
+ * with the moe_decode precision contract (x BF16 as given, fp32
+ * accumulation, h in fp32).  A miss can stay where it lives and run there,
+ * its partial sum merged exactly with the GPU's (explainx.ai guide,
+ * "Decode: decide whether to move an expert or compute where it lives").
+ *   x          host [T][H] BF16
+ *   ids, w     host [T][k]
+ *   include    host [T][k] bytes, non-zero = computed here; NULL = all pairs
+ *   host_pool  host blocks of expert_bytes in the moe_expert_layout format
+ *   host_index host [E]: block index of each expert in host_pool; NULL =
+ *              block e holds expert e.  An included expert without a block
+ *              (index < 0) is MOE_EINVAL.
+ *   y          host [T][H] float, overwritten
+ *   n_threads  host threads (0 = all hardware threads); a persistent pool
+ *              is kept between calls.
+ * Blocks the caller.  The shared expert is not part of this call. */
+int moe_host_experts(const moe_desc* desc, const void* x, int32_t T,
+                     const int32_t* ids, const float* w, const uint8_t* include,
+                     const void* host_pool, const int32_t* host_index,
+                     float* y, int32_t n_threads);
+
+/* moe_host_expert_rate: expert bytes per second moe_host_experts streams
+ * from host_pool on one token over its first n_experts_timed experts, best of
+ * reps: the host expert-kernel rate the q* split uses as b_host (the pages
+ * profile the host side's own rate, "FreeToken 753b Model Explained",
+ * "Measure System Bandwidth"). */
+int moe_host_expert_rate(const moe_desc* desc, const void* host_pool,
+                         int32_t n_experts_timed, int32_t reps, int32_t n_threads,
+                         double* bytes_per_s);
+
 /* ---- misc -------------------------------------------------------------- */
 const char* moe_last_error(void);
 int32_t moe_abi_version(void);

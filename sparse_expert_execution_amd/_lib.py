@@ -38,7 +38,7 @@ EXPORTS = (
     "moe_cache_create", "moe_cache_destroy", "moe_cache_set_bandwidths",
     "moe_cache_plan", "cache_fill", "moe_cache_release",
     "moe_cache_debug_fail_fills", "moe_cache_planner", "moe_probe_bandwidths",
-    "moe_last_error", "moe_abi_version",
+    "moe_host_experts", "moe_host_expert_rate", "moe_last_error", "moe_abi_version",
 )
 
 
@@ -115,6 +115,8 @@ def lib():
         "moe_cache_planner": (P, [P]),
         "moe_probe_bandwidths": (ctypes.c_int, [P, P, SZ, I32, I32, P,
                                                 ctypes.POINTER(D), ctypes.POINTER(D)]),
+        "moe_host_experts": (ctypes.c_int, [P, P, I32, P, P, P, P, P, P, I32]),
+        "moe_host_expert_rate": (ctypes.c_int, [P, P, I32, I32, I32, ctypes.POINTER(D)]),
         "moe_last_error": (ctypes.c_char_p, []),
         "moe_abi_version": (I32, []),
     }

@@ -24,9 +24,11 @@ using moe::hip_status;
 using moe::set_error;
 
 namespace {
-
 constexpr size_t kAlign = 256;
 size_t align_up(size_t v) { return (v + kAlign - 1) & ~(kAlign - 1); }
+}  // namespace
+
+namespace moe {
 
 int check_desc(const moe_desc* d) {
   if (!d) return set_error(MOE_EINVAL, "desc is null");
@@ -65,6 +67,13 @@ void layout(const moe_desc* d, size_t off[6], size_t* bytes) {
     *bytes = align_up(3 * cg + 3 * sg);
   }
 }
+
+}  // namespace moe
+
+using moe::check_desc;
+using moe::layout;
+
+namespace {
 
 struct PrefillWs {
   size_t xq_codes, xq_scales, chunk_counts, seg_start, tiles, sorted_pair, hq_codes, hq_scales,
@@ -188,6 +197,8 @@ static int decode_impl(const moe_desc* desc, const void* x, const void* w_router
                        int32_t* ids, float* w, const int32_t* slot_of_expert,
                        const void* slot_pool, const void* shared_expert, float* y, void* ws,
                        size_t ws_bytes, void* stream) {
+  if (desc->top_k > 8)
+    return set_error(MOE_EUNSUPPORTED, "decode supports top_k <= 8 (got %d)", desc->top_k);
   if (T < 0 || T > MOE_DECODE_MAX_T || T * desc->top_k > 1024)
     return set_error(MOE_EINVAL, "decode T %d outside [1, %d] or T*k > 1024", T, MOE_DECODE_MAX_T);
   if (!moe::decode_shape_supported(desc->wtype, desc->hidden, desc->inter))

@@ -223,6 +223,28 @@ class ExpertCache:
         return out
 
 
+def host_experts(desc, x, ids, w, host_pool, y, include=None, host_index=None, threads=0):
+    """moe_host_experts on host tensors: x [T][H] bf16, ids [T][k] int32, w [T][k]
+    float32, include [T][k] uint8 or None, host_pool uint8 (pinned or not),
+    host_index [E] int32 or None, y [T][H] float32 (overwritten)."""
+    for t in (x, ids, w, host_pool, y) + tuple(v for v in (include, host_index) if v is not None):
+        if t.is_cuda:
+            raise ValueError("moe_host_experts takes host tensors")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+    check(lib().moe_host_experts(ctypes.byref(desc), _ptr(x), x.shape[0], _ptr(ids), _ptr(w),
+                                 _ptr(include) if include is not None else None, _ptr(host_pool),
+                                 _ptr(host_index) if host_index is not None else None, _ptr(y),
+                                 threads), "moe_host_experts")
+
+
+def host_expert_rate(desc, host_pool, n_experts=8, reps=3, threads=0):
+    r = ctypes.c_double()
+    check(lib().moe_host_expert_rate(ctypes.byref(desc), _ptr(host_pool), n_experts, reps,
+                                     threads, ctypes.byref(r)), "moe_host_expert_rate")
+    return r.value
+
+
 def probe_bandwidths(pinned_host, dev, reps=3, threads=0, stream=None):
     bp, bh = ctypes.c_double(), ctypes.c_double()
     check(lib().moe_probe_bandwidths(_ptr(pinned_host), _ptr(dev), pinned_host.numel(), reps,

@@ -437,6 +437,47 @@ def test_cache_trace_fills_tables_and_merge(ops):
         assert olayer.row_rel_error(y.cpu().numpy(), full) < TOL, st
 
 
+def test_cache_trace_with_host_experts_merges_to_full_layer(ops):
+    """The whole split: GPU partial over resident + filled experts, host
+    partial over the other misses from moe_host_experts reading the pinned
+    pool, merged on the GPU, equals the full layer (oracle)."""
+    _say("cache trace + host experts")
+    name = "small_cache"
+    s = synth.SHAPES[name]
+    E, k, slots, steps = s["n_experts"], s["top_k"], s["slots"], 24
+    L = GpuLayer(name)
+    eb = L.expert_bytes
+    host_pool = torch.empty(E * eb, dtype=torch.uint8).pin_memory()
+    host_pool.copy_(L.pool.cpu())
+    dev_pool = torch.zeros(slots * eb, dtype=torch.uint8, device="cuda")
+    table = torch.zeros((1, E), dtype=torch.int32, device="cuda")
+    cache = ops.ExpertCache(host_pool, 1, E, eb, dev_pool, slots, table)
+    side = torch.cuda.Stream()
+    comp = torch.cuda.current_stream()
+    ids_tr, w_tr = synth.zipf_trace(E, k, steps, s["zipf"], s["drift"], seed=3)
+    y_host = torch.empty((1, s["hidden"]), dtype=torch.float32).pin_memory()
+    for st in range(steps):
+        ids_np, w_np = ids_tr[st:st + 1], w_tr[st:st + 1]
+        plan = cache.plan(0, ids_np, w_np, 2)
+        cache.fill(plan, side, comp)
+        x = L.tokens(1, stream=st)
+        ids = torch.from_numpy(ids_np.astype(np.int32)).cuda()
+        w = torch.from_numpy(w_np.astype(np.float32)).cuda()
+        y = torch.empty((1, s["hidden"]), dtype=torch.float32, device="cuda")
+        ws = ops.workspace(L.desc, 1, 1)
+        ops.decode(L.desc, x, ids, w, dev_pool, y, ws, slot_of=table[0])
+        cache.release(plan, comp)
+        host = set(ops.plan_dict(plan)["host"])
+        inc = np.array([[int(e) in host for e in ids_np[0]]], dtype=np.uint8)
+        ops.host_experts(L.desc, x.cpu(), torch.from_numpy(ids_np.astype(np.int32)),
+                         torch.from_numpy(w_np.astype(np.float32)), host_pool, y_host,
+                         include=torch.from_numpy(inc))
+        ops.merge_partials(y, y_host.cuda(non_blocking=True), y)
+        torch.cuda.synchronize()
+        full = _oracle_out(L, x, ids_np, w_np)
+        assert olayer.row_rel_error(y.cpu().numpy(), full) < TOL, st
+
+
 def test_cache_injected_fill_failure_rolls_back(ops):
     _say("cache injected failure")
     name = "small_cache"
