@@ -50,6 +50,7 @@ hipError_t launch_decode(const DecodeLaunch& f, hipStream_t st) {
   a.hdr = f.hdr;
   a.z = f.z;
   a.h = f.h;
+  a.st = f.stamps;
   a.y = f.y;
   a.expert_bytes = f.expert_bytes;
   for (int i = 0; i < 6; ++i) a.off[i] = f.off[i];

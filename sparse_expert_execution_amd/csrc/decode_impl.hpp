@@ -49,8 +49,17 @@ constexpr int kMaxUnits = kMaxPairs + 1;
 constexpr int kMaxEntries = kMaxPairs + kMaxT;
 constexpr int kXStage16 = 7680;     // 16-byte words of staged x (120 KB)
 constexpr int kHStage4 = 1536;      // float4s of staged h (24 KB)
+constexpr int kYOut = 512;          // y results per wave list in the down phase
+constexpr int kDnH4 = kXStage16 + kHStage4 - kW * kYOut / 2;  // float4s of staged h (down)
+constexpr int kMaxCE = 2;           // entries per virtual unit of the down phase, at most
 constexpr int kRankMaxE = 256;      // the rank top-k handles E up to this
 constexpr unsigned kSpinLimit = 1u << 21;
+
+// a value the same in every lane of the wave, kept in a scalar register
+__device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ float uni(float v) {
+  return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(v)));
+}
 
 // header words of the workspace: every counter on its own 128-byte line
 enum { kHRouted = 0, kHGateUp = 32, kHExit = 64, kHError = 128, kHTiming = 160, kHStamps = 192 };
@@ -67,6 +76,7 @@ struct DecArgs {
   unsigned* hdr;
   float* z;                // [T][E]
   float* h;                // [T*k + T][I]
+  unsigned long long* st;  // [workgroup][16] phase stamps
   float* y;                // [T][H]
   int64_t expert_bytes;
   int64_t off[6];
@@ -83,11 +93,15 @@ struct DecArgs {
 // (2), exit (3), router rows done (5), past the router wait (6), gate/up done
 // (7), h staged (11), first down segment done (12), and of the last
 // workgroup's exit (4), as uint64 from kHStamps; the same stamps of the
-// grid's last workgroup 16 slots further
+// grid's last workgroup 16 slots further; every workgroup's stamps also go to
+// its own 16 slots of a.st
 __device__ __forceinline__ void stamp(bool on, const DecArgs& a, int i) {
-  if (on && threadIdx.x == 0 && (blockIdx.x == 0 || blockIdx.x == gridDim.x - 1))
-    reinterpret_cast<unsigned long long*>(a.hdr + kHStamps)[i + (blockIdx.x ? 16 : 0)] =
-        wall_clock64();
+  if (on && threadIdx.x == 0) {
+    const unsigned long long c = wall_clock64();
+    a.st[blockIdx.x * 16 + i] = c;
+    if (blockIdx.x == 0 || blockIdx.x == gridDim.x - 1)
+      reinterpret_cast<unsigned long long*>(a.hdr + kHStamps)[i + (blockIdx.x ? 16 : 0)] = c;
+  }
 }
 
 // Data that one workgroup hands to others (z, h, the cleared y) is written
@@ -170,21 +184,31 @@ struct PlanLds {
   int ent_pair[kMaxEntries];     // t*k + j, or T*k + t for the shared expert
   int ent_tok[kMaxEntries];
   float ent_gw[kMaxEntries];
-  int n_routed, n_units;
+  // down work: each unit's entries in chunks of at most CE (virtual units)
+  int vu_unit[kMaxEntries], vu_e0[kMaxEntries], vu_n[kMaxEntries];
+  int n_routed, n_units, n_vu;
 };
 
 struct DecLds {
   PlanLds p;
-  // x of every token: 16-byte word (t * CPV + c) * NV + v holds elements
-  // 8c..8c+7 of weight vector v (CPV = elements per vector / 8, NV vectors
-  // per row), so the lanes of a wave read consecutive words
-  uint4 xs[kXStage16];
   union {
-    float zs[4 * kHStage4];      // logits of every token, rows padded to float4s
-    // h of the entries of one down pass; an entry's I values as float4s at
-    // (c * V + v) for elements 4c..4c+3 of 16-byte weight vector v (V vectors
-    // per row), so the lanes of a row group read consecutive float4s
-    float4 hs[kHStage4];
+    struct {                       // routing and gate/up
+      // x of every token: 16-byte word (t * CPV + c) * NV + v holds elements
+      // 8c..8c+7 of weight vector v (CPV = elements per vector / 8, NV
+      // vectors per row), so the lanes of a wave read consecutive words
+      uint4 xs[kXStage16];
+      union {
+        float zs[4 * kHStage4];    // logits of every token, rows padded to float4s
+        float4 hs[kHStage4];       // per-wave lists of gate/up h results
+      };
+    } g;
+    struct {                       // down
+      int2 yout[kW * kYOut];       // per-wave lists of y results
+      // h of the entries of one down pass; an entry's I values as float4s at
+      // (c * V + v) for elements 4c..4c+3 of 16-byte weight vector v (V
+      // vectors per row), so the lanes of a row group read consecutive float4s
+      float4 hst[kDnH4];
+    } d;
   };
 };
 
@@ -272,11 +296,11 @@ __device__ void rank_topk(const DecArgs& a, DecLds& S) {
   const int E4 = (E + 3) & ~3;             // rows padded to whole float4s with -inf
   for (int i = threadIdx.x; i < T * E4; i += kT) {
     const int t = i / E4, e = i - t * E4;
-    S.zs[i] = e < E ? coherent_load(a.z + (int64_t)t * E + e) : -INFINITY;
+    S.g.zs[i] = e < E ? coherent_load(a.z + (int64_t)t * E + e) : -INFINITY;
   }
   __syncthreads();
   for (int t = wave; t < T; t += kW) {
-    const float* zt = S.zs + t * E4;
+    const float* zt = S.g.zs + t * E4;
     float m = -INFINITY;
     for (int e = lane; e < E; e += 64) m = fmaxf(m, zt[e]);
     m = wave_max_dpp(m);
@@ -294,8 +318,8 @@ __device__ void rank_topk(const DecArgs& a, DecLds& S) {
   for (int i = threadIdx.x; i < n * sp; i += kT) {
     const int item = i / sp, part = i - item * sp;
     const int t = item / E, e = item - t * E;
-    const float4* zt4 = reinterpret_cast<const float4*>(S.zs + t * E4);
-    const float my = S.zs[t * E4 + e];
+    const float4* zt4 = reinterpret_cast<const float4*>(S.g.zs + t * E4);
+    const float my = S.g.zs[t * E4 + e];
     int rank = 0;
 #pragma unroll 4
     for (int c = part; c < E4 / 4; c += sp) {
@@ -331,7 +355,7 @@ __device__ void rank_topk(const DecArgs& a, DecLds& S) {
 // Expert list of this launch, built the same way in every workgroup: the
 // distinct resident experts in order of first appearance over the (token,
 // rank) pairs, each with its pairs in order, then the shared expert.
-template <int M>
+template <int M, int CE>
 __device__ void build_units(const DecArgs& a, DecLds& S, bool route) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int T = a.T, k = a.k, E = a.E, P = T * k;
@@ -404,6 +428,17 @@ __device__ void build_units(const DecArgs& a, DecLds& S, bool route) {
     }
     L.unit_start[n_units] = pos;
     L.n_units = n_units;
+    int nvu = 0;
+    for (int u = 0; u < n_units; ++u) {
+      const int e1 = L.unit_start[u + 1];
+      for (int e = L.unit_start[u]; e < e1; e += CE) {
+        L.vu_unit[nvu] = u;
+        L.vu_e0[nvu] = e;
+        L.vu_n[nvu] = e1 - e < CE ? e1 - e : CE;
+        ++nvu;
+      }
+    }
+    L.n_vu = nvu;
   }
   __syncthreads();
   for (int u = threadIdx.x; u < n_routed; u += kT) {
@@ -445,7 +480,7 @@ __device__ void stage_x(const DecArgs& a, DecLds& S) {
   for (int q = threadIdx.x; q < n; q += kT) {
     const int t = q / (a.H / 8), w8 = q - t * (a.H / 8);
     const int v = w8 / CPV, c = w8 - v * CPV;
-    S.xs[(t * CPV + c) * NV + v] = ldg16(a.x + (int64_t)t * a.H + w8 * 8);
+    S.g.xs[(t * CPV + c) * NV + v] = ldg16(a.x + (int64_t)t * a.H + w8 * 8);
   }
 }
 
@@ -494,7 +529,7 @@ __device__ __forceinline__ float gu_dot(const DecArgs& a, const DecLds& S, const
     const int v = lane + 64 * l;
     if (l >= a.lx || v >= nvh) continue;
     if (WT == 1) {
-      const uint4 xx = S.xs[t * nvh + v];
+      const uint4 xx = S.g.xs[t * nvh + v];
       gp = dot2_bf16(b.g[l].x, xx.x, gp);
       gp = dot2_bf16(b.g[l].y, xx.y, gp);
       gp = dot2_bf16(b.g[l].z, xx.z, gp);
@@ -507,7 +542,7 @@ __device__ __forceinline__ float gu_dot(const DecArgs& a, const DecLds& S, const
       uint32_t xp[16];
 #pragma unroll
       for (int c = 0; c < CPV; ++c) {
-        const uint4 t4 = S.xs[(t * CPV + c) * nvh + v];
+        const uint4 t4 = S.g.xs[(t * CPV + c) * nvh + v];
         xp[4 * c] = t4.x; xp[4 * c + 1] = t4.y; xp[4 * c + 2] = t4.z; xp[4 * c + 3] = t4.w;
       }
       gp = fmaf(dot_fp4_bf16_block(b.g[l], xp), e8m0_to_f32(b.gs[l]), gp);
@@ -537,7 +572,7 @@ __device__ __forceinline__ void flush_h(const DecArgs& a, WaveOut& o) {
 template <int WT, int LXC, int RG, bool SHARED, class After>
 __device__ void gateup_range(const DecArgs& a, DecLds& S, int64_t q0, int64_t q1,
                              After&& after) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = uni((int)(threadIdx.x >> 6));
   const int I = a.I;
   const int64_t first = q0 + wave;
   const int nq = first < q1 ? (int)((q1 - first + kW - 1) / kW) : 0;
@@ -553,7 +588,7 @@ __device__ void gateup_range(const DecArgs& a, DecLds& S, int64_t q0, int64_t q1
   };
   WaveOut out;
   out.cap = kHStage4 / kW * 2;
-  out.buf = reinterpret_cast<int2*>(S.hs) + wave * out.cap;
+  out.buf = reinterpret_cast<int2*>(S.g.hs) + wave * out.cap;
   out.n = 0;
   GuBuf<LXC> buf[RG];
 #pragma unroll
@@ -591,11 +626,154 @@ __device__ void gateup_range(const DecArgs& a, DecLds& S, int64_t q0, int64_t q1
 // ---------------------------------------------------------------------------
 // down rows
 // ---------------------------------------------------------------------------
+// The work is the rows of H of every virtual unit (a unit's entries in chunks
+// of at most CE), flattened unit-major and split evenly over the grid.  A
+// workgroup walks its share in passes: a pass stages h of the entries it needs
+// into LDS once and gathers its y results in per-wave lists, written out at
+// the pass end.  Within a pass the rows go segment by segment (a segment: the
+// pass's rows of one virtual unit) in steps of kW * rpw rows, each wave taking
+// rpw rows per step with lr lanes per row and nv vectors per lane (lane j of a
+// row group holds vectors j, j + lr, ...), so a lane needs the same h values
+// for every row of a segment and keeps them in registers.  The loads of the
+// next DD steps stay in flight across segment boundaries.
 template <int NVC>
 struct DnBuf {
   uint4 q[NVC];
-  uint32_t s[NVC];
+  uint32_t s[NVC];   // MXFP4: the aligned word holding the scale byte
 };
+
+struct DnLane {
+  int rpw;       // rows per wave per step (64 / lr)
+  int grp, j;    // this lane's row group and its lane in the group
+  int sh;        // log2 of the rows per step (kW * rpw)
+};
+
+
+// Cursor over the segments of a pass that ends at row p1 (rows of the
+// flattened virtual-unit list, which stays below 2^31); every field is the
+// same in all lanes.  A segment's weights base and its entries' tokens and
+// gate weights are read once, when the cursor enters it.
+template <int CE>
+struct DnCur {
+  int lo, hi;          // rows of the segment
+  int v;               // its virtual unit
+  int s, ns;           // the step in it, its steps
+  int e0, n;           // its entries
+  int tokH[CE];        // token * H of each entry
+  float gw[CE];        // gate weight of each entry
+  const uint8_t* base; // the unit's weights
+};
+
+template <int CE>
+__device__ __forceinline__ void dn_enter(const DecArgs& a, const DecLds& S, const DnLane& L,
+                                         int v, int lo, int p1, DnCur<CE>& c) {
+  c.v = uni(v);
+  c.lo = uni(lo);
+  const int e = (c.v + 1) * a.H;
+  c.hi = uni(e < p1 ? e : p1);
+  c.s = 0;
+  c.ns = uni((c.hi - c.lo + (1 << L.sh) - 1) >> L.sh);
+  c.e0 = uni(S.p.vu_e0[v]);
+  c.n = uni(S.p.vu_n[v]);
+#pragma unroll
+  for (int i = 0; i < CE; ++i) {
+    const int en = c.e0 + (i < c.n ? i : 0);
+    c.tokH[i] = uni(S.p.ent_tok[en]) * a.H;
+    c.gw[i] = uni(S.p.ent_gw[en]);
+  }
+  c.base = unit_base(a, uni(S.p.unit_slot[uni(S.p.vu_unit[v])]));
+}
+
+// the segment holding row d (any row of the pass)
+template <int CE>
+__device__ __forceinline__ void dn_seg(const DecArgs& a, const DecLds& S, const DnLane& L, int d,
+                                       int p1, DnCur<CE>& c) {
+  dn_enter(a, S, L, d / a.H, d, p1, c);
+}
+
+// past the pass's last step the cursor stays on its last segment
+template <int CE>
+__device__ __forceinline__ void dn_next(const DecArgs& a, const DecLds& S, const DnLane& L, int p1,
+                                        DnCur<CE>& c) {
+  c.s = uni(c.s + 1);
+  if (c.s >= c.ns && c.hi < p1) dn_enter(a, S, L, c.v + 1, c.hi, p1, c);
+}
+
+template <int CE>
+__device__ __forceinline__ int dn_row(const DnLane& L, const DnCur<CE>& c, int wave) {
+  return c.lo + (c.s << L.sh) + wave * L.rpw + L.grp;
+}
+
+// End of the pass that starts at row p0 of a share ending at d1: as many
+// segments as the h stage and the y lists hold (the last one may be cut at a
+// step); *steps = the pass's steps.  The first step always fits (kMaxCE
+// entries of I values fit the stage, kMaxCE * rpw results a list).
+__device__ int pass_end(const DecArgs& a, const DecLds& S, int p0, int d1, const DnLane& L,
+                        int* steps) {
+  const int E0 = uni(S.p.vu_e0[p0 / a.H]);
+  const int hcap = kDnH4 * 4 / a.I;
+  int slots = 0, total = 0;
+  int d = p0;
+  while (d < d1) {
+    const int v = d / a.H;
+    const int e = (v + 1) * a.H;
+    const int hi = e < d1 ? e : d1;
+    const int n = uni(S.p.vu_n[v]);
+    if (uni(S.p.vu_e0[v]) + n - E0 > hcap) break;
+    const int ns = (hi - d + (1 << L.sh) - 1) >> L.sh;
+    const int per = n * L.rpw;
+    if (slots + ns * per > kYOut) {
+      const int k = (kYOut - slots) / per;
+      d += k << L.sh;
+      total += k;
+      break;
+    }
+    slots += ns * per;
+    total += ns;
+    d = hi;
+  }
+  *steps = uni(total);
+  return uni(d);
+}
+
+// Always NVC loads (rows past the segment read its first row, vectors past nv
+// read vector j; neither is used), so that every step issues the same loads
+// and the waits for a step's data can be counted exactly.  MXFP4 scales come
+// as the aligned 32-bit word that holds the byte (within the expert block:
+// the scale array starts and ends on a 32-byte boundary of a 256-byte aligned
+// expert block).
+template <int WT, int NVC, int CE>
+__device__ __forceinline__ void dn_load(const DecArgs& a, const DnLane& L, const DnCur<CE>& c,
+                                        int wave, DnBuf<NVC>& b) {
+  const int row = dn_row(L, c, wave);
+  const int r = (row < c.hi ? row : c.lo) - c.v * a.H;
+#pragma unroll
+  for (int n = 0; n < NVC; ++n) {
+    const int v = L.j + (n < a.nv ? a.lr * n : 0);
+    if (WT == 1) {
+      b.q[n] = ldg16(c.base + a.off[2] + ((int64_t)r * a.I + (int64_t)v * 8) * 2);
+    } else {
+      b.q[n] = ldg16(c.base + a.off[4] + (int64_t)r * (a.I / 2) + (int64_t)v * 16);
+      const int so = r * (a.I / 32) + v;
+      b.s[n] = *reinterpret_cast<const uint32_t*>(c.base + a.off[5] + (so & ~3));
+    }
+  }
+}
+
+// the scale byte of vector v of row r within its loaded word
+__device__ __forceinline__ uint32_t dn_scale(const DecArgs& a, int r, int v, uint32_t word) {
+  return (word >> (((r * (a.I / 32) + v) & 3) * 8)) & 0xffu;
+}
+
+// y results of a wave to memory (fp32 atomics; index -1: none)
+__device__ __forceinline__ void flush_y(const DecArgs& a, WaveOut& o) {
+  const int lane = threadIdx.x & 63;
+  for (int q = lane; q < o.n; q += 64) {
+    const int2 p = o.buf[q];
+    if (p.x >= 0) unsafeAtomicAdd(a.y + p.x, __int_as_float(p.y));
+  }
+  o.n = 0;
+}
 
 // dot of one 16-byte weight vector with its EPV h values (EPV / 4 float4s)
 template <int WT>
@@ -633,113 +811,79 @@ __device__ __forceinline__ float wdot_h(const uint4 q, uint32_t sc, const float4
   }
 }
 
-// h values kept in registers per lane for single-entry passes: EPV floats per
-// down vector, as long as that stays within 32 floats
-template <int WT, int NVC>
+// h values of a segment's entries kept in registers per lane: EPV floats per
+// down vector and entry, as long as that stays within 32 floats per entry
+// (else they are read from the stage per row)
+template <int WT, int NVC, int CE>
 struct HRegs {
   static constexpr int EPV = WT == 1 ? 8 : 32;
   static constexpr bool kOn = NVC * EPV <= 32;
-  float4 v[kOn ? NVC : 1][EPV / 4];
+  float4 v[kOn ? CE : 1][kOn ? NVC : 1][EPV / 4];
 };
 
-// this lane's h values of one staged entry (hs: the entry's float4s)
-template <int WT, int NVC>
-__device__ __forceinline__ void h_regs(const DecArgs& a, const float4* hs, int j,
-                                       HRegs<WT, NVC>& hv) {
+// this lane's h values of staged entries [er, er + n)
+template <int WT, int NVC, int CE>
+__device__ __forceinline__ void h_regs(const DecArgs& a, const DecLds& S, int j, int er, int n,
+                                       HRegs<WT, NVC, CE>& hv) {
   constexpr int EPV = WT == 1 ? 8 : 32;
-  if constexpr (HRegs<WT, NVC>::kOn) {
-    const int V = a.I / EPV;
+  if constexpr (HRegs<WT, NVC, CE>::kOn) {
+    const int V = a.I / EPV, I4 = a.I / 4;
 #pragma unroll
-    for (int n = 0; n < NVC; ++n) {
-      if (n >= a.nv) break;
+    for (int i = 0; i < CE; ++i) {
+      if (i >= n) break;
 #pragma unroll
-      for (int c = 0; c < EPV / 4; ++c) hv.v[n][c] = hs[c * V + j + a.lr * n];
+      for (int nn = 0; nn < NVC; ++nn) {
+        if (nn >= a.nv) break;
+#pragma unroll
+        for (int c = 0; c < EPV / 4; ++c)
+          hv.v[i][nn][c] = S.d.hst[(er + i) * I4 + c * V + j + a.lr * nn];
+      }
     }
   }
 }
 
-// Down rows of one workgroup: its share [d0, d1) of the flattened (unit, row
-// of H) list is taken one unit segment at a time; a segment's rows are walked
-// in steps of kW * (64 / lr) rows, each wave taking 64 / lr rows per step with
-// lr lanes per row and nv vectors per lane (lane j of a row group holds
-// vectors j, j + lr, ...).
-struct DnMap {
-  int64_t lo, hi;    // rows of the current segment
-  int rpw;           // rows per wave per step
-  int grp, j;        // row group of this lane, lane within it
-  __device__ int64_t row(int step, int wave) const {
-    return lo + (int64_t)step * kW * rpw + wave * rpw + grp;
-  }
-  __device__ int steps() const { return (int)((hi - lo + kW * rpw - 1) / (kW * rpw)); }
-};
-
-// Always NVC loads (rows past the segment read its first row, vectors past nv
-// read vector j; neither is used), so that every step issues the same loads
-// and the waits for a step's data can be counted exactly.
-template <int WT, int NVC>
-__device__ __forceinline__ void dn_load(const DecArgs& a, const DecLds& S, const DnMap& m,
-                                        int u, int64_t row, DnBuf<NVC>& b) {
-  const int r = (int)((row < m.hi ? row : m.lo) - (int64_t)u * a.H);
-  const uint8_t* base = unit_base(a, S.p.unit_slot[u]);
-#pragma unroll
-  for (int n = 0; n < NVC; ++n) {
-    const int v = m.j + (n < a.nv ? a.lr * n : 0);
-    if (WT == 1) {
-      b.q[n] = ldg16(base + a.off[2] + ((int64_t)r * a.I + (int64_t)v * 8) * 2);
-    } else {
-      b.q[n] = ldg16(base + a.off[4] + (int64_t)r * (a.I / 2) + (int64_t)v * 16);
-      b.s[n] = (base + a.off[5])[(int64_t)r * (a.I / 32) + v];
-    }
-  }
-}
-
-// y results of a wave to memory (fp32 atomics; index -1: none)
-__device__ __forceinline__ void flush_y(const DecArgs& a, WaveOut& o) {
-  const int lane = threadIdx.x & 63;
-  for (int q = lane; q < o.n; q += 64) {
-    const int2 p = o.buf[q];
-    if (p.x >= 0) unsafeAtomicAdd(a.y + p.x, __int_as_float(p.y));
-  }
-  o.n = 0;
-}
-
-// row (of unit u) . h for the staged entries [c0, c1), each result times the
-// entry's gate weight listed for y[token][row].  A single entry's h values
-// come in registers when they fit (hv), else from LDS per row.  Rows past the
-// segment (unused weights) list index -1.  The list has room for the pass.
-template <int WT, int NVC>
-__device__ __forceinline__ void dn_compute(const DecArgs& a, const DecLds& S, const DnMap& m,
-                                           int u, int64_t row, int c0, int c1,
-                                           const DnBuf<NVC>& b, const HRegs<WT, NVC>& hv,
+// the lane's row of the cursor's step . h of each entry of the segment
+// (staged entries from er), each result times the entry's gate weight listed
+// for y[token][row]; rows past the segment list index -1
+template <int WT, int NVC, int CE>
+__device__ __forceinline__ void dn_compute(const DecArgs& a, const DecLds& S, const DnLane& L,
+                                           const DnCur<CE>& c, int wave, int er,
+                                           const DnBuf<NVC>& b, const HRegs<WT, NVC, CE>& hv,
                                            WaveOut& out) {
   constexpr int EPV = WT == 1 ? 8 : 32;
-  const bool valid = row < m.hi;
-  const int r = (int)(row - (int64_t)u * a.H);
+  const int row = dn_row(L, c, wave);
+  const bool valid = row < c.hi;
+  const int r = (valid ? row : c.lo) - c.v * a.H;
   const int V = a.I / EPV;
-  for (int en = c0; en < c1; ++en) {
-    float s = 0.f;
-    if (HRegs<WT, NVC>::kOn && c1 - c0 == 1) {
+  uint32_t sc[NVC];
 #pragma unroll
-      for (int n = 0; n < NVC; ++n) {
-        if (n >= a.nv) break;
-        s += wdot_h<WT>(b.q[n], b.s[n], hv.v[HRegs<WT, NVC>::kOn ? n : 0]);
+  for (int nn = 0; nn < NVC; ++nn)
+    sc[nn] = WT == 1 ? 0u : dn_scale(a, r, L.j + (nn < a.nv ? a.lr * nn : 0), b.s[nn]);
+#pragma unroll
+  for (int i = 0; i < CE; ++i) {
+    if (i >= c.n) break;
+    float s = 0.f;
+    if constexpr (HRegs<WT, NVC, CE>::kOn) {
+#pragma unroll
+      for (int nn = 0; nn < NVC; ++nn) {
+        if (nn >= a.nv) break;
+        s += wdot_h<WT>(b.q[nn], sc[nn], hv.v[i][nn]);
       }
     } else {
-      const float4* hs = S.hs + (en - c0) * (a.I / 4);
+      const float4* hs = S.d.hst + (er + i) * (a.I / 4);
 #pragma unroll
-      for (int n = 0; n < NVC; ++n) {
-        if (n >= a.nv) break;
+      for (int nn = 0; nn < NVC; ++nn) {
+        if (nn >= a.nv) break;
         float4 h4[EPV / 4];
 #pragma unroll
-        for (int c = 0; c < EPV / 4; ++c) h4[c] = hs[c * V + m.j + a.lr * n];
-        s += wdot_h<WT>(b.q[n], b.s[n], h4);
+        for (int q = 0; q < EPV / 4; ++q) h4[q] = hs[q * V + L.j + a.lr * nn];
+        s += wdot_h<WT>(b.q[nn], sc[nn], h4);
       }
     }
     s = group_sum(s, a.lr);
-    if (m.j == 0)
-      out.buf[out.n + m.grp] =
-          make_int2(valid ? S.p.ent_tok[en] * a.H + r : -1, __float_as_int(S.p.ent_gw[en] * s));
-    out.n += m.rpw;
+    if (L.j == 0)
+      out.buf[out.n + L.grp] = make_int2(valid ? c.tokH[i] + r : -1, __float_as_int(c.gw[i] * s));
+    out.n += L.rpw;
   }
 }
 
@@ -753,7 +897,7 @@ __device__ __forceinline__ void stage_h(const DecArgs& a, DecLds& S, __amdgpu_bu
   for (int q = threadIdx.x; q < n4; q += kT) {
     const int e = q / I4, c4 = q - e * I4;
     const int v = c4 / (EPV / 4), cc = c4 - v * (EPV / 4);
-    S.hs[e * I4 + cc * V + v] = coherent_load16(hr, (S.p.ent_pair[c0 + e] * a.I + c4 * 4) * 4);
+    S.d.hst[e * I4 + cc * V + v] = coherent_load16(hr, (S.p.ent_pair[c0 + e] * a.I + c4 * 4) * 4);
   }
 }
 
@@ -769,8 +913,9 @@ __global__ __launch_bounds__(kT) void decode_kernel(DecArgs a) {
   constexpr int RG = RGV / (2 * LXC) > 0 ? RGV / (2 * LXC) : 1;
   constexpr int DDV = WT == 1 ? 16 : (LXC >= 4 ? 4 : 8);  // down vectors in flight per lane
   constexpr int DD = NVC >= DDV ? 1 : DDV / NVC;
+  constexpr int CE = kMaxCE;               // entries per down virtual unit
   __shared__ DecLds S;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = uni((int)(threadIdx.x >> 6));
   const int bid = blockIdx.x, G = a.G;
   const bool route = a.NRW > 0;
   const bool timing = a.hdr[kHTiming] != 0;     // uniform: a scalar load
@@ -801,19 +946,27 @@ __global__ __launch_bounds__(kT) void decode_kernel(DecArgs a) {
     __syncthreads();
     stamp(timing, a, 6);
   }
-  build_units<M>(a, S, route);
+  build_units<M, CE>(a, S, route);
   stamp(timing, a, 1);
   const int n_routed = S.p.n_routed, n_units = S.p.n_units;
 
   // 3. routed gate/up rows
-  int64_t d0, d1;
-  split((int64_t)n_units * a.H, G, bid, d0, d1);
-  DnMap m;
-  m.rpw = 64 / a.lr;
-  m.grp = lane / a.lr;
-  m.j = lane - m.grp * a.lr;
-  m.lo = d0;
-  m.hi = d0 < d1 ? min(d1, (d0 / a.H + 1) * (int64_t)a.H) : d1;
+  DnLane L;
+  L.rpw = 64 / a.lr;
+  L.grp = lane / a.lr;
+  L.j = lane - L.grp * a.lr;
+  L.sh = 31 - __builtin_clz(kW * L.rpw);
+  int d0, d1;
+  {
+    int64_t lo, hi;
+    split((int64_t)S.p.n_vu * a.H, G, bid, lo, hi);
+    d0 = uni((int)lo);
+    d1 = uni((int)hi);
+  }
+  int p_steps = 0;
+  int p1 = d0 < d1 ? pass_end(a, S, d0, d1, L, &p_steps) : d0;
+  DnCur<CE> lc;                            // load cursor of the down rows
+  if (d0 < d1) dn_seg(a, S, L, d0, p1, lc);
   DnBuf<NVC> ring[DD];
   {
     int64_t lo, hi;
@@ -821,64 +974,65 @@ __global__ __launch_bounds__(kT) void decode_kernel(DecArgs a) {
     gateup_range<WT, LXC, RG, false>(a, S, lo, hi, [] {});
   }
 
-  // 4. count this workgroup done, issue the first down rows' loads, then the
-  // grid-wide wait for h
+  // 4. count this workgroup done, issue the loads of its first down steps,
+  // then the grid-wide wait for h
   stamp(timing, a, 7);
   signal_done(a.hdr + kHGateUp);
-  if (m.lo < d1) {
-    const int u = (int)(m.lo / a.H);
+  if (d0 < d1) {
 #pragma unroll
-    for (int d = 0; d < DD; ++d) dn_load<WT, NVC>(a, S, m, u, m.row(d, wave), ring[d]);
+    for (int d = 0; d < DD; ++d) {
+      dn_load<WT, NVC, CE>(a, L, lc, wave, ring[d]);
+      dn_next(a, S, L, p1, lc);
+    }
   }
   if (threadIdx.x == 0) wait_geq(a, a.hdr + kHGateUp, (unsigned)G);
   __syncthreads();
   stamp(timing, a, 2);
 
-  // 5. down rows, unit segment by segment; h of up to ce entries staged at a
-  // time (and no more than the per-wave y list holds over a segment); DD
-  // steps of weight loads in flight
+  // 5. down rows, pass by pass
   const __amdgpu_buffer_rsrc_t hr = __builtin_amdgcn_make_buffer_rsrc(
       a.h, 0, (a.T * a.k + a.T) * a.I * 4, 0x00020000);
-  WaveOut out;                             // y results, in the x stage
-  out.cap = kXStage16 * 2 / kW;
-  out.buf = reinterpret_cast<int2*>(S.xs) + wave * out.cap;
+  WaveOut out;                             // y results
+  out.cap = kYOut;
+  out.buf = S.d.yout + wave * kYOut;
   out.n = 0;
-  int ce = kHStage4 / (a.I / 4);
-  {
-    const int per_entry = (a.H / (kW * m.rpw) + 1 + DD) * m.rpw;  // list slots per entry
-    if (ce > out.cap / per_entry) ce = out.cap / per_entry;
-    if (ce < 1) ce = 1;
-  }
-  bool loaded = true;                      // ring holds the segment's first steps
-  while (m.lo < d1) {
-    const int u = (int)(m.lo / a.H);
-    const int e0 = S.p.unit_start[u], e1 = S.p.unit_start[u + 1];
-    const int ns = m.steps();
-    for (int c0 = e0; c0 < e1; c0 += ce) {
-      const int c1 = min(e1, c0 + ce);
-      __syncthreads();
-      stage_h<WT>(a, S, hr, c0, c1);
-      if (!loaded) {
-#pragma unroll
-        for (int d = 0; d < DD; ++d) dn_load<WT, NVC>(a, S, m, u, m.row(d, wave), ring[d]);
-      }
-      loaded = false;
-      __syncthreads();
-      stamp(timing, a, 11);
-      HRegs<WT, NVC> hv;
-      if (c1 - c0 == 1) h_regs<WT, NVC>(a, S.hs, m.j, hv);
-      for (int s0 = 0; s0 < ns; s0 += DD) {
-#pragma unroll
-        for (int d = 0; d < DD; ++d) {
-          dn_compute<WT, NVC>(a, S, m, u, m.row(s0 + d, wave), c0, c1, ring[d], hv, out);
-          dn_load<WT, NVC>(a, S, m, u, m.row(s0 + d + DD, wave), ring[d]);
-        }
-      }
-      flush_y(a, out);
+  bool first = true;                       // the ring holds the pass's first steps
+  for (int p0 = d0; p0 < d1; p0 = p1) {
+    if (!first) {
+      p1 = pass_end(a, S, p0, d1, L, &p_steps);
+      dn_seg(a, S, L, p0, p1, lc);
     }
+    const int vl = (p1 - 1) / a.H;
+    const int E0 = uni(S.p.vu_e0[p0 / a.H]), E1 = uni(S.p.vu_e0[vl]) + uni(S.p.vu_n[vl]);
+    __syncthreads();
+    stage_h<WT>(a, S, hr, E0, E1);
+    if (!first) {
+#pragma unroll
+      for (int d = 0; d < DD; ++d) {
+        dn_load<WT, NVC, CE>(a, L, lc, wave, ring[d]);
+        dn_next(a, S, L, p1, lc);
+      }
+    }
+    first = false;
+    __syncthreads();
+    stamp(timing, a, 11);
+    DnCur<CE> cc;                          // compute cursor
+    dn_seg(a, S, L, p0, p1, cc);
+    HRegs<WT, NVC, CE> hv;
+    for (int s0 = 0; s0 < p_steps; s0 += DD) {
+#pragma unroll
+      for (int d = 0; d < DD; ++d) {
+        if (s0 + d < p_steps) {
+          if (cc.s == 0) h_regs<WT, NVC, CE>(a, S, L.j, cc.e0 - E0, cc.n, hv);
+          dn_compute<WT, NVC, CE>(a, S, L, cc, wave, cc.e0 - E0, ring[d], hv, out);
+          dn_next(a, S, L, p1, cc);
+        }
+        dn_load<WT, NVC, CE>(a, L, lc, wave, ring[d]);
+        dn_next(a, S, L, p1, lc);
+      }
+    }
+    flush_y(a, out);
     stamp(timing, a, 12);
-    m.lo = m.hi;
-    m.hi = min(d1, m.lo + a.H);
   }
 
   // exit: the last workgroup out resets the counters for the next call

@@ -18,6 +18,7 @@ struct DecodeLaunch {
   unsigned* hdr;          // counter header (zero before first use)
   float* z;               // [T][E]
   float* h;               // [T*k + T][I]
+  unsigned long long* stamps;  // [kMaxWorkgroups][16] phase stamps (timing only)
   float* y;
   int64_t expert_bytes;
   int64_t off[6];
@@ -57,6 +58,9 @@ hipError_t launch_route_small(const void* x, const void* w_router, int router_f3
 hipError_t launch_route_large(const void* x, const void* w_router, int router_f32, int T,
                               int H, int E, int k, int renorm, float* logits, int32_t* ids,
                               float* w, hipStream_t st);
+
+// per-workgroup phase stamps at the end of the decode workspace
+constexpr size_t kDecodeStampBytes = 1024 * 16 * 8;
 
 // decode: router (optional) + experts + combine in one kernel, at most
 // decode_max_tokens(H) tokens per launch
