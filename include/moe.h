@@ -91,14 +91,17 @@ int moe_expert_layout(const moe_desc* desc, size_t offsets[6], size_t* bytes);
 
 /* Workspace bytes a call needs (0 if none).  mode: 0 = moe_route,
  * 1 = moe_decode / moe_route_decode, 2 = moe_prefill, for T tokens.  Returns
- * 0 and sets the error text for an invalid descriptor or T.  Route and decode
- * workspaces start with a header of counters (256 bytes for route, 1024 for
- * decode) that must be zero before a workspace's first use; every call leaves
- * it zero again.  A workspace must not be used by two calls that can run
- * concurrently.  Decode header word 128 is set to 1 if a wait inside the
- * kernel expired (only possible on an oversubscribed device); setting word
- * 160 to non-zero makes the kernel record phase timestamps (100 MHz clock,
- * uint64) from word 192 on. */
+ * 0 and sets the error text for an invalid descriptor or T.  A route
+ * workspace starts with a 256-byte counter header that must be zero before
+ * its first use; every call leaves it zero again.  A decode workspace must be
+ * zero as a whole before its first use (its 8 KB header holds counters, which
+ * every call leaves zero, and the generation of the last launch, against which
+ * the logits the kernel hands between workgroups are tagged).  A workspace
+ * must not be used by two calls that can run concurrently.  Decode header
+ * word 32 (uint32) is set to 1 if a wait inside the kernel expired (only
+ * possible on an oversubscribed device); setting word 64 to non-zero makes
+ * the kernel record phase timestamps (100 MHz clock, uint64) from word 1152
+ * on and per workgroup at the end of the workspace. */
 #define MOE_MODE_ROUTE 0
 #define MOE_MODE_DECODE 1
 #define MOE_MODE_PREFILL 2

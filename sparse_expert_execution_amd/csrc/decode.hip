@@ -55,7 +55,7 @@ hipError_t launch_decode(const DecodeLaunch& f, hipStream_t st) {
   a.expert_bytes = f.expert_bytes;
   for (int i = 0; i < 6; ++i) a.off[i] = f.off[i];
   a.T = f.T; a.H = f.H; a.I = f.I; a.E = f.E; a.k = f.k; a.renorm = f.renorm;
-  a.NRW = f.w_router ? (f.E + kW - 1) / kW : 0;
+  a.route = f.w_router ? 1 : 0;
   const int epv = elems_per_vector(f.wtype);
   a.lx = (f.H / epv + 63) / 64;
   if (!down_map(f.I / epv, &a.lr, &a.nv)) return hipErrorInvalidValue;

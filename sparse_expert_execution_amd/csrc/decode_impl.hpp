@@ -12,14 +12,14 @@
 // Decode is bound by reading the selected experts' weights once from HBM, so
 // the kernel is a persistent grid (every workgroup resident at once) that
 // keeps as many of those reads in flight as it can:
-//   1. router workgroups form z[t][e] = W_r[e] . x[t] (one wave per expert
-//      row) and count themselves done; every workgroup clears its slice of y
-//      and starts on its share of the shared expert's gate/up rows, which
-//      need no routing.
+//   1. every workgroup stages x into LDS, takes its share of the router dot
+//      products z[t][e] = W_r[e] . x[t] and counts itself done, clears its
+//      slice of y and starts on its share of the shared expert's gate/up
+//      rows, which need no routing.
 //   2. every workgroup waits for the router count, ranks the tokens itself
-//      (softmax + DPP arg-max top-k, the same result in every workgroup) and
-//      lists the distinct resident experts in first-appearance order with
-//      their (pair, token, weight) entries.
+//      (softmax + DPP arg-max top-k, one wave per token, the same result in
+//      every workgroup) and lists the distinct resident experts in
+//      first-appearance order with their (pair, token, weight) entries.
 //   3. gate/up: the rows of I of all selected experts are split evenly over
 //      the grid; a wave streams one gate row and one up row at a time (two in
 //      flight), dots them with each of the expert's tokens and writes
@@ -52,7 +52,6 @@ constexpr int kHStage4 = 1536;      // float4s of staged h (24 KB)
 constexpr int kYOut = 512;          // y results per wave list in the down phase
 constexpr int kDnH4 = kXStage16 + kHStage4 - kW * kYOut / 2;  // float4s of staged h (down)
 constexpr int kMaxCE = 2;           // entries per virtual unit of the down phase, at most
-constexpr int kRankMaxE = 256;      // the rank top-k handles E up to this
 constexpr unsigned kSpinLimit = 1u << 21;
 
 // a value the same in every lane of the wave, kept in a scalar register
@@ -61,8 +60,21 @@ __device__ __forceinline__ float uni(float v) {
   return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(v)));
 }
 
-// header words of the workspace: every counter on its own 128-byte line
-enum { kHRouted = 0, kHGateUp = 32, kHExit = 64, kHError = 128, kHTiming = 160, kHStamps = 192 };
+// Header words of the decode workspace (8 KB), every counter on its own
+// 128-byte line.  A grid-wide count is spread over kNCtr lines (workgroup b
+// counts on line b % kNCtr) so that the atomics of a full grid do not queue
+// on one address.
+constexpr int kLine = 32;           // words per 128-byte line
+constexpr int kNCtr = 16;
+enum {
+  kHGen = 0,                        // generation of the last finished launch
+  kHError = 32,                     // 1: a wait expired
+  kHTiming = 64,                    // non-zero: record phase stamps
+  kHExitTop = 96,                   // exit groups complete
+  kHGateUp = 128,                   // kNCtr lines: workgroups done with gate/up
+  kHExit = kHGateUp + kNCtr * kLine,  // kNCtr lines: workgroups exited
+  kHStamps = kHExit + kNCtr * kLine   // uint64 phase stamps
+};
 
 struct DecArgs {
   const uint16_t* x;       // [T][H] bf16
@@ -74,7 +86,7 @@ struct DecArgs {
   const uint8_t* pool;
   const uint8_t* shared;
   unsigned* hdr;
-  float* z;                // [T][E]
+  uint64_t* z;             // [T][E] logits tagged with the launch's generation
   float* h;                // [T*k + T][I]
   unsigned long long* st;  // [workgroup][16] phase stamps
   float* y;                // [T][H]
@@ -82,7 +94,7 @@ struct DecArgs {
   int64_t off[6];
   int T, H, I, E, k, renorm;
   int G;                   // workgroups in the grid, all resident at once
-  int NRW;                 // router workgroups (0: ids and w are inputs)
+  int route;               // 0: ids and w are inputs
   int lx;                  // 16-byte vectors per lane per gate/up row
   int lr;                  // lanes per down row (a power of two <= 64)
   int nv;                  // 16-byte vectors per lane per down row
@@ -90,8 +102,9 @@ struct DecArgs {
 
 // phase timing (header word kHTiming non-zero): 100 MHz wall clock of
 // workgroup 0 at start (0), expert list ready (1), past the grid-wide wait
-// (2), exit (3), router rows done (5), past the router wait (6), gate/up done
-// (7), h staged (11), first down segment done (12), and of the last
+// (2), exit (3), router dot products done (5), first token's logits in (6),
+// gate/up done (7), gate/up counted (8), top-k done (9), h staged (11), a
+// down pass done (12), and of the last
 // workgroup's exit (4), as uint64 from kHStamps; the same stamps of the
 // grid's last workgroup 16 slots further; every workgroup's stamps also go to
 // its own 16 slots of a.st
@@ -112,9 +125,6 @@ __device__ __forceinline__ void stamp(bool on, const DecArgs& a, int i) {
 __device__ __forceinline__ void coherent_store(float* p, float v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ float coherent_load(const float* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
 __device__ __forceinline__ void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
@@ -125,31 +135,84 @@ __device__ __forceinline__ float4 coherent_load16(__amdgpu_buffer_rsrc_t r, int 
                      __uint_as_float(v.w));
 }
 
-// thread 0 only: wait until *p >= target.  Polls back off (64 to 512
-// cycles) so that the waiting workgroups do not flood the line the counter
-// sits on.
-__device__ void wait_geq(const DecArgs& a, unsigned* p, unsigned target) {
+
+// every wave waits for its coherent stores, then thread 0 counts the
+// workgroup on its line of a spread count
+__device__ void signal_done(unsigned* count) {
+  wait_stores();
+  __syncthreads();
+  if (threadIdx.x == 0)
+    __hip_atomic_fetch_add(count + (blockIdx.x % kNCtr) * kLine, 1u, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// wave 0 only: wait until the lines of a spread count add up to target
+__device__ void wait_count(const DecArgs& a, unsigned* count, unsigned target) {
+  const int lane = threadIdx.x & 63;
   unsigned spins = 0;
   int nap = 1;
-  while (__hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+  for (;;) {
+    const unsigned v = lane < kNCtr ? __hip_atomic_load(count + lane * kLine, __ATOMIC_RELAXED,
+                                                        __HIP_MEMORY_SCOPE_AGENT)
+                                    : 0u;
+    if (__builtin_amdgcn_readfirstlane((unsigned)wave_sum_dpp((float)v)) >= target) break;
     if (nap == 1) __builtin_amdgcn_s_sleep(1);
     else if (nap == 2) __builtin_amdgcn_s_sleep(2);
     else if (nap == 4) __builtin_amdgcn_s_sleep(4);
     else __builtin_amdgcn_s_sleep(8);
     if (nap < 8) nap <<= 1;
     if (++spins > kSpinLimit) {
-      __hip_atomic_store(a.hdr + kHError, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (lane == 0)
+        __hip_atomic_store(a.hdr + kHError, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       break;
     }
   }
 }
 
-// every wave waits for its coherent stores, then thread 0 counts the
-// workgroup
-__device__ void signal_done(unsigned* p) {
-  wait_stores();
-  __syncthreads();
-  if (threadIdx.x == 0) __hip_atomic_fetch_add(p, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// Logits handed from the router workgroups to every workgroup: each z is
+// stored with the launch's generation in its upper half, and a reader polls
+// its entries until all carry this launch's generation (a launch's
+// generation is one more than the header's, which the last workgroup out
+// advances).  No count and no wait for store completion are needed.
+__device__ __forceinline__ void z_store(uint64_t* p, float z, unsigned gen) {
+  __hip_atomic_store(p, ((uint64_t)gen << 32) | __float_as_uint(z), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// one wave: logits of expert lane + 64 i of row zt into v (-inf past E)
+template <int M>
+__device__ void z_load(const DecArgs& a, const uint64_t* zt, unsigned gen, float v[M]) {
+  const int lane = threadIdx.x & 63;
+  bool have[M];
+#pragma unroll
+  for (int i = 0; i < M; ++i) {
+    have[i] = lane + 64 * i >= a.E;
+    v[i] = -INFINITY;
+  }
+  unsigned spins = 0;
+  for (;;) {
+    bool all = true;
+#pragma unroll
+    for (int i = 0; i < M; ++i) {
+      if (!have[i]) {
+        const uint64_t q =
+            __hip_atomic_load(zt + lane + 64 * i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if ((unsigned)(q >> 32) == gen) {
+          v[i] = __uint_as_float((unsigned)q);
+          have[i] = true;
+        } else {
+          all = false;
+        }
+      }
+    }
+    if (__all(all)) break;
+    __builtin_amdgcn_s_sleep(2);
+    if (++spins > kSpinLimit) {
+      if (lane == 0)
+        __hip_atomic_store(a.hdr + kHError, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      break;
+    }
+  }
 }
 
 // [lo, hi) of an even split of n items over G parts
@@ -197,10 +260,7 @@ struct DecLds {
       // 8c..8c+7 of weight vector v (CPV = elements per vector / 8, NV
       // vectors per row), so the lanes of a wave read consecutive words
       uint4 xs[kXStage16];
-      union {
-        float zs[4 * kHStage4];    // logits of every token, rows padded to float4s
-        float4 hs[kHStage4];       // per-wave lists of gate/up h results
-      };
+      float4 hs[kHStage4];         // per-wave lists of gate/up h results
     } g;
     struct {                       // down
       int2 yout[kW * kYOut];       // per-wave lists of y results
@@ -215,54 +275,99 @@ struct DecLds {
 // ---------------------------------------------------------------------------
 // routing: z rows (router workgroups) and the per-workgroup expert list
 // ---------------------------------------------------------------------------
-__device__ void router_rows(const DecArgs& a) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int T = a.T, H = a.H, E = a.E;
-  const int e = blockIdx.x * kW + wave;
-  if (e >= E) return;
-  const int epv = a.router_f32 ? 4 : 8;
-  const int nvr = H / epv;
-  const uint8_t* row = static_cast<const uint8_t*>(a.wr) + (int64_t)e * H * (a.router_f32 ? 4 : 2);
-  for (int t0 = 0; t0 < T; t0 += 4) {
-    float acc[4] = {0.f, 0.f, 0.f, 0.f};
-    for (int i0 = 0; i0 * 64 < nvr; i0 += 4) {
-      uint4 wv[4];
+// Router dot products z[t][e] = W_r[e] . x[t] over the whole grid: item i is
+// (expert i % E, tokens kRTG * (i / E) ...), taken by workgroup i % G, wave
+// (i / G) % kW, so every workgroup has a share.  A row is read in rounds of
+// kRL 16-byte vectors per lane; x comes from the LDS stage.
+constexpr int kRTG = 4;    // tokens per router item
+constexpr int kRL = 8;     // row vectors per lane per round
+
+struct RouterRow {
+  uint4 v[kRL];
+};
+
+__device__ __forceinline__ int router_items(const DecArgs& a) {
+  return a.E * ((a.T + kRTG - 1) / kRTG);
+}
+__device__ __forceinline__ int router_rounds(const DecArgs& a) {
+  const int nvr = a.H / (a.router_f32 ? 4 : 8);
+  return (nvr + 64 * kRL - 1) / (64 * kRL);
+}
+
+__device__ __forceinline__ void router_load(const DecArgs& a, int item, int c, RouterRow& w) {
+  const int lane = threadIdx.x & 63;
+  const int e = item % a.E;
+  const int nvr = a.H / (a.router_f32 ? 4 : 8);
+  const uint8_t* row =
+      static_cast<const uint8_t*>(a.wr) + (int64_t)e * a.H * (a.router_f32 ? 4 : 2);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int v = lane + 64 * (i0 + i);
-        wv[i] = v < nvr ? ldg16(row + (int64_t)v * 16) : make_uint4(0, 0, 0, 0);
+  for (int r = 0; r < kRL; ++r) {
+    const int v = lane + 64 * (c * kRL + r);
+    w.v[r] = v < nvr ? ldg16(row + (int64_t)v * 16) : make_uint4(0, 0, 0, 0);
+  }
+}
+
+// 8 bf16 values of token t, elements 8u .. 8u + 7, from the x stage
+template <int WT>
+__device__ __forceinline__ uint4 xs8(const DecArgs& a, const DecLds& S, int t, int u) {
+  if (WT == 1) return S.g.xs[t * (a.H / 8) + u];
+  return S.g.xs[(t * 4 + (u & 3)) * (a.H / 32) + (u >> 2)];
+}
+
+template <int WT>
+__device__ __forceinline__ void router_dot(const DecArgs& a, const DecLds& S, int item, int c,
+                                           const RouterRow& w, float acc[kRTG]) {
+  const int lane = threadIdx.x & 63;
+  const int t0 = (item / a.E) * kRTG;
+  const int nvr = a.H / (a.router_f32 ? 4 : 8);
+#pragma unroll
+  for (int r = 0; r < kRL; ++r) {
+    const int v = lane + 64 * (c * kRL + r);
+    if (v >= nvr) continue;
+#pragma unroll
+    for (int tt = 0; tt < kRTG; ++tt) {
+      if (t0 + tt >= a.T) break;
+      float s = acc[tt];
+      if (a.router_f32) {
+        const uint4 xx = xs8<WT>(a, S, t0 + tt, v >> 1);
+        const uint32_t x0 = (v & 1) ? xx.z : xx.x, x1 = (v & 1) ? xx.w : xx.y;
+        s = fmaf(__uint_as_float(w.v[r].x), bf16_lo(x0), s);
+        s = fmaf(__uint_as_float(w.v[r].y), bf16_hi(x0), s);
+        s = fmaf(__uint_as_float(w.v[r].z), bf16_lo(x1), s);
+        s = fmaf(__uint_as_float(w.v[r].w), bf16_hi(x1), s);
+      } else {
+        const uint4 xx = xs8<WT>(a, S, t0 + tt, v);
+        s = dot2_bf16(w.v[r].x, xx.x, s);
+        s = dot2_bf16(w.v[r].y, xx.y, s);
+        s = dot2_bf16(w.v[r].z, xx.z, s);
+        s = dot2_bf16(w.v[r].w, xx.w, s);
       }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int v = lane + 64 * (i0 + i);
-        if (v >= nvr) continue;
-#pragma unroll
-        for (int tt = 0; tt < 4; ++tt) {
-          if (t0 + tt >= T) break;
-          const uint16_t* xt = a.x + (int64_t)(t0 + tt) * H;
-          float s = acc[tt];
-          if (a.router_f32) {
-            const uint2 xx = *reinterpret_cast<const uint2*>(xt + v * 4);
-            s = fmaf(__uint_as_float(wv[i].x), bf16_lo(xx.x), s);
-            s = fmaf(__uint_as_float(wv[i].y), bf16_hi(xx.x), s);
-            s = fmaf(__uint_as_float(wv[i].z), bf16_lo(xx.y), s);
-            s = fmaf(__uint_as_float(wv[i].w), bf16_hi(xx.y), s);
-          } else {
-            const uint4 xx = ldg16(xt + v * 8);
-            s = dot2_bf16(wv[i].x, xx.x, s);
-            s = dot2_bf16(wv[i].y, xx.y, s);
-            s = dot2_bf16(wv[i].z, xx.z, s);
-            s = dot2_bf16(wv[i].w, xx.w, s);
-          }
-          acc[tt] = s;
-        }
-      }
+      acc[tt] = s;
     }
+  }
+}
+
+// this wave's router items from `item` on (its first round already loaded
+// into w), each z written with an agent-coherent store
+template <int WT>
+__device__ void router_items_run(const DecArgs& a, const DecLds& S, int item, RouterRow& w,
+                                 unsigned gen) {
+  const int lane = threadIdx.x & 63;
+  const int n_items = router_items(a), nr = router_rounds(a);
+  bool loaded = true;
+  for (; item < n_items; item += a.G * kW) {
+    float acc[kRTG] = {0.f, 0.f, 0.f, 0.f};
+    for (int c = 0; c < nr; ++c) {
+      if (!loaded) router_load(a, item, c, w);
+      loaded = false;
+      router_dot<WT>(a, S, item, c, w, acc);
+    }
+    const int e = item % a.E, t0 = (item / a.E) * kRTG;
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
-      if (t0 + tt >= T) break;
-      const float s = wave_sum_dpp(acc[tt]);
-      if (lane == 0) coherent_store(a.z + (int64_t)(t0 + tt) * E + e, s);
+    for (int tt = 0; tt < kRTG; ++tt) {
+      if (t0 + tt >= a.T) break;
+      const float z = wave_sum_dpp(acc[tt]);
+      if (lane == 0) z_store(a.z + (int64_t)(t0 + tt) * a.E + e, z, gen);
     }
   }
 }
@@ -285,22 +390,44 @@ __device__ __forceinline__ float group_sum(float v, int lr) {
   return v;
 }
 
-// Top-k of every token for E <= kRankMaxE: the logits go to LDS; an expert's
-// rank is the number of experts ahead of it (larger logit, or equal logit and
-// lower id), so the k experts of rank < k land directly in descending order.
-// Weights are the softmax probabilities max-subtracted in fp32 (renormalised
-// over the k when asked).
-__device__ void rank_topk(const DecArgs& a, DecLds& S) {
+// Expert list of this launch, built the same way in every workgroup: the
+// distinct resident experts in order of first appearance over the (token,
+// rank) pairs, each with its pairs in order, then the shared expert.
+// Top-k of every token when T * E <= kRankItems, by the whole workgroup: the
+// logits go to LDS (polled until they carry this launch's generation); an
+// expert's rank is the number of experts ahead of it (larger logit, or equal
+// logit and lower id), so the k experts of rank < k land directly in
+// descending order.  Leaves ids, each selected logit (zsel) and each token's
+// softmax max and 1 / sum (mx, inv; max-subtracted, fp32).
+constexpr int kRankItems = 256;
+
+__device__ void rank_topk(const DecArgs& a, DecLds& S, unsigned gen) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int T = a.T, E = a.E, k = a.k, n = T * E;
   const int E4 = (E + 3) & ~3;             // rows padded to whole float4s with -inf
+  float* zs = reinterpret_cast<float*>(S.g.hs);
   for (int i = threadIdx.x; i < T * E4; i += kT) {
     const int t = i / E4, e = i - t * E4;
-    S.g.zs[i] = e < E ? coherent_load(a.z + (int64_t)t * E + e) : -INFINITY;
+    float z = -INFINITY;
+    if (e < E) {
+      const uint64_t* p = a.z + (int64_t)t * E + e;
+      unsigned spins = 0;
+      uint64_t q = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      while ((unsigned)(q >> 32) != gen) {
+        __builtin_amdgcn_s_sleep(2);
+        if (++spins > kSpinLimit) {
+          __hip_atomic_store(a.hdr + kHError, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          break;
+        }
+        q = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      z = __uint_as_float((unsigned)q);
+    }
+    zs[i] = z;
   }
   __syncthreads();
   for (int t = wave; t < T; t += kW) {
-    const float* zt = S.g.zs + t * E4;
+    const float* zt = zs + t * E4;
     float m = -INFINITY;
     for (int e = lane; e < E; e += 64) m = fmaxf(m, zt[e]);
     m = wave_max_dpp(m);
@@ -318,8 +445,8 @@ __device__ void rank_topk(const DecArgs& a, DecLds& S) {
   for (int i = threadIdx.x; i < n * sp; i += kT) {
     const int item = i / sp, part = i - item * sp;
     const int t = item / E, e = item - t * E;
-    const float4* zt4 = reinterpret_cast<const float4*>(S.g.zs + t * E4);
-    const float my = S.g.zs[t * E4 + e];
+    const float4* zt4 = reinterpret_cast<const float4*>(zs + t * E4);
+    const float my = zs[t * E4 + e];
     int rank = 0;
 #pragma unroll 4
     for (int c = part; c < E4 / 4; c += sp) {
@@ -337,40 +464,157 @@ __device__ void rank_topk(const DecArgs& a, DecLds& S) {
     }
   }
   __syncthreads();
-  for (int p = threadIdx.x; p < T * k; p += kT) {
-    const int t = p / k;
-    S.p.w[p] = expf(S.p.zsel[p] - S.p.mx[t]) * S.p.inv[t];
+}
+
+// inclusive prefix sum over the lanes of a wave
+__device__ __forceinline__ int wave_scan(int v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int o = __shfl_up(v, d);
+    if (lane >= d) v += o;
   }
-  __syncthreads();
-  if (a.renorm) {
-    for (int t = threadIdx.x; t < T; t += kT) {
-      float s = 0.f;
-      for (int j = 0; j < k; ++j) s += S.p.w[t * k + j];
-      for (int j = 0; j < k; ++j) S.p.w[t * k + j] /= s;
+  return v;
+}
+
+// The expert list by one wave when T * k + (shared expert) <= 64 (one pair,
+// and at most one unit, per lane), with
+// ballots and wave-ordered LDS accesses instead of workgroup barriers: units
+// in first-appearance order of their expert over the pairs, a unit's entries
+// in any order (each entry's result is independent of the others), then the
+// shared expert's T entries and the virtual units of the down phase.  from_zsel:
+// the gate weights come from the selected logits and the softmax statistics
+// (renormalised here when asked), else they are in L.w.
+template <int CE>
+__device__ void build_units_wave(const DecArgs& a, DecLds& S, bool route, bool from_zsel) {
+  PlanLds& L = S.p;
+  const int lane = threadIdx.x & 63;
+  const int T = a.T, k = a.k, E = a.E, P = T * k;
+  const int p = lane;
+  int e = -1;
+  float wp = 0.f;
+  if (p < P) {
+    e = L.ids[p];
+    if (from_zsel) {
+      const int t = p / k;
+      wp = expf(L.zsel[p] - L.mx[t]) * L.inv[t];
+    } else {
+      wp = L.w[p];
     }
-    __syncthreads();
+  }
+  if (from_zsel && a.renorm) {
+    if (p < P) L.w[p] = wp;
+    float sum = 0.f;
+    if (p < P) {
+      const int t0 = (p / k) * k;
+      for (int j = 0; j < k; ++j) sum += L.w[t0 + j];
+      wp /= sum;
+    }
+  }
+  if (route && blockIdx.x == 0 && p < P) {
+    a.ids[p] = e;
+    a.w[p] = wp;
+  }
+  int slot = -1;
+  if (p < P && e >= 0 && e < E) slot = a.slot_of ? a.slot_of[e] : e;
+  const bool ok = slot >= 0;
+  if (ok) L.first[e] = 0x7fffffff;
+  if (ok) atomicMin(&L.first[e], p);
+  const bool isfirst = ok && L.first[e] == p;
+  const uint64_t fm = __ballot(isfirst);
+  const int n_routed = __popcll(fm);
+  if (isfirst) {
+    const int u = __popcll(fm & ((1ull << lane) - 1ull));
+    L.unit_expert[u] = e;
+    L.unit_slot[u] = slot;
+    L.first[e] = u;                        // from here on: the expert's unit
+  }
+  if (lane <= n_routed) L.cnt[lane] = 0;
+  const int u = ok ? L.first[e] : 0;
+  int li = 0;
+  if (ok) li = atomicAdd(&L.cnt[u], 1);
+  const bool sh = a.shared != nullptr;
+  const int n_units = n_routed + (sh ? 1 : 0);
+  const int c = lane < n_routed ? L.cnt[lane] : (sh && lane == n_routed ? T : 0);
+  const int incl = wave_scan(c);
+  if (lane < n_units) L.unit_start[lane] = incl - c;
+  if (lane == 0) L.unit_start[n_units] = __builtin_amdgcn_readlane(incl, 63);
+  if (sh && lane == n_routed) L.unit_slot[lane] = -1;
+  const int start = incl - c;
+  const int ustart = __shfl(start, u);     // with every lane active
+  if (ok) {
+    const int pos = ustart + li;
+    L.ent_pair[pos] = p;
+    L.ent_tok[pos] = p / k;
+    L.ent_gw[pos] = wp;
+  }
+  if (sh) {
+    const int base = __shfl(start, n_routed);
+    if (lane < T) {
+      L.ent_pair[base + lane] = P + lane;
+      L.ent_tok[base + lane] = lane;
+      L.ent_gw[base + lane] = 1.f;
+    }
+  }
+  // virtual units: each unit's entries in chunks of CE
+  const int nv = lane < n_units ? (c + CE - 1) / CE : 0;
+  const int vincl = wave_scan(nv);
+  for (int j = 0; j < nv; ++j) {
+    const int q = vincl - nv + j;
+    L.vu_unit[q] = lane;
+    L.vu_e0[q] = start + j * CE;
+    L.vu_n[q] = c - j * CE < CE ? c - j * CE : CE;
+  }
+  if (lane == 63) L.n_vu = vincl;
+  if (lane == 0) {
+    L.n_routed = n_routed;
+    L.n_units = n_units;
   }
 }
 
 // Expert list of this launch, built the same way in every workgroup: the
 // distinct resident experts in order of first appearance over the (token,
-// rank) pairs, each with its pairs in order, then the shared expert.
+// rank) pairs, each with its pairs, then the shared expert.
 template <int M, int CE>
-__device__ void build_units(const DecArgs& a, DecLds& S, bool route) {
+__device__ void build_units(const DecArgs& a, DecLds& S, bool route, bool timing, unsigned gen) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int T = a.T, k = a.k, E = a.E, P = T * k;
   PlanLds& L = S.p;
-  if (route) {
-    if (E <= kRankMaxE) {
-      rank_topk(a, S);
-    } else {
-      for (int t = wave; t < T; t += kW)
-        topk_one_token<M, true>(a.z + (int64_t)t * E, E, k, a.renorm, &L.ids[t * k], &L.w[t * k]);
+  const bool from_zsel = route && T * E <= kRankItems;
+  if (from_zsel) {
+    rank_topk(a, S, gen);
+  } else if (route) {
+    for (int t = wave; t < T; t += kW) {
+      float v[M];
+      z_load<M>(a, a.z + (int64_t)t * E, gen, v);
+      stamp(timing, a, 6);
+      topk_select<M>(v, E, k, a.renorm, &L.ids[t * k], &L.w[t * k]);
     }
+    __syncthreads();
   } else {
     for (int p = threadIdx.x; p < P; p += kT) {
       L.ids[p] = a.ids[p];
       L.w[p] = a.w[p];
+    }
+    __syncthreads();
+  }
+  stamp(timing, a, 9);
+  if (P + (a.shared ? 1 : 0) <= 64) {
+    if (wave == 0) build_units_wave<CE>(a, S, route, from_zsel);
+    __syncthreads();
+    return;
+  }
+  if (from_zsel) {
+    for (int p = threadIdx.x; p < P; p += kT)
+      L.w[p] = expf(L.zsel[p] - L.mx[p / k]) * L.inv[p / k];
+    __syncthreads();
+    if (a.renorm) {
+      for (int t = threadIdx.x; t < T; t += kT) {
+        float s = 0.f;
+        for (int j = 0; j < k; ++j) s += L.w[t * k + j];
+        for (int j = 0; j < k; ++j) L.w[t * k + j] /= s;
+      }
+      __syncthreads();
     }
   }
   for (int e = threadIdx.x; e < E; e += kT) L.first[e] = 0x7fffffff;
@@ -554,12 +798,13 @@ __device__ __forceinline__ float gu_dot(const DecArgs& a, const DecLds& S, const
   return gsum / (1.0f + expf(-gsum)) * usum;
 }
 
-// h results of a wave to memory (coherent stores)
+// h results of a wave to memory (coherent stores; an index past h is dropped)
 __device__ __forceinline__ void flush_h(const DecArgs& a, WaveOut& o) {
   const int lane = threadIdx.x & 63;
+  const int n = (a.T * a.k + a.T) * a.I;
   for (int q = lane; q < o.n; q += 64) {
     const int2 p = o.buf[q];
-    coherent_store(a.h + p.x, __int_as_float(p.y));
+    if ((unsigned)p.x < (unsigned)n) coherent_store(a.h + p.x, __int_as_float(p.y));
   }
   o.n = 0;
 }
@@ -765,12 +1010,14 @@ __device__ __forceinline__ uint32_t dn_scale(const DecArgs& a, int r, int v, uin
   return (word >> (((r * (a.I / 32) + v) & 3) * 8)) & 0xffu;
 }
 
-// y results of a wave to memory (fp32 atomics; index -1: none)
+// y results of a wave to memory (fp32 atomics; index -1: none; an index past
+// y is dropped rather than written)
 __device__ __forceinline__ void flush_y(const DecArgs& a, WaveOut& o) {
   const int lane = threadIdx.x & 63;
+  const int n = a.T * a.H;
   for (int q = lane; q < o.n; q += 64) {
     const int2 p = o.buf[q];
-    if (p.x >= 0) unsafeAtomicAdd(a.y + p.x, __int_as_float(p.y));
+    if (p.x >= 0 && p.x < n) unsafeAtomicAdd(a.y + p.x, __int_as_float(p.y));
   }
   o.n = 0;
 }
@@ -904,7 +1151,7 @@ __device__ __forceinline__ void stage_h(const DecArgs& a, DecLds& S, __amdgpu_bu
 // ---------------------------------------------------------------------------
 // the kernel.  WT: 1 BF16, 2 MXFP4.  LXC, NVC: register capacity (vectors per
 // lane) of a gate/up row and of a down row.  M: logits per lane in the wave
-// top-k used for E > kRankMaxE (E <= 64 M).  RG gate/up rows and DD steps of
+// top-k (E <= 64 M).  RG gate/up rows and DD steps of
 // down rows are loaded ahead.
 // ---------------------------------------------------------------------------
 template <int WT, int LXC, int NVC, int M>
@@ -917,23 +1164,29 @@ __global__ __launch_bounds__(kT) void decode_kernel(DecArgs a) {
   __shared__ DecLds S;
   const int lane = threadIdx.x & 63, wave = uni((int)(threadIdx.x >> 6));
   const int bid = blockIdx.x, G = a.G;
-  const bool route = a.NRW > 0;
+  const bool route = a.route != 0;
   const bool timing = a.hdr[kHTiming] != 0;     // uniform: a scalar load
+  const unsigned gen =
+      __hip_atomic_load(a.hdr + kHGen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
   stamp(timing, a, 0);
 
-  // 1. router rows; x into LDS; clear y; the shared expert's gate/up rows
-  if (bid < a.NRW) {
-    router_rows(a);
-    stamp(timing, a, 5);
-    signal_done(a.hdr + kHRouted);
-  }
+  // 1. router dot products (every workgroup), with x staged into LDS while
+  // the first row loads are in flight; clear y; the shared expert's gate/up
+  // rows
+  RouterRow rw;
+  const int item0 = bid + G * wave;
+  if (route && item0 < router_items(a)) router_load(a, item0, 0, rw);
   stage_x<WT>(a, S);
+  __syncthreads();
+  if (route) {
+    router_items_run<WT>(a, S, item0, rw, uni((int)gen));
+    stamp(timing, a, 5);
+  }
   {
     int64_t lo, hi;
     split((int64_t)a.T * a.H, G, bid, lo, hi);
     for (int64_t i = lo + threadIdx.x; i < hi; i += kT) coherent_store(a.y + i, 0.f);
   }
-  __syncthreads();
   if (a.shared) {
     int64_t lo, hi;
     split(a.I, G, bid, lo, hi);
@@ -941,12 +1194,7 @@ __global__ __launch_bounds__(kT) void decode_kernel(DecArgs a) {
   }
 
   // 2. the expert list
-  if (route) {
-    if (threadIdx.x == 0) wait_geq(a, a.hdr + kHRouted, (unsigned)a.NRW);
-    __syncthreads();
-    stamp(timing, a, 6);
-  }
-  build_units<M, CE>(a, S, route);
+  build_units<M, CE>(a, S, route, timing, gen);
   stamp(timing, a, 1);
   const int n_routed = S.p.n_routed, n_units = S.p.n_units;
 
@@ -978,6 +1226,7 @@ __global__ __launch_bounds__(kT) void decode_kernel(DecArgs a) {
   // then the grid-wide wait for h
   stamp(timing, a, 7);
   signal_done(a.hdr + kHGateUp);
+  stamp(timing, a, 8);
   if (d0 < d1) {
 #pragma unroll
     for (int d = 0; d < DD; ++d) {
@@ -985,7 +1234,7 @@ __global__ __launch_bounds__(kT) void decode_kernel(DecArgs a) {
       dn_next(a, S, L, p1, lc);
     }
   }
-  if (threadIdx.x == 0) wait_geq(a, a.hdr + kHGateUp, (unsigned)G);
+  if (wave == 0) wait_count(a, a.hdr + kHGateUp, (unsigned)G);
   __syncthreads();
   stamp(timing, a, 2);
 
@@ -1035,16 +1284,27 @@ __global__ __launch_bounds__(kT) void decode_kernel(DecArgs a) {
     stamp(timing, a, 12);
   }
 
-  // exit: the last workgroup out resets the counters for the next call
+  // exit: counted per group of workgroups (b % kNCtr), then per group; the
+  // last workgroup out clears the counts and advances the generation
   stamp(timing, a, 3);
   __syncthreads();
   if (threadIdx.x == 0) {
-    const unsigned old =
-        __hip_atomic_fetch_add(a.hdr + kHExit, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (old == (unsigned)G - 1) {
-      __hip_atomic_store(a.hdr + kHRouted, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(a.hdr + kHGateUp, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(a.hdr + kHExit, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int grp = bid % kNCtr;
+    const unsigned gsize = (unsigned)((G - grp + kNCtr - 1) / kNCtr);
+    const unsigned ngrp = (unsigned)(G < kNCtr ? G : kNCtr);
+    const unsigned old = __hip_atomic_fetch_add(a.hdr + kHExit + grp * kLine, 1u,
+                                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (old == gsize - 1 &&
+        __hip_atomic_fetch_add(a.hdr + kHExitTop, 1u, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT) == ngrp - 1) {
+      for (int j = 0; j < kNCtr; ++j) {
+        __hip_atomic_store(a.hdr + kHGateUp + j * kLine, 0u, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(a.hdr + kHExit + j * kLine, 0u, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+      }
+      __hip_atomic_store(a.hdr + kHExitTop, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(a.hdr + kHGen, gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       if (a.hdr[kHTiming])
         reinterpret_cast<unsigned long long*>(a.hdr + kHStamps)[4] = wall_clock64();
     }

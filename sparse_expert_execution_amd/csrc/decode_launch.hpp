@@ -40,7 +40,6 @@ hipError_t launch_t(DecArgs& a, hipStream_t st) {
   const int64_t units = (int64_t)(a.T * a.k < a.E ? a.T * a.k : a.E) + (a.shared ? 1 : 0);
   const int64_t useful = (units * a.I + 1) / 2;
   int G = (int)(useful < cap ? useful : cap);
-  if (G < a.NRW) G = a.NRW;
   if (G > cus * occ || G > 1024 || G < 1) return hipErrorInvalidConfiguration;
   a.G = G;
   hipLaunchKernelGGL((decode_kernel<WT, LXC, NVC, M>), dim3(G), dim3(kT), 0, st, a);

@@ -204,92 +204,74 @@ __device__ __forceinline__ float wave_max_dpp(float v) {
   return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
 }
 
-// Order-preserving key of a (value, expert id) pair: larger value first,
-// lower id first among equal values.  The wave maximum of the keys is the
-// arg-max with the lower-id tie-break.
-__device__ __forceinline__ uint64_t topk_key(float v, int id) {
-  uint32_t b = __float_as_uint(v);
-  b = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
-  return ((uint64_t)b << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)id);
-}
-__device__ __forceinline__ int topk_key_id(uint64_t k) {
-  return (int)(0xFFFFFFFFu - (uint32_t)(k & 0xFFFFFFFFu));
-}
-
-template <int CTRL>
-__device__ __forceinline__ uint64_t dpp_max_u64(uint64_t v) {
-  const uint32_t lo = dpp_u<CTRL>((uint32_t)v);
-  const uint32_t hi = dpp_u<CTRL>((uint32_t)(v >> 32));
-  const uint64_t o = ((uint64_t)hi << 32) | lo;
-  return o > v ? o : v;
+__device__ __forceinline__ uint32_t wave_max_u32_dpp(uint32_t v) {
+  v = max(v, dpp_u<kDppXor1>(v));
+  v = max(v, dpp_u<kDppXor2>(v));
+  v = max(v, dpp_u<kDppHalfMirror>(v));
+  v = max(v, dpp_u<kDppMirror>(v));
+  const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)v, 0);
+  const uint32_t r1 = (uint32_t)__builtin_amdgcn_readlane((int)v, 16);
+  const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)v, 32);
+  const uint32_t r3 = (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
+  return max(max(r0, r1), max(r2, r3));
 }
 
-__device__ __forceinline__ uint64_t wave_max_u64_dpp(uint64_t v) {
-  v = dpp_max_u64<kDppXor1>(v);
-  v = dpp_max_u64<kDppXor2>(v);
-  v = dpp_max_u64<kDppHalfMirror>(v);
-  v = dpp_max_u64<kDppMirror>(v);
-  uint64_t best = 0;
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, 16 * r);
-    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), 16 * r);
-    const uint64_t k = ((uint64_t)hi << 32) | lo;
-    best = k > best ? k : best;
-  }
-  return best;
+// order-preserving 32-bit key of a finite float (larger value, larger key;
+// never 0) and back
+__device__ __forceinline__ uint32_t fkey(float v) {
+  const uint32_t b = __float_as_uint(v);
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+__device__ __forceinline__ float fkey_value(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
 }
 
-// Top-k of one token's logits by one wave: k rounds of a DPP arg-max over
-// order-preserving (value, lower id first) keys; probabilities from a
-// max-subtracted softmax over all E logits.
-// M = ceil(E / 64) logits per lane (E <= 64 * M).
-// SC1: read the logits with agent-coherent loads (written by other
-// workgroups of the same kernel).
-template <int M, bool SC1 = false>
-__device__ inline void topk_one_token(const float* zt, int E, int k, int renorm, int32_t* ids_out,
-                                      float* w_out) {
+// Top-k of one token's E logits by one wave, from the values each lane holds
+// (v[i] = logit of expert lane + 64 i, -inf past E): softmax over all E
+// (max-subtracted, fp32), then k rounds of a wave-wide arg-max, so the k ids
+// come out in descending order of logit with ties going to the lower id.  A
+// round takes the wave maximum of each lane's best 32-bit key, then among the
+// lanes that hold it the lowest expert id.  Lanes 0..k-1 write ids_out /
+// w_out (renormalised over the k when renorm).
+template <int M>
+__device__ inline void topk_select(float v[M], int E, int k, int renorm, int32_t* ids_out,
+                                   float* w_out) {
   const int lane = threadIdx.x & 63;
-  float v[M];
-  bool live[M];
+  uint32_t key[M];
   float m = -INFINITY;
 #pragma unroll
   for (int i = 0; i < M; ++i) {
-    const int e = lane + 64 * i;
-    live[i] = e < E;
-    if (SC1)
-      v[i] = live[i] ? __hip_atomic_load(zt + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                     : -INFINITY;
-    else
-      v[i] = live[i] ? zt[e] : -INFINITY;
+    const bool live = lane + 64 * i < E;
+    key[i] = live ? fkey(v[i]) : 0u;
     m = fmaxf(m, v[i]);
   }
   m = wave_max_dpp(m);
   float ps = 0.f;
 #pragma unroll
   for (int i = 0; i < M; ++i)
-    if (live[i]) ps += expf(v[i] - m);
+    if (key[i]) ps += expf(v[i] - m);
   const float inv = 1.0f / wave_sum_dpp(ps);
   float wsum = 0.f, my_w = 0.f;
   int my_id = 0;
   for (int j = 0; j < k; ++j) {
-    uint64_t best = 0;
-#pragma unroll
-    for (int i = 0; i < M; ++i) {
-      if (live[i]) {
-        const uint64_t key = topk_key(v[i], lane + 64 * i);
-        best = key > best ? key : best;
-      }
-    }
-    best = wave_max_u64_dpp(best);
-    const int id = topk_key_id(best);
-    float zv = 0.f;
+    uint32_t lb = 0;
+    int li = 0;
 #pragma unroll
     for (int i = 0; i < M; ++i)
-      if (lane + 64 * i == id) { live[i] = false; zv = v[i]; }
-    // the winner's logit, from the lane that held it
-    zv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(zv), id & 63));
-    const float p = expf(zv - m) * inv;
+      if (key[i] > lb) { lb = key[i]; li = i; }
+    const uint32_t gm = wave_max_u32_dpp(lb);
+    uint64_t win = __ballot(lb == gm);
+    int id = 0x7fffffff;
+    while (win) {                          // almost always a single lane
+      const int l = __builtin_ctzll(win);
+      const int cand = l + 64 * __builtin_amdgcn_readlane(li, l);
+      id = cand < id ? cand : id;
+      win &= win - 1;
+    }
+#pragma unroll
+    for (int i = 0; i < M; ++i)
+      if (lane + 64 * i == id) key[i] = 0u;
+    const float p = expf(fkey_value(gm) - m) * inv;
     wsum += p;
     if (lane == j) { my_w = p; my_id = id; }
   }
@@ -297,6 +279,20 @@ __device__ inline void topk_one_token(const float* zt, int E, int k, int renorm,
     ids_out[lane] = my_id;
     w_out[lane] = renorm ? my_w / wsum : my_w;
   }
+}
+
+// top-k of one token whose logits zt[0..E) are in memory (E <= 64 M)
+template <int M>
+__device__ inline void topk_one_token(const float* zt, int E, int k, int renorm, int32_t* ids_out,
+                                      float* w_out) {
+  const int lane = threadIdx.x & 63;
+  float v[M];
+#pragma unroll
+  for (int i = 0; i < M; ++i) {
+    const int e = lane + 64 * i;
+    v[i] = e < E ? zt[e] : -INFINITY;
+  }
+  topk_select<M>(v, E, k, renorm, ids_out, w_out);
 }
 
 }  // namespace moe

@@ -16,7 +16,7 @@ struct DecodeLaunch {
   const void* pool;
   const void* shared;
   unsigned* hdr;          // counter header (zero before first use)
-  float* z;               // [T][E]
+  uint64_t* z;            // [T][E] generation-tagged logits
   float* h;               // [T*k + T][I]
   unsigned long long* stamps;  // [kMaxWorkgroups][16] phase stamps (timing only)
   float* y;

@@ -273,16 +273,32 @@ def test_decode_dsv4_full_layer_sampled(ops, T, sample):
     assert olayer.row_rel_error(y[sample], ref) < TOL
 
 
-def _route_decode(ops, L, x, slot_of=None):
+def _route_decode(ops, L, x, slot_of=None, ws=None):
     T, k, H = x.shape[0], L.s["top_k"], L.s["hidden"]
     ids = torch.full((T, k), -7, dtype=torch.int32, device="cuda")
     w = torch.full((T, k), float("nan"), dtype=torch.float32, device="cuda")
     y = torch.full((T, H), float("nan"), dtype=torch.float32, device="cuda")
-    ws = ops.workspace(L.desc, T, 1)
+    if ws is None:
+        ws = ops.workspace(L.desc, T, 1)
     ops.route_decode(L.desc, x, L.w_router, ids, w, L.pool, y, ws, slot_of=slot_of,
                      shared=L.shared)
     torch.cuda.synchronize()
     return ids, w, y, ws
+
+
+def _launches(L, T):
+    """Kernel launches of one decode call: x of every token of a launch must
+    fit the 120 KB LDS stage, and a launch takes at most 16 tokens."""
+    per = min(61440 // L.s["hidden"], 16)
+    return (T + per - 1) // per
+
+
+def _counters_clear(ws, launches):
+    """Decode header after `launches` launches on a fresh workspace: every
+    count back at zero (exit groups at word 96, the gate/up and exit lines
+    from word 128), the launch generation (word 0) advanced once per launch."""
+    hdr = ws[:8192].view(torch.int32)
+    return torch.count_nonzero(hdr[96:1152]).item() == 0 and hdr[0].item() == launches
 
 
 def _check_ids(L, x, gi, gw, renorm=False):
@@ -296,6 +312,7 @@ def _check_ids(L, x, gi, gw, renorm=False):
 @pytest.mark.parametrize("name,T,wtype", [("tiny", 1, "bf16"), ("tiny", 4, "mxfp4"),
                                           ("qwen_bf16_decode", 1, None),
                                           ("qwen_bf16_decode", 4, None),
+                                          ("qwen_bf16_decode", 16, None),
                                           ("ragged_decode", 3, None),
                                           ("ragged_decode", 9, None),
                                           ("glm_cache_decode", 1, None)])
@@ -309,13 +326,21 @@ def test_route_decode(ops, name, T, wtype):
     _check_ids(L, x, gi, gw)
     ref = _oracle_out(L, x, gi, gw)
     assert olayer.row_rel_error(y.cpu().numpy(), ref) < TOL
-    # the ticket counter is re-armed
-    assert torch.count_nonzero(ws[:256]).item() == 0
+    # the counts are re-armed
+    assert _counters_clear(ws, _launches(L, T))
     # a second call on the same workspace: same routing, same output up to
     # the order of the fp32 atomic adds
-    ids2, w2, y2, _ = _route_decode(ops, L, x)
+    ids2, w2, y2, _ = _route_decode(ops, L, x, ws=ws)
     assert torch.equal(ids, ids2)
     assert olayer.row_rel_error(y2.cpu().numpy(), y.cpu().numpy().astype(np.float64)) < 1e-5
+    # then fewer tokens on that workspace: the logits left by the earlier
+    # launches (other rows, older generation) must not be taken
+    if T > 1:
+        xs = x[1:].contiguous()
+        ids3, w3, y3, _ = _route_decode(ops, L, xs, ws=ws)
+        assert torch.equal(ids3, ids[1:])
+        assert olayer.row_rel_error(y3.cpu().numpy(), ref[1:]) < TOL
+        assert _counters_clear(ws, 2 * _launches(L, T) + _launches(L, T - 1))
 
 
 @pytest.mark.parametrize("T,sample", [(1, [0]), (4, [1])])
@@ -328,7 +353,7 @@ def test_route_decode_dsv4_full_sampled(ops, T, sample):
     _check_ids(L, x, gi, gw)
     ref = _oracle_out(L, x, gi, gw, tokens=sample)
     assert olayer.row_rel_error(y.cpu().numpy()[sample], ref) < TOL
-    assert torch.count_nonzero(ws[:256]).item() == 0
+    assert _counters_clear(ws, _launches(L, T))
 
 
 def test_route_decode_partial_subset(ops):
