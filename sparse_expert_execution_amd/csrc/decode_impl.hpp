@@ -13,23 +13,25 @@
 // the kernel is a persistent grid (every workgroup resident at once) that
 // keeps as many of those reads in flight as it can:
 //   1. every workgroup stages x into LDS, takes its share of the router dot
-//      products z[t][e] = W_r[e] . x[t] and counts itself done, clears its
-//      slice of y and starts on its share of the shared expert's gate/up
-//      rows, which need no routing.
-//   2. every workgroup waits for the router count, ranks the tokens itself
-//      (softmax + DPP arg-max top-k, one wave per token, the same result in
-//      every workgroup) and lists the distinct resident experts in
-//      first-appearance order with their (pair, token, weight) entries.
+//      products z[t][e] = W_r[e] . x[t] (stored tagged with the launch's
+//      generation), clears its slice of y and starts on its share of the
+//      shared expert's gate/up rows, which need no routing.
+//   2. every workgroup polls the logits until they carry this launch's
+//      generation, ranks the tokens itself (softmax + rank count for small
+//      batches, a DPP arg-max per token otherwise; the same result in every
+//      workgroup) and lists the distinct resident experts in first-appearance
+//      order with their (pair, token, weight) entries.
 //   3. gate/up: the rows of I of all selected experts are split evenly over
 //      the grid; a wave streams one gate row and one up row at a time (two in
 //      flight), dots them with each of the expert's tokens and writes
-//      h = silu(g) * u to the workspace.
-//   4. each workgroup counts itself done with gate/up, issues the loads of
-//      its first down rows and waits for the whole grid (the only grid-wide
-//      wait).
-//   5. down: the rows of H of all selected experts are split evenly over the
-//      grid; each row is dotted with h of each of the expert's tokens and the
-//      gate-weighted result added into y[t][row] with an fp32 atomic.
+//      h = silu(g) * u to the workspace, tagged with the launch's generation.
+//   4. each workgroup issues the loads of its first down rows; there is no
+//      grid-wide wait: the h values a workgroup needs are polled one by one
+//      until they carry this launch's generation.
+//   5. down: the rows of H of every expert (its tokens in chunks of two) are
+//      split evenly over the grid; each row is dotted with h of each of the
+//      chunk's tokens and the gate-weighted result added into y[t][row] with
+//      an fp32 atomic, once every workgroup has cleared its slice of y.
 // Waits are bounded: an expired wait sets an error word and lets the kernel
 // finish with wrong results instead of hanging.
 #pragma once
@@ -71,8 +73,8 @@ enum {
   kHError = 32,                     // 1: a wait expired
   kHTiming = 64,                    // non-zero: record phase stamps
   kHExitTop = 96,                   // exit groups complete
-  kHGateUp = 128,                   // kNCtr lines: workgroups done with gate/up
-  kHExit = kHGateUp + kNCtr * kLine,  // kNCtr lines: workgroups exited
+  kHYZero = 128,                    // kNCtr lines: workgroups that cleared their y slice
+  kHExit = kHYZero + kNCtr * kLine,   // kNCtr lines: workgroups exited
   kHStamps = kHExit + kNCtr * kLine   // uint64 phase stamps
 };
 
@@ -87,7 +89,7 @@ struct DecArgs {
   const uint8_t* shared;
   unsigned* hdr;
   uint64_t* z;             // [T][E] logits tagged with the launch's generation
-  float* h;                // [T*k + T][I]
+  uint64_t* h;             // [T*k + T][I] h values tagged with the generation
   unsigned long long* st;  // [workgroup][16] phase stamps
   float* y;                // [T][H]
   int64_t expert_bytes;
@@ -98,6 +100,7 @@ struct DecArgs {
   int lx;                  // 16-byte vectors per lane per gate/up row
   int lr;                  // lanes per down row (a power of two <= 64)
   int nv;                  // 16-byte vectors per lane per down row
+  unsigned gen;            // this launch's generation (set in the kernel)
 };
 
 // phase timing (header word kHTiming non-zero): 100 MHz wall clock of
@@ -127,13 +130,6 @@ __device__ __forceinline__ void coherent_store(float* p, float v) {
 }
 __device__ __forceinline__ void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
-// 16 bytes at a byte offset of a buffer, agent-coherent (sc1)
-__device__ __forceinline__ float4 coherent_load16(__amdgpu_buffer_rsrc_t r, int byte_off) {
-  const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 16);
-  return make_float4(__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z),
-                     __uint_as_float(v.w));
-}
 
 
 // every wave waits for its coherent stores, then thread 0 counts the
@@ -399,7 +395,7 @@ __device__ __forceinline__ float group_sum(float v, int lr) {
 // logit and lower id), so the k experts of rank < k land directly in
 // descending order.  Leaves ids, each selected logit (zsel) and each token's
 // softmax max and 1 / sum (mx, inv; max-subtracted, fp32).
-constexpr int kRankItems = 256;
+constexpr int kRankItems = 128;
 
 __device__ void rank_topk(const DecArgs& a, DecLds& S, unsigned gen) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -798,13 +794,16 @@ __device__ __forceinline__ float gu_dot(const DecArgs& a, const DecLds& S, const
   return gsum / (1.0f + expf(-gsum)) * usum;
 }
 
-// h results of a wave to memory (coherent stores; an index past h is dropped)
+// h results of a wave to memory, each tagged with the launch's generation
+// (an index past h is dropped)
 __device__ __forceinline__ void flush_h(const DecArgs& a, WaveOut& o) {
   const int lane = threadIdx.x & 63;
   const int n = (a.T * a.k + a.T) * a.I;
   for (int q = lane; q < o.n; q += 64) {
     const int2 p = o.buf[q];
-    if ((unsigned)p.x < (unsigned)n) coherent_store(a.h + p.x, __int_as_float(p.y));
+    if ((unsigned)p.x < (unsigned)n)
+      __hip_atomic_store(a.h + p.x, ((uint64_t)a.gen << 32) | (uint32_t)p.y, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
   }
   o.n = 0;
 }
@@ -1134,17 +1133,57 @@ __device__ __forceinline__ void dn_compute(const DecArgs& a, const DecLds& S, co
   }
 }
 
-// stage h of entries [c0, c1) into LDS (coherent loads, transposed layout)
+// stage h of entries [c0, c1) into LDS (transposed layout): each value is
+// polled until it carries this launch's generation; a thread loads the four
+// values of up to four float4s before it checks any of them
 template <int WT>
-__device__ __forceinline__ void stage_h(const DecArgs& a, DecLds& S, __amdgpu_buffer_rsrc_t hr,
-                                        int c0, int c1) {
+__device__ void stage_h(const DecArgs& a, DecLds& S, int c0, int c1) {
   constexpr int EPV = WT == 1 ? 8 : 32;
+  constexpr int B = 4;
   const int I4 = a.I / 4, V = a.I / EPV;
   const int n4 = (c1 - c0) * I4;
-  for (int q = threadIdx.x; q < n4; q += kT) {
-    const int e = q / I4, c4 = q - e * I4;
-    const int v = c4 / (EPV / 4), cc = c4 - v * (EPV / 4);
-    S.d.hst[e * I4 + cc * V + v] = coherent_load16(hr, (S.p.ent_pair[c0 + e] * a.I + c4 * 4) * 4);
+  for (int q0 = threadIdx.x; q0 < n4; q0 += B * kT) {
+    uint64_t w[B][4];
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+      const int q = q0 + b * kT;
+      if (q < n4) {
+        const int e = q / I4, c4 = q - e * I4;
+        const uint64_t* src = a.h + (int64_t)S.p.ent_pair[c0 + e] * a.I + c4 * 4;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          w[b][j] = __hip_atomic_load(src + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+      const int q = q0 + b * kT;
+      if (q < n4) {
+        const int e = q / I4, c4 = q - e * I4;
+        const uint64_t* src = a.h + (int64_t)S.p.ent_pair[c0 + e] * a.I + c4 * 4;
+        unsigned spins = 0;
+        for (;;) {
+          bool all = true;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            if ((unsigned)(w[b][j] >> 32) != a.gen) {
+              all = false;
+              w[b][j] = __hip_atomic_load(src + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+          }
+          if (all) break;
+          __builtin_amdgcn_s_sleep(1);
+          if (++spins > kSpinLimit) {
+            __hip_atomic_store(a.hdr + kHError, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            break;
+          }
+        }
+        const int v = c4 / (EPV / 4), cc = c4 - v * (EPV / 4);
+        S.d.hst[e * I4 + cc * V + v] =
+            make_float4(__uint_as_float((uint32_t)w[b][0]), __uint_as_float((uint32_t)w[b][1]),
+                        __uint_as_float((uint32_t)w[b][2]), __uint_as_float((uint32_t)w[b][3]));
+      }
+    }
   }
 }
 
@@ -1168,6 +1207,7 @@ __global__ __launch_bounds__(kT) void decode_kernel(DecArgs a) {
   const bool timing = a.hdr[kHTiming] != 0;     // uniform: a scalar load
   const unsigned gen =
       __hip_atomic_load(a.hdr + kHGen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
+  a.gen = gen;
   stamp(timing, a, 0);
 
   // 1. router dot products (every workgroup), with x staged into LDS while
@@ -1192,6 +1232,10 @@ __global__ __launch_bounds__(kT) void decode_kernel(DecArgs a) {
     split(a.I, G, bid, lo, hi);
     gateup_range<WT, LXC, RG, true>(a, S, lo, hi, [] {});
   }
+  // the slice of y is clear (counted once its stores are done; checked
+  // before the first y result is added)
+  signal_done(a.hdr + kHYZero);
+  stamp(timing, a, 8);
 
   // 2. the expert list
   build_units<M, CE>(a, S, route, timing, gen);
@@ -1222,11 +1266,9 @@ __global__ __launch_bounds__(kT) void decode_kernel(DecArgs a) {
     gateup_range<WT, LXC, RG, false>(a, S, lo, hi, [] {});
   }
 
-  // 4. count this workgroup done, issue the loads of its first down steps,
-  // then the grid-wide wait for h
+  // 4. issue the loads of the first down steps; h is polled per value when
+  // staged (no grid-wide wait)
   stamp(timing, a, 7);
-  signal_done(a.hdr + kHGateUp);
-  stamp(timing, a, 8);
   if (d0 < d1) {
 #pragma unroll
     for (int d = 0; d < DD; ++d) {
@@ -1234,13 +1276,14 @@ __global__ __launch_bounds__(kT) void decode_kernel(DecArgs a) {
       dn_next(a, S, L, p1, lc);
     }
   }
-  if (wave == 0) wait_count(a, a.hdr + kHGateUp, (unsigned)G);
-  __syncthreads();
+  // the y-cleared count, read now and checked before the first y add
+  const unsigned yz = lane < kNCtr ? __hip_atomic_load(a.hdr + kHYZero + lane * kLine,
+                                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                                   : 0u;
+  bool y_clear = false;
   stamp(timing, a, 2);
 
   // 5. down rows, pass by pass
-  const __amdgpu_buffer_rsrc_t hr = __builtin_amdgcn_make_buffer_rsrc(
-      a.h, 0, (a.T * a.k + a.T) * a.I * 4, 0x00020000);
   WaveOut out;                             // y results
   out.cap = kYOut;
   out.buf = S.d.yout + wave * kYOut;
@@ -1254,7 +1297,7 @@ __global__ __launch_bounds__(kT) void decode_kernel(DecArgs a) {
     const int vl = (p1 - 1) / a.H;
     const int E0 = uni(S.p.vu_e0[p0 / a.H]), E1 = uni(S.p.vu_e0[vl]) + uni(S.p.vu_n[vl]);
     __syncthreads();
-    stage_h<WT>(a, S, hr, E0, E1);
+    stage_h<WT>(a, S, E0, E1);
     if (!first) {
 #pragma unroll
       for (int d = 0; d < DD; ++d) {
@@ -1280,6 +1323,11 @@ __global__ __launch_bounds__(kT) void decode_kernel(DecArgs a) {
         dn_next(a, S, L, p1, lc);
       }
     }
+    if (!y_clear) {
+      if (__builtin_amdgcn_readfirstlane((unsigned)wave_sum_dpp((float)yz)) < (unsigned)G)
+        wait_count(a, a.hdr + kHYZero, (unsigned)G);
+      y_clear = true;
+    }
     flush_y(a, out);
     stamp(timing, a, 12);
   }
@@ -1298,7 +1346,7 @@ __global__ __launch_bounds__(kT) void decode_kernel(DecArgs a) {
         __hip_atomic_fetch_add(a.hdr + kHExitTop, 1u, __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_AGENT) == ngrp - 1) {
       for (int j = 0; j < kNCtr; ++j) {
-        __hip_atomic_store(a.hdr + kHGateUp + j * kLine, 0u, __ATOMIC_RELAXED,
+        __hip_atomic_store(a.hdr + kHYZero + j * kLine, 0u, __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
         __hip_atomic_store(a.hdr + kHExit + j * kLine, 0u, __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);

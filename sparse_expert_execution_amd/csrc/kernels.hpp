@@ -17,7 +17,7 @@ struct DecodeLaunch {
   const void* shared;
   unsigned* hdr;          // counter header (zero before first use)
   uint64_t* z;            // [T][E] generation-tagged logits
-  float* h;               // [T*k + T][I]
+  uint64_t* h;            // [T*k + T][I] generation-tagged h
   unsigned long long* stamps;  // [kMaxWorkgroups][16] phase stamps (timing only)
   float* y;
   int64_t expert_bytes;
