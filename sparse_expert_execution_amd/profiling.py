@@ -8,6 +8,11 @@
         ``rocprofv3 --pmc FETCH_SIZE`` (then WRITE_SIZE) to calibrate the
         counters against kernels whose traffic is known.
 
+    python -m sparse_expert_execution_amd.profiling run-prefill <workload>
+        [--tokens T] [--calls N]
+        Builds one synthetic layer (every expert resident) and makes N
+        moe_route + moe_prefill calls over T tokens, for a kernel trace.
+
     python -m sparse_expert_execution_amd.profiling summarize --name NAME
         --stats run_kernel_stats.csv --fetch fetch.csv --write write.csv
         --alg-bytes B --cmd-stats "..." --cmd-fetch "..." --cmd-write "..."
@@ -88,6 +93,40 @@ def cmd_run(args):
           f"{PROBE_BYTES} B, copy {COPY_BYTES} B", flush=True)
 
 
+def cmd_run_prefill(args):
+    import torch
+    sys.path.insert(0, ROOT)
+    import synth
+    from sparse_expert_execution_amd import ops
+    s = synth.SHAPES[args.workload]
+    desc = ops.make_desc(s["hidden"], s["inter"], s["n_experts"], s["top_k"],
+                         has_shared=s["shared"], wtype=s["wtype"], router_wtype="bf16")
+    _, eb = ops.expert_layout(desc)
+    E, T, k = s["n_experts"], args.tokens, s["top_k"]
+    pool = torch.empty(E * eb, dtype=torch.uint8, device="cuda")
+    for e in range(E):
+        ops.pack_expert(desc, pool[e * eb:(e + 1) * eb],
+                        *synth.expert_weights(args.workload, 0, e, device="cuda"))
+    sh = None
+    if s["shared"]:
+        sh = torch.empty(eb, dtype=torch.uint8, device="cuda")
+        ops.pack_expert(desc, sh, *synth.expert_weights(args.workload, 0, E, device="cuda"))
+    wr = synth.router_weights(args.workload, 0, device="cuda")
+    x = synth.tokens(args.workload, 0, T, device="cuda")
+    ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    y = torch.empty((T, s["hidden"]), dtype=torch.float32, device="cuda")
+    rws = ops.workspace(desc, T, 0)
+    ws = ops.workspace(desc, T, 2)
+    torch.cuda.synchronize()
+    for _ in range(args.calls):
+        ops.route(desc, x, wr, ids, w, rws)
+        ops.prefill(desc, x, ids, w, pool, y, ws, shared=sh)
+    torch.cuda.synchronize()
+    print(f"profiling run: {args.calls} route + prefill calls of {args.workload} T={T}",
+          flush=True)
+
+
 def _counter_rows(path, counter):
     rows = []
     with open(path) as f:
@@ -101,8 +140,27 @@ def _mean(xs):
     return sum(xs) / len(xs) if xs else None
 
 
+def _stats_table(stats):
+    lines = ["| kernel | calls | avg us | min us | max us | % |", "|---|---|---|---|---|---|"]
+    for r in sorted(stats, key=lambda r: -float(r["TotalDurationNs"]))[:12]:
+        lines.append(f"| {r['Name'][:80]} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
+                     f"{float(r['Percentage']):.1f} |")
+    return lines
+
+
 def cmd_summarize(args):
     stats = list(csv.DictReader(open(args.stats)))
+    if not args.fetch:
+        lines = [f"# {args.name}", "", "Kernel trace (rocprofv3 --kernel-trace --stats):", "",
+                 f"    {args.cmd_stats}", ""] + _stats_table(stats)
+        if args.note:
+            lines += ["", args.note]
+        os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+        with open(os.path.join(ROOT, "profiles", f"{args.name}.md"), "w") as f:
+            f.write("\n".join(lines) + "\n")
+        print("\n".join(lines))
+        return
     fetch = _counter_rows(args.fetch, "FETCH_SIZE")
     write = _counter_rows(args.write, "WRITE_SIZE")
     dec = lambda n: "decode_kernel" in n
@@ -128,12 +186,7 @@ def cmd_summarize(args):
     with open(os.path.join(ROOT, "profiles", f"{args.name}.traffic.json"), "w") as f:
         json.dump(rec, f, indent=1)
     lines = [f"# {args.name}", "", "Kernel trace (rocprofv3 --kernel-trace --stats):", "",
-             f"    {args.cmd_stats}", "", "| kernel | calls | avg us | min us | max us | % |",
-             "|---|---|---|---|---|---|"]
-    for r in sorted(stats, key=lambda r: -float(r["TotalDurationNs"]))[:12]:
-        lines.append(f"| {r['Name'][:80]} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
-                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
-                     f"{float(r['Percentage']):.1f} |")
+             f"    {args.cmd_stats}", ""] + _stats_table(stats)
     lines += ["", "HBM traffic of the decode kernel (rocprofv3 --pmc, one counter per run):", "",
               f"    {args.cmd_fetch}", f"    {args.cmd_write}", "",
               f"- FETCH_SIZE per launch: {f_dec} KiB raw; read-probe calibration "
@@ -155,11 +208,16 @@ def main():
     r.add_argument("--tokens", type=int, default=1)
     r.add_argument("--layers", type=int, default=8)
     r.add_argument("--calls", type=int, default=16)
+    rp = sub.add_parser("run-prefill")
+    rp.add_argument("workload")
+    rp.add_argument("--tokens", type=int, default=4096)
+    rp.add_argument("--calls", type=int, default=10)
     s = sub.add_parser("summarize")
     s.add_argument("--name", required=True)
     s.add_argument("--stats", required=True)
-    s.add_argument("--fetch", required=True)
-    s.add_argument("--write", required=True)
+    s.add_argument("--fetch", default=None)
+    s.add_argument("--write", default=None)
+    s.add_argument("--note", default="")
     s.add_argument("--alg-bytes", type=float, default=None)
     s.add_argument("--cmd-stats", default="")
     s.add_argument("--cmd-fetch", default="")
@@ -167,6 +225,8 @@ def main():
     a = ap.parse_args()
     if a.cmd == "run":
         cmd_run(a)
+    elif a.cmd == "run-prefill":
+        cmd_run_prefill(a)
     else:
         cmd_summarize(a)
 
