@@ -197,13 +197,15 @@ def prefill_record(ops, Lw, T, steps, warmup):
     }
 
 
-def cache_record(ops, steps_limit=None):
+def cache_record(ops, steps_limit=None, resize_at=None):
     """Expert-cache decode: 64 LRU slots over a 256-expert pinned host pool,
     Zipf(1.1) trace drifting every 32 steps, q = q* from the measured PCIe
     rate and the measured host expert-kernel rate.  Per step: fills on a side
     stream, the GPU partial over resident + filled experts, the host partial
     over the other misses (moe_host_experts on the host cores, while the GPU
-    works), then the exact merge on the GPU."""
+    works), then the exact merge on the GPU.  resize_at {step: n_slots}:
+    elastic rebuilds of the cache before those steps (shrinking in place,
+    growing into a pool allocated before the timed loop)."""
     name = "glm_cache_decode"
     s = synth.SHAPES[name]
     H, I, E, k, slots = s["hidden"], s["inter"], s["n_experts"], s["top_k"], s["slots"]
@@ -239,19 +241,40 @@ def cache_record(ops, steps_limit=None):
     comp = torch.cuda.current_stream()
     hits = misses = fills = 0
     qs = []
+    resize_at = resize_at or {}
+    grow_pools, n_cur = {}, slots
+    for st_r in sorted(resize_at):
+        if resize_at[st_r] > n_cur:
+            grow_pools[st_r] = torch.empty(resize_at[st_r] * eb, dtype=torch.uint8,
+                                           device="cuda")
+        n_cur = resize_at[st_r]
+    phases = [[0, 0]]                      # [hits, misses] per budget phase
+    rebuild_ev = []
+    cur_pool = dev_pool
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.time()
     t_start.record(comp)
     for st in range(steps):
+        if st in resize_at:
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            cur_pool = grow_pools.get(st, cur_pool)
+            e0.record(comp)
+            cache.resize(cur_pool, resize_at[st], comp)
+            e1.record(comp)
+            rebuild_ev.append((st, resize_at[st], e0, e1))
+            phases.append([0, 0])
         plan = cache.plan(0, ids_tr[st], w_tr[st], -1)
         hits += plan.n_hits
         misses += plan.n_misses
+        phases[-1][0] += plan.n_hits
+        phases[-1][1] += plan.n_misses
         fills += plan.q
         qs.append(plan.q)
         cache.fill(plan, side, comp)
-        ops.decode(desc, xs[st:st + 1], d_ids[st:st + 1], d_w[st:st + 1], dev_pool, y, ws,
+        ops.decode(desc, xs[st:st + 1], d_ids[st:st + 1], d_w[st:st + 1], cur_pool, y, ws,
                    slot_of=table[0])
         cache.release(plan, comp)
         # the host side runs while the GPU works on the fills and the decode
@@ -276,6 +299,11 @@ def cache_record(ops, steps_limit=None):
         "b_pcie_GBps": bp / 1e9, "b_host_read_GBps": bh / 1e9,
         "b_host_expert_kernel_GBps": bx / 1e9, "host_experts_run": host_experts,
         "fill_GBps": fills * eb / (ms * 1e-3) / 1e9,
+        **({"budgets": [slots] + [n for _, n, _, _ in rebuild_ev],
+            "rebuild_at_step": [st for st, _, _, _ in rebuild_ev],
+            "rebuild_ms": [a.elapsed_time(b) for _, _, a, b in rebuild_ev],
+            "miss_rate_per_budget": [m / max(1, h + m) for h, m in phases]}
+           if rebuild_ev else {}),
     }
 
 
@@ -387,6 +415,12 @@ def main():
             log(json.dumps(details["glm_cache_decode"]))
         except Exception as ex:
             details["glm_cache_decode_error"] = repr(ex)
+        try:
+            log("cache decode trace, elastic budget 64 -> 32 -> 96 slots")
+            details["glm_cache_decode_elastic"] = cache_record(ops, resize_at={170: 32, 340: 96})
+            log(json.dumps(details["glm_cache_decode_elastic"]))
+        except Exception as ex:
+            details["glm_cache_decode_elastic_error"] = repr(ex)
 
     cpu = None
     if not args.no_cpu:

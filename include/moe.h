@@ -286,6 +286,18 @@ int moe_planner_plan(moe_planner* p, int32_t layer, const int32_t* ids,
 int moe_planner_rollback(moe_planner* p);
 /* slot of each expert of `layer` (-1 = not resident), host out [n_experts] */
 int moe_planner_slot_table(const moe_planner* p, int32_t layer, int32_t* out);
+/* Rebuild the cache state under a budget of n_slots (>= 1) slots: the
+ * n_slots most recently used residents survive (ties to the lower slot) and
+ * keep their recency; a survivor whose slot is below n_slots stays there,
+ * the others move, in old-slot order, into the free slots below n_slots in
+ * ascending order; the rest are evicted.  old_of_new: host out [n_slots],
+ * the old slot each new slot's expert comes from (-1 = empty).  The pages
+ * rebuild the GPU expert cache under a revised VRAM budget at scheduler safe
+ * points without restarting or reloading the host pool (futuresignalnews.com,
+ * "3. Elastic Memory Management"); which experts survive and where they go is
+ * the reading used.  Drops the rollback level. */
+int moe_planner_resize(moe_planner* p, int32_t n_slots, int32_t* old_of_new);
+int32_t moe_planner_n_slots(const moe_planner* p);
 
 /* ---- expert cache: planner + async fills from a pinned host pool ------- */
 /* moe_cache_create keeps the caller's pointers until moe_cache_destroy:
@@ -320,6 +332,19 @@ int cache_fill(moe_cache* c, const moe_plan* plan, void* side_stream,
 /* Record, on compute_stream, the last use of every slot the plan reads
  * (hits and fills); call after the step's moe_decode is enqueued. */
 int moe_cache_release(moe_cache* c, const moe_plan* plan, void* compute_stream);
+/* Rebuild the cache under a new budget of n_slots at a safe point (between
+ * steps: after the last step's moe_cache_release): moe_planner_resize's rule,
+ * then, on compute_stream, one device-to-device copy per survivor that
+ * changes address and the device slot table updated (evicted -> -1, moved ->
+ * new slot).  dev_slot_pool (caller-owned, n_slots blocks of expert_bytes)
+ * is either the current pool (shrinking in place: no copy overlaps) or a
+ * range disjoint from it (else MOE_EINVAL); the old pool must stay allocated
+ * until compute_stream has passed this call.  Fills after the rebuild wait
+ * for it.  Elastic memory management (futuresignalnews.com, "3. Elastic
+ * Memory Management"; "FreeToken 753b Model Explained", "Sparse expert
+ * execution"). */
+int moe_cache_resize(moe_cache* c, void* dev_slot_pool, int32_t n_slots,
+                     void* compute_stream);
 /* Test hook: make the next n cache_fill calls fail before any copy. */
 int moe_cache_debug_fail_fills(moe_cache* c, int32_t n);
 const moe_planner* moe_cache_planner(const moe_cache* c);

@@ -26,6 +26,15 @@ textbook LRU and brute force):
   * q is clamped to the slots that can take a fill (n_slots - hits);
   * q* = argmin over q in [0, m] of max(q / B_pcie, (m - q) / B_host), ties
     to the larger q (the expert size cancels).
+
+Elastic budget: the GPU expert cache can be rebuilt under a revised slot
+budget at a scheduler safe point, without restarting or reloading the host
+pool (futuresignalnews.com, "3. Elastic Memory Management"; "FreeToken 753b
+Model Explained", "Sparse expert execution").  Readings taken (parity
+unpinned against the pages): the n' most recently used residents survive
+(ties to the lower slot) and keep their recency; a survivor whose slot is
+below n' stays there, the others move, in old-slot order, into the free slots
+below n' in ascending order; the rest are evicted.
 """
 
 import numpy as np
@@ -100,6 +109,32 @@ class LRUCache:
         return {"selected": S, "hits": hits, "misses": misses, "q": q_eff,
                 "fills": fills, "victims": victims, "host": host}
 
+    def resize(self, n_new):
+        """Rebuild under a budget of n_new slots.  Returns old_of_new: for
+        each new slot, the old slot its expert comes from (-1: empty)."""
+        resident = [s for s in range(self.n_slots) if self.slot_key[s] is not None]
+        resident.sort(key=lambda s: (-self.stamp[s], s))
+        keep = resident[:n_new]
+        for s in resident[n_new:]:
+            del self.where[self.slot_key[s]]
+        stay = sorted(s for s in keep if s < n_new)
+        movers = sorted(s for s in keep if s >= n_new)
+        free = [d for d in range(n_new) if d not in set(stay)]
+        old_of_new = [-1] * n_new
+        for s in stay:
+            old_of_new[s] = s
+        for s, d in zip(movers, free):
+            old_of_new[d] = s
+        key = [None] * n_new
+        stamp = [0] * n_new
+        for d, s in enumerate(old_of_new):
+            if s >= 0:
+                key[d] = self.slot_key[s]
+                stamp[d] = self.stamp[s]
+                self.where[key[d]] = d
+        self.slot_key, self.stamp, self.n_slots = key, stamp, n_new
+        return old_of_new
+
     def slot_of_expert(self, layer, n_experts):
         out = np.full(n_experts, -1, dtype=np.int32)
         for (l, e), s in self.where.items():
@@ -109,11 +144,13 @@ class LRUCache:
 
 
 def lru_sim(trace_ids, trace_w, n_slots, n_experts, q=None, b_pcie=None,
-            b_host=None, layer=0):
+            b_host=None, layer=0, resize_at=None):
     """Run a single-layer trace through the cache.
 
     trace_ids [steps, T, k] (or [steps, k]); trace_w same shape.
     q: a fixed per-step fill count, or None to use q* from the bandwidths.
+    resize_at: optional {step: n_slots}: rebuild under that budget before
+    the step.
     Returns (list of per-step plans, [steps, E] slot table after each step).
     """
     trace_ids = np.asarray(trace_ids)
@@ -121,6 +158,8 @@ def lru_sim(trace_ids, trace_w, n_slots, n_experts, q=None, b_pcie=None,
     cache = LRUCache(n_slots)
     plans, tables = [], []
     for s in range(trace_ids.shape[0]):
+        if resize_at and s in resize_at:
+            cache.resize(resize_at[s])
         S, _ = selected_experts(trace_ids[s], trace_w[s])
         m = sum((layer, e) not in cache.where for e in S)
         qs = qstar(m, b_pcie, b_host) if q is None else q

@@ -210,6 +210,76 @@ int cache_fill(moe_cache* c, const moe_plan* plan, void* side_stream, void* comp
   return MOE_OK;
 }
 
+int moe_cache_resize(moe_cache* c, void* dev_slot_pool, int32_t n_slots, void* compute_stream) {
+  if (!c || !dev_slot_pool) return set_error(MOE_EINVAL, "null pointer");
+  if (n_slots < 1) return set_error(MOE_EINVAL, "slot budget %d < 1", n_slots);
+  uint8_t* np = static_cast<uint8_t*>(dev_slot_pool);
+  const size_t eb = c->expert_bytes;
+  if (np != c->dev_pool) {
+    const uint8_t* a0 = c->dev_pool;
+    const uint8_t* a1 = a0 + (size_t)c->n_slots * eb;
+    const uint8_t* b1 = np + (size_t)n_slots * eb;
+    if (np < a1 && a0 < b1)
+      return set_error(MOE_EINVAL, "new slot pool overlaps the old one without being it");
+  }
+  hipStream_t comp = static_cast<hipStream_t>(compute_stream);
+  const int32_t n_old = c->n_slots;
+  std::vector<int32_t> old_key(n_old);
+  for (int32_t s = 0; s < n_old; ++s) old_key[s] = moe::planner_slot_key(c->planner, s);
+  // events of the new budget first, so that a failure leaves everything as it was
+  std::vector<hipEvent_t> ev(n_slots, nullptr);
+  hipError_t err = hipSuccess;
+  for (int32_t s = n_old; s < n_slots && err == hipSuccess; ++s)
+    err = hipEventCreateWithFlags(&ev[s], hipEventDisableTiming);
+  if (err != hipSuccess) {
+    for (hipEvent_t e : ev)
+      if (e) (void)hipEventDestroy(e);
+    return hip_status(err, "moe_cache_resize");
+  }
+  std::vector<int32_t> old_of_new(n_slots);
+  int st = moe::planner_resize(c->planner, n_slots, old_of_new.data());
+  if (st) {
+    for (hipEvent_t e : ev)
+      if (e) (void)hipEventDestroy(e);
+    return st;
+  }
+  std::vector<int32_t> new_of_old(n_old, -1);
+  for (int32_t d = 0; d < n_slots; ++d)
+    if (old_of_new[d] >= 0) new_of_old[old_of_new[d]] = d;
+  // survivors that change place: device-to-device copies on the compute
+  // stream, after every earlier reader of the old slots
+  for (int32_t d = 0; d < n_slots && err == hipSuccess; ++d) {
+    const int32_t s = old_of_new[d];
+    if (s < 0) continue;
+    uint8_t* dst = np + (size_t)d * eb;
+    const uint8_t* src = c->dev_pool + (size_t)s * eb;
+    if (dst != src) err = hipMemcpyAsync(dst, src, eb, hipMemcpyDeviceToDevice, comp);
+  }
+  std::vector<std::pair<int32_t, int32_t>> ups;
+  for (int32_t s = 0; s < n_old; ++s) {
+    if (old_key[s] < 0) continue;
+    if (new_of_old[s] < 0) ups.emplace_back(old_key[s], -1);
+    else if (new_of_old[s] != s) ups.emplace_back(old_key[s], new_of_old[s]);
+  }
+  for (int32_t s = 0; s < n_old; ++s) {
+    if (s < n_slots) ev[s] = c->slot_event[s];
+    else (void)hipEventDestroy(c->slot_event[s]);
+  }
+  c->slot_event = std::move(ev);
+  c->slot_recorded.assign(n_slots, 0);
+  c->dev_pool = np;
+  c->n_slots = n_slots;
+  if (err == hipSuccess) st = push_updates(c, ups, comp);
+  else st = hip_status(err, "moe_cache_resize copies");
+  // every slot's last use is now this rebuild
+  for (int32_t s = 0; s < n_slots && st == MOE_OK; ++s) {
+    err = hipEventRecord(c->slot_event[s], comp);
+    if (err != hipSuccess) st = hip_status(err, "moe_cache_resize");
+    else c->slot_recorded[s] = 1;
+  }
+  return st;
+}
+
 int moe_cache_release(moe_cache* c, const moe_plan* plan, void* compute_stream) {
   if (!c || !plan) return set_error(MOE_EINVAL, "null pointer");
   hipStream_t comp = static_cast<hipStream_t>(compute_stream);

@@ -155,6 +155,59 @@ int planner_rollback(moe_planner* p) {
   return MOE_OK;
 }
 
+// Rebuild under n_new slots: the n_new most recently used residents survive
+// (ties to the lower slot) with their recency; a survivor below n_new keeps
+// its slot, the others move in old-slot order into the free slots below
+// n_new, ascending.  old_of_new[d] = the old slot of new slot d's expert (-1:
+// empty).
+int planner_resize(moe_planner* p, int32_t n_new, int32_t* old_of_new) {
+  if (!p || !old_of_new) return set_error(MOE_EINVAL, "null pointer");
+  if (n_new < 1) return set_error(MOE_EINVAL, "slot budget %d < 1", n_new);
+  std::vector<int32_t> res;
+  for (int32_t s = 0; s < p->n_slots; ++s)
+    if (p->st.slot_key[s] >= 0) res.push_back(s);
+  std::stable_sort(res.begin(), res.end(), [&](int32_t a, int32_t b) {
+    if (p->st.stamp[a] != p->st.stamp[b]) return p->st.stamp[a] > p->st.stamp[b];
+    return a < b;
+  });
+  const size_t keep = std::min<size_t>(res.size(), (size_t)n_new);
+  std::vector<char> used(n_new, 0);
+  std::vector<int32_t> movers;
+  for (int32_t d = 0; d < n_new; ++d) old_of_new[d] = -1;
+  for (size_t i = 0; i < keep; ++i) {
+    const int32_t s = res[i];
+    if (s < n_new) {
+      old_of_new[s] = s;
+      used[s] = 1;
+    } else {
+      movers.push_back(s);
+    }
+  }
+  std::sort(movers.begin(), movers.end());
+  int32_t d = 0;
+  for (int32_t s : movers) {
+    while (used[d]) ++d;
+    old_of_new[d] = s;
+    used[d] = 1;
+  }
+  PlannerState ns;
+  ns.slot_key.assign(n_new, -1);
+  ns.stamp.assign(n_new, 0);
+  ns.where.assign(p->st.where.size(), -1);
+  ns.clock = p->st.clock;
+  for (int32_t t = 0; t < n_new; ++t) {
+    const int32_t s = old_of_new[t];
+    if (s < 0) continue;
+    ns.slot_key[t] = p->st.slot_key[s];
+    ns.stamp[t] = p->st.stamp[s];
+    ns.where[ns.slot_key[t]] = t;
+  }
+  p->st = std::move(ns);
+  p->n_slots = n_new;
+  p->have_saved = false;
+  return MOE_OK;
+}
+
 void planner_forget_slot(moe_planner* p, int32_t slot) {
   const int32_t key = p->st.slot_key[slot];
   if (key >= 0) p->st.where[key] = -1;
@@ -204,6 +257,12 @@ int moe_planner_plan(moe_planner* p, int32_t layer, const int32_t* ids, const fl
 }
 
 int moe_planner_rollback(moe_planner* p) { return moe::planner_rollback(p); }
+
+int moe_planner_resize(moe_planner* p, int32_t n_slots, int32_t* old_of_new) {
+  return moe::planner_resize(p, n_slots, old_of_new);
+}
+
+int32_t moe_planner_n_slots(const moe_planner* p) { return p ? p->n_slots : -1; }
 
 int moe_planner_slot_table(const moe_planner* p, int32_t layer, int32_t* out) {
   if (!p || !out) return set_error(MOE_EINVAL, "null pointer");

@@ -155,6 +155,18 @@ class Planner:
               "moe_planner_slot_table")
         return out
 
+    def resize(self, n_slots):
+        """New slot budget; returns old_of_new (numpy int32 [n_slots])."""
+        import numpy as np
+        out = np.empty(n_slots, dtype=np.int32)
+        check(lib().moe_planner_resize(self._h, n_slots, out.ctypes.data_as(ctypes.c_void_p)),
+              "moe_planner_resize")
+        return out
+
+    @property
+    def n_slots(self):
+        return lib().moe_planner_n_slots(self._h)
+
 
 def plan_dict(p):
     """A moe_plan as plain Python lists."""
@@ -210,6 +222,12 @@ class ExpertCache:
     def release(self, plan, compute_stream=None):
         check(lib().moe_cache_release(self._h, ctypes.byref(plan), _stream(compute_stream)),
               "moe_cache_release")
+
+    def resize(self, pool, n_slots, compute_stream=None):
+        """Rebuild under n_slots slots held in `pool` (the current pool or a
+        disjoint device buffer of n_slots * expert_bytes)."""
+        check(lib().moe_cache_resize(self._h, _ptr(pool), n_slots, _stream(compute_stream)),
+              "moe_cache_resize")
 
     def debug_fail_fills(self, n):
         check(lib().moe_cache_debug_fail_fills(self._h, n), "debug_fail_fills")

@@ -151,6 +151,40 @@ def test_planner_matches_oracle_lru_on_zipf_trace(q, bw):
         assert [v[1] if v[0] >= 0 else -1 for v in g["victims"]] == r["victims"]
 
 
+def test_planner_resize_matches_oracle_on_zipf_trace():
+    """Elastic budget 64 -> 32 -> 96 -> 8 mid-trace, across two layers: the
+    planner's tables and move maps equal the oracle's after every step."""
+    from sparse_expert_execution_amd import ops
+    ids, w = synth.zipf_trace(256, 8, 400, 1.1, 32)
+    at = {100: 32, 200: 96, 300: 8}
+    p = ops.Planner(2, 256, 64)
+    p.set_bandwidths(51.5, 178.0)
+    c = ocache.LRUCache(64)
+    for s in range(ids.shape[0]):
+        if s in at:
+            assert list(p.resize(at[s])) == c.resize(at[s])
+            assert p.n_slots == at[s]
+        layer = s % 2
+        S, _ = ocache.selected_experts(ids[s], w[s])
+        m = sum((layer, e) not in c.where for e in S)
+        r = c.step(layer, ids[s], w[s], ocache.qstar(m, 51.5, 178.0))
+        g = ops.plan_dict(p.plan(layer, ids[s], w[s], -1))
+        assert g["hits"] == r["hits"] and g["fills"] == r["fills"], s
+        for l in range(2):
+            assert np.array_equal(p.slot_table(l), c.slot_of_expert(l, 256)), s
+
+
+def test_planner_resize_errors():
+    from sparse_expert_execution_amd import ops
+    p = ops.Planner(1, 8, 4)
+    with pytest.raises(_lib_mod.MoeError):
+        p.resize(0)
+    p.plan(0, np.array([1, 2], np.int32), np.array([0.5, 0.5], np.float32), 2)
+    p.resize(2)
+    with pytest.raises(_lib_mod.MoeError):      # a rebuild drops the rollback level
+        p.rollback()
+
+
 def test_planner_global_across_layers_matches_oracle():
     rng = np.random.default_rng(4)
     steps, E = 300, 16

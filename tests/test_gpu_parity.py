@@ -462,6 +462,65 @@ def test_cache_trace_fills_tables_and_merge(ops):
         assert olayer.row_rel_error(y.cpu().numpy(), full) < TOL, st
 
 
+def test_cache_elastic_rebuild_keeps_outputs(ops):
+    """Elastic budget mid-trace: shrink in place to half the slots, then grow
+    into a new, larger pool.  After every step the device slot table equals
+    the oracle LRU (with the same rebuilds) and GPU partial + host partial
+    still merge to the full layer, so the moved experts arrived intact."""
+    _say("cache elastic rebuild")
+    name = "small_cache"
+    s = synth.SHAPES[name]
+    E, k, slots, steps = s["n_experts"], s["top_k"], s["slots"], 36
+    layers = s["layers"]
+    Ls = [GpuLayer(name, layer=l) for l in range(layers)]
+    eb = Ls[0].expert_bytes
+    host_pool = torch.empty(layers * E * eb, dtype=torch.uint8).pin_memory()
+    for l in range(layers):
+        host_pool[l * E * eb:(l + 1) * E * eb].copy_(Ls[l].pool.cpu())
+    pools = [torch.zeros(slots * eb, dtype=torch.uint8, device="cuda")]
+    table = torch.zeros((layers, E), dtype=torch.int32, device="cuda")
+    cache = ops.ExpertCache(host_pool, layers, E, eb, pools[0], slots, table)
+    side = torch.cuda.Stream()
+    comp = torch.cuda.current_stream()
+    ids_tr, w_tr = synth.zipf_trace(E, k, steps, s["zipf"], s["drift"], seed=8)
+    oc = ocache.LRUCache(slots)
+    rebuild = {12: ("same", slots // 2), 24: ("new", 2 * slots)}
+    rng = np.random.default_rng(9)
+    for st in range(steps):
+        if st in rebuild:
+            kind, n = rebuild[st]
+            if kind == "new":
+                pools.append(torch.zeros(n * eb, dtype=torch.uint8, device="cuda"))
+            cache.resize(pools[-1], n, comp)
+            oc.resize(n)
+        layer = int(rng.integers(0, layers))
+        ids_np, w_np = ids_tr[st:st + 1], w_tr[st:st + 1]
+        q = int(rng.integers(1, k + 1))
+        plan = cache.plan(layer, ids_np, w_np, q)
+        ref_plan = oc.step(layer, ids_np, w_np, q)
+        pd = ops.plan_dict(plan)
+        assert pd["fills"] == ref_plan["fills"] and pd["hits"] == ref_plan["hits"], st
+        cache.fill(plan, side, comp)
+        L = Ls[layer]
+        x = L.tokens(1, stream=st)
+        ids = torch.from_numpy(ids_np.astype(np.int32)).cuda()
+        w = torch.from_numpy(w_np.astype(np.float32)).cuda()
+        y = torch.empty((1, s["hidden"]), dtype=torch.float32, device="cuda")
+        ws = ops.workspace(L.desc, 1, 1)
+        ops.decode(L.desc, x, ids, w, pools[-1], y, ws, slot_of=table[layer])
+        cache.release(plan, comp)
+        inc = (oc.slot_of_expert(layer, E) >= 0)[ids_np]
+        yh = torch.from_numpy(_oracle_out(L, x, ids_np, w_np, include=~inc)
+                              .astype(np.float32)).cuda()
+        ops.merge_partials(y, yh, y)
+        torch.cuda.synchronize()
+        got_table = table.cpu().numpy()
+        for l in range(layers):
+            assert np.array_equal(got_table[l], oc.slot_of_expert(l, E)), (st, l)
+        full = _oracle_out(L, x, ids_np, w_np)
+        assert olayer.row_rel_error(y.cpu().numpy(), full) < TOL, st
+
+
 def test_cache_trace_with_host_experts_merges_to_full_layer(ops):
     """The whole split: GPU partial over resident + filled experts, host
     partial over the other misses from moe_host_experts reading the pinned

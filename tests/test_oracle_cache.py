@@ -10,14 +10,20 @@ import synth
 from oracle import cache
 
 
-def _textbook_lru(trace_ids, trace_w, n_slots):
+def _textbook_lru(trace_ids, trace_w, n_slots, resize_at=None):
     """OrderedDict LRU over whole steps: hits refresh in selection order,
     then misses (heaviest first) are inserted, evicting the least recently
-    used entry that is not part of the current step.  Returns per-step
-    (hits, misses, resident set, victims)."""
+    used entry that is not part of the current step.  resize_at {step: n}:
+    before that step the capacity becomes n and the least recently used
+    entries beyond it are dropped.  Returns per-step (hits, misses, resident
+    set, victims)."""
     od = OrderedDict()
     out = []
-    for ids, w in zip(trace_ids, trace_w):
+    for s, (ids, w) in enumerate(zip(trace_ids, trace_w)):
+        if resize_at and s in resize_at:
+            n_slots = resize_at[s]
+            while len(od) > n_slots:
+                od.popitem(last=False)
         sel, weight = [], {}
         for e, g in zip(np.ravel(ids).tolist(), np.ravel(w).tolist()):
             if e not in weight:
@@ -136,3 +142,45 @@ def test_qstar_with_page_bandwidths():
     # 51.5 GB/s pinned PCIe and 178 GB/s host expert-kernel bandwidth
     # (explainx.ai guide, resource table): 8 misses -> 2 filled, 6 on the CPU
     assert cache.qstar(8, 51.5, 178.0) == 2
+
+
+def test_resize_matches_ordereddict_on_zipf_trace():
+    """Elastic budget 64 -> 32 -> 96 mid-trace: the survivors of a rebuild are
+    the most recently used experts, and the cache then behaves as a textbook
+    LRU of the new capacity."""
+    ids, w = _trace()
+    at = {170: 32, 340: 96}
+    plans, table = cache.lru_sim(ids, w, 64, 256, q=8, resize_at=at)
+    ref = _textbook_lru(ids, w, 64, resize_at=at)
+    for s, (p, (hits, misses, resident, victims)) in enumerate(zip(plans, ref)):
+        assert p["hits"] == hits, s
+        assert p["misses"] == misses, s
+        assert set(np.nonzero(table[s] >= 0)[0].tolist()) == resident, s
+    for s in range(table.shape[0]):
+        cap = 64 if s < 170 else (32 if s < 340 else 96)
+        used = table[s][table[s] >= 0]
+        assert len(set(used.tolist())) == used.size and np.all(used < cap), s
+
+
+def test_resize_growth_moves_nothing():
+    c = cache.LRUCache(4)
+    c.step(0, [1, 2, 3], [0.5, 0.3, 0.2], q=3)
+    before = (list(c.slot_key), list(c.stamp))
+    m = c.resize(6)
+    assert m == [0, 1, 2, -1, -1, -1]
+    assert c.slot_key[:4] == before[0] and c.stamp[:4] == before[1]
+    assert c.slot_key[4:] == [None, None]
+
+
+def test_resize_shrink_placement():
+    """Survivors below the new budget stay; the others fill the free slots
+    below it in ascending order, taken in old-slot order."""
+    c = cache.LRUCache(6)
+    c.step(0, [10, 11, 12, 13, 14, 15], [6, 5, 4, 3, 2, 1], q=6)   # slots 0..5
+    c.step(0, [15, 13, 11], [1, 1, 1], q=0)                           # touch 5, 3, 1
+    m = c.resize(3)
+    # most recent: 11 (slot 1), 13 (slot 3), 15 (slot 5); 1 stays, 3 -> 0, 5 -> 2
+    assert m == [3, 1, 5]
+    assert c.where == {(0, 13): 0, (0, 11): 1, (0, 15): 2}
+    m = c.resize(1)
+    assert m == [1] and c.where == {(0, 11): 0}     # 11 now sits in slot 1
