@@ -197,6 +197,48 @@ def prefill_record(ops, Lw, T, steps, warmup):
     }
 
 
+def prefill_stream_record(ops, Lp, host_pool, lb, T, n_layers, buffers):
+    """Prefill over n_layers layers whose expert blocks stream from the pinned
+    host pool through `buffers` (1 or 2) full-layer device buffers: per layer
+    route, acquire (copy on a side stream), prefill, release.  The layers
+    share one set of synthetic weights (copied into every host slot); each
+    has its own synthetic tokens."""
+    s = Lp.s
+    H, k, E = s["hidden"], s["top_k"], s["n_experts"]
+    eb = lb // (E + 1)
+    bufs = [torch.empty(lb, dtype=torch.uint8, device="cuda") for _ in range(buffers)]
+    ls = ops.LayerStream(host_pool, n_layers, lb, bufs)
+    xs = [synth.tokens(Lp.name, l, T, device="cuda") for l in range(n_layers)]
+    ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    y = torch.empty((T, H), dtype=torch.float32, device="cuda")
+    rws = ops.workspace(Lp.desc, T, 0)
+    fws = ops.workspace(Lp.desc, T, 2)
+    copy = torch.cuda.Stream()
+    comp = torch.cuda.current_stream()
+
+    def one_pass():
+        for l in range(n_layers):
+            ops.route(Lp.desc, xs[l], Lp.routers[0], ids, w, rws)
+            buf = ls.acquire(l, copy, comp)
+            ops.prefill(Lp.desc, xs[l], ids, w, buf[:E * eb], y, fws, shared=buf[E * eb:])
+            ls.release(l, comp)
+
+    one_pass()                              # warm-up
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(comp)
+    one_pass()
+    e1.record(comp)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1)
+    del ls, bufs
+    return {"tokens": T, "layers": n_layers, "buffers": buffers,
+            "ms_per_layer": ms / n_layers, "tokens_per_s": T * n_layers / (ms * 1e-3),
+            "layer_bytes": lb, "stream_GBps": lb * n_layers / (ms * 1e-3) / 1e9}
+
+
 def cache_record(ops, steps_limit=None, resize_at=None):
     """Expert-cache decode: 64 LRU slots over a 256-expert pinned host pool,
     Zipf(1.1) trace drifting every 32 steps, q = q* from the measured PCIe
@@ -405,6 +447,25 @@ def main():
                 details[f"prefill_T{T}"] = prefill_record(ops, Lp, T, max(3, args.steps // 4),
                                                           2)
                 log(f"prefill T={T}", json.dumps(details[f"prefill_T{T}"]))
+            # full-layer streaming from a pinned host pool: two buffers vs one
+            n_st = 4
+            E3 = Lp.s["n_experts"]
+            _, eb3 = ops.expert_layout(Lp.desc)
+            lb = (E3 + 1) * eb3
+            host_pool = torch.empty(n_st * lb, dtype=torch.uint8).pin_memory()
+            host_pool[:E3 * eb3].copy_(Lp.pools[0])
+            host_pool[E3 * eb3:lb].copy_(Lp.shared[0])
+            for l in range(1, n_st):
+                host_pool[l * lb:(l + 1) * lb].copy_(host_pool[:lb])
+            for T in (4096, 8192, 16384):
+                for nbuf in (2, 1):
+                    key = f"prefill_stream_T{T}_{nbuf}buf"
+                    details[key] = prefill_stream_record(ops, Lp, host_pool, lb, T, n_st, nbuf)
+                    log(key, json.dumps(details[key]))
+                d2 = details[f"prefill_stream_T{T}_2buf"]["tokens_per_s"]
+                d1 = details[f"prefill_stream_T{T}_1buf"]["tokens_per_s"]
+                details[f"prefill_stream_T{T}_single_buffer_loss"] = 1.0 - d1 / d2
+            del host_pool
             del Lp
             torch.cuda.empty_cache()
         except Exception as ex:

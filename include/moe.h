@@ -349,6 +349,37 @@ int moe_cache_resize(moe_cache* c, void* dev_slot_pool, int32_t n_slots,
 int moe_cache_debug_fail_fills(moe_cache* c, int32_t n);
 const moe_planner* moe_cache_planner(const moe_cache* c);
 
+/* ---- full-layer prefill streaming -------------------------------------- */
+/* A long prompt routes to nearly every expert of a layer, so prefill streams
+ * whole layers from the pinned host pool; with two full-layer buffers the
+ * next layer is copied over PCIe while the GPU computes the current one
+ * ("FreeToken 753b Model Explained", "Prefill: load almost every expert
+ * without idling the GPU"; marktechpost article, full-layer double
+ * buffering).  One buffer gives the pages' ablation (copy, then compute).
+ *   host_pool  pinned host memory, [n_layers] blocks of layer_bytes (a
+ *              layer's expert blocks in slot order, e.g. its E routed experts
+ *              then its shared expert)
+ *   dev_buf0/1 caller-owned device buffers of layer_bytes each; dev_buf1 NULL
+ *              = single buffer.  Kept until moe_layer_stream_destroy.
+ * Creates HIP events; the object is single-threaded. */
+typedef struct moe_layer_stream moe_layer_stream;
+int moe_layer_stream_create(moe_layer_stream** out, const void* host_pool,
+                            int32_t n_layers, size_t layer_bytes, void* dev_buf0,
+                            void* dev_buf1);
+void moe_layer_stream_destroy(moe_layer_stream* s);
+/* Make `layer` resident for the work enqueued next on compute_stream: if its
+ * buffer (layer mod buffers) does not hold it yet, one hipMemcpyAsync on
+ * copy_stream after the buffer's last release; compute_stream then waits for
+ * the copy.  With two buffers the copy of layer + 1 is issued at once into
+ * the other buffer if that buffer's layer has been released.  *dev_layer =
+ * the device block of the layer.  MOE_ECACHE if the buffer still holds an
+ * unreleased layer. */
+int moe_layer_stream_acquire(moe_layer_stream* s, int32_t layer, void* copy_stream,
+                             void* compute_stream, void** dev_layer);
+/* The layer's work is enqueued on compute_stream: its buffer may be
+ * refilled after that work. */
+int moe_layer_stream_release(moe_layer_stream* s, int32_t layer, void* compute_stream);
+
 /* ---- bandwidth probe --------------------------------------------------- */
 /* Measures pinned host->device copy bandwidth (bytes / s) from `pinned_host`
  * into `dev` (both >= bytes) on `stream`, and host-memory streaming read

@@ -36,6 +36,8 @@ EXPORTS = (
     "moe_planner_create", "moe_planner_destroy", "moe_planner_set_bandwidths",
     "moe_planner_plan", "moe_planner_rollback", "moe_planner_slot_table",
     "moe_planner_resize", "moe_planner_n_slots", "moe_cache_resize",
+    "moe_layer_stream_create", "moe_layer_stream_destroy", "moe_layer_stream_acquire",
+    "moe_layer_stream_release",
     "moe_cache_create", "moe_cache_destroy", "moe_cache_set_bandwidths",
     "moe_cache_plan", "cache_fill", "moe_cache_release",
     "moe_cache_debug_fail_fills", "moe_cache_planner", "moe_probe_bandwidths",
@@ -109,6 +111,10 @@ def lib():
         "moe_planner_resize": (ctypes.c_int, [P, I32, P]),
         "moe_planner_n_slots": (ctypes.c_int32, [P]),
         "moe_cache_resize": (ctypes.c_int, [P, P, I32, P]),
+        "moe_layer_stream_create": (ctypes.c_int, [ctypes.POINTER(P), P, I32, SZ, P, P]),
+        "moe_layer_stream_destroy": (None, [P]),
+        "moe_layer_stream_acquire": (ctypes.c_int, [P, I32, P, P, ctypes.POINTER(P)]),
+        "moe_layer_stream_release": (ctypes.c_int, [P, I32, P]),
         "moe_cache_create": (ctypes.c_int, [ctypes.POINTER(P), P, I32, I32, SZ, P, I32, P]),
         "moe_cache_destroy": (None, [P]),
         "moe_cache_set_bandwidths": (ctypes.c_int, [P, D, D]),

@@ -1240,7 +1240,7 @@ __global__ __launch_bounds__(kT) void decode_kernel(DecArgs a) {
   // 2. the expert list
   build_units<M, CE>(a, S, route, timing, gen);
   stamp(timing, a, 1);
-  const int n_routed = S.p.n_routed, n_units = S.p.n_units;
+  const int n_routed = S.p.n_routed;
 
   // 3. routed gate/up rows
   DnLane L;

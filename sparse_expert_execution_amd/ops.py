@@ -269,3 +269,42 @@ def probe_bandwidths(pinned_host, dev, reps=3, threads=0, stream=None):
                                      threads, _stream(stream), ctypes.byref(bp),
                                      ctypes.byref(bh)), "moe_probe_bandwidths")
     return bp.value, bh.value
+
+
+class LayerStream:
+    """moe_layer_stream_*: full-layer streaming of expert blocks from a pinned
+    host pool into one or two device buffers (double-buffered prefill).
+
+    host_pool  pinned uint8 tensor of n_layers * layer_bytes
+    bufs       one or two device uint8 tensors of layer_bytes each
+    """
+
+    def __init__(self, host_pool, n_layers, layer_bytes, bufs):
+        self._h = ctypes.c_void_p()
+        self._keep = (host_pool, tuple(bufs))
+        b1 = _ptr(bufs[1]) if len(bufs) > 1 else None
+        check(lib().moe_layer_stream_create(ctypes.byref(self._h), _ptr(host_pool), n_layers,
+                                            layer_bytes, _ptr(bufs[0]), b1),
+              "moe_layer_stream_create")
+        self._bufs = list(bufs)
+
+    def __del__(self):
+        if getattr(self, "_h", None) and self._h.value:
+            lib().moe_layer_stream_destroy(self._h)
+            self._h = ctypes.c_void_p()
+
+    def acquire(self, layer, copy_stream, compute_stream=None):
+        """Returns the device buffer (tensor) that holds `layer` for the work
+        enqueued next on compute_stream."""
+        out = ctypes.c_void_p()
+        check(lib().moe_layer_stream_acquire(self._h, layer, _stream(copy_stream),
+                                             _stream(compute_stream), ctypes.byref(out)),
+              "moe_layer_stream_acquire")
+        for b in self._bufs:
+            if b.data_ptr() == out.value:
+                return b
+        raise RuntimeError("moe_layer_stream_acquire returned an unknown buffer")
+
+    def release(self, layer, compute_stream=None):
+        check(lib().moe_layer_stream_release(self._h, layer, _stream(compute_stream)),
+              "moe_layer_stream_release")

@@ -219,3 +219,23 @@ def test_planner_errors_and_rollback():
     assert np.array_equal(p.slot_table(0), before)
     with pytest.raises(_lib_mod.MoeError):
         p.rollback()                               # only one level
+
+
+def test_layer_stream_argument_checks():
+    """moe_layer_stream_create rejects bad arguments before any HIP call."""
+    L = _lib_mod.lib()
+    out = ctypes.c_void_p()
+    host = ctypes.create_string_buffer(1024)
+    dev = ctypes.create_string_buffer(1024)
+    assert L.moe_layer_stream_create(None, host, 2, 512, dev, None) == _lib_mod.MOE_EINVAL
+    assert L.moe_layer_stream_create(ctypes.byref(out), None, 2, 512, dev, None) == \
+        _lib_mod.MOE_EINVAL
+    assert L.moe_layer_stream_create(ctypes.byref(out), host, 0, 512, dev, None) == \
+        _lib_mod.MOE_EINVAL
+    assert L.moe_layer_stream_create(ctypes.byref(out), host, 2, 0, dev, None) == \
+        _lib_mod.MOE_EINVAL
+    # overlapping buffers
+    base = ctypes.addressof(dev)
+    assert L.moe_layer_stream_create(ctypes.byref(out), host, 2, 512, ctypes.c_void_p(base),
+                                     ctypes.c_void_p(base + 256)) == _lib_mod.MOE_EINVAL
+    assert not out.value

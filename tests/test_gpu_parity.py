@@ -396,6 +396,52 @@ def test_prefill_partial_subset(ops):
     assert olayer.row_rel_error(y, ref) < TOL
 
 
+@pytest.mark.parametrize("buffers", [1, 2])
+def test_prefill_layer_stream(ops, buffers):
+    """Full-layer streaming from a pinned pool (one or two device buffers):
+    every layer's prefill through the streamed buffer equals the prefill over
+    its resident pool bit for bit, and the oracle."""
+    _say("prefill layer stream", buffers)
+    name = "ragged_prefill"
+    s = synth.SHAPES[name]
+    n_layers, T, E, H = 4, 48, s["n_experts"], s["hidden"]
+    Ls = [GpuLayer(name, layer=l) for l in range(n_layers)]
+    eb = Ls[0].expert_bytes
+    lb = (E + (1 if s["shared"] else 0)) * eb
+    host = torch.empty(n_layers * lb, dtype=torch.uint8).pin_memory()
+    for l, L in enumerate(Ls):
+        host[l * lb:l * lb + E * eb].copy_(L.pool.cpu())
+        if s["shared"]:
+            host[l * lb + E * eb:(l + 1) * lb].copy_(L.shared.cpu())
+    bufs = [torch.empty(lb, dtype=torch.uint8, device="cuda") for _ in range(buffers)]
+    ls = ops.LayerStream(host, n_layers, lb, bufs)
+    copy = torch.cuda.Stream()
+    comp = torch.cuda.current_stream()
+    outs = []
+    for l, L in enumerate(Ls):
+        x = L.tokens(T)
+        ids, w = _route_gpu(ops, L, x)
+        buf = ls.acquire(l, copy, comp)
+        y = torch.full((T, H), float("nan"), dtype=torch.float32, device="cuda")
+        ops.prefill(L.desc, x, ids, w, buf[:E * eb], y, ops.workspace(L.desc, T, 2),
+                    shared=buf[E * eb:] if s["shared"] else None)
+        ls.release(l, comp)
+        outs.append((x, ids, w, y))
+    torch.cuda.synchronize()
+    for l, (x, ids, w, y) in enumerate(outs):
+        L = Ls[l]
+        got = y.cpu().numpy().astype(np.float64)
+        assert np.array_equal(got, _run_decode(ops, L, x, ids, w, fn="prefill")), l
+        ref = _oracle_out(L, x, ids.cpu().numpy(), w.cpu().numpy(), prefill=True)
+        assert olayer.row_rel_error(got, ref) < TOL, l
+    # a buffer whose layer has not been released cannot take another layer
+    ls.acquire(0, copy, comp)
+    with pytest.raises(ops._lib.MoeError):
+        ls.acquire(buffers, copy, comp)
+    ls.release(0, comp)
+    torch.cuda.synchronize()
+
+
 def test_prefill_dsv4_full_layer_sampled(ops):
     _say("prefill dsv4 4096")
     L = GpuLayer("dsv4_mxfp4_prefill")
