@@ -54,8 +54,10 @@ def traffic_record(name):
 class Layers:
     """All layers of one workload resident in HBM."""
 
-    def __init__(self, ops, name, n_layers, log_every=8):
-        s = synth.SHAPES[name]
+    def __init__(self, ops, name, n_layers, log_every=8, wtype=None):
+        s = dict(synth.SHAPES[name])
+        if wtype:
+            s["wtype"] = wtype
         self.s = s
         self.name = name
         self.desc = ops.make_desc(s["hidden"], s["inter"], s["n_experts"], s["top_k"],
@@ -439,6 +441,18 @@ def main():
             torch.cuda.empty_cache()
         except Exception as ex:  # keep the headline line
             details["dsv4_mxfp4_decode_error"] = repr(ex)
+        try:
+            # the same layers with NVFP4 experts (E4M3 scale per 16 + fp32 per matrix)
+            log("building", name2, "with NVFP4 experts")
+            Ln = Layers(ops, name2, synth.SHAPES[name2]["layers"], log_every=8, wtype="nvfp4")
+            for T in (1, 4):
+                details[f"dsv4_nvfp4_decode_T{T}"] = decode_record(ops, Ln, T, args.steps,
+                                                                   args.warmup)
+                log(f"dsv4 nvfp4 T={T}", json.dumps(details[f"dsv4_nvfp4_decode_T{T}"]))
+            del Ln
+            torch.cuda.empty_cache()
+        except Exception as ex:
+            details["dsv4_nvfp4_decode_error"] = repr(ex)
         try:
             name3 = "dsv4_mxfp4_prefill"
             log("building", name3)

@@ -60,6 +60,11 @@ extern "C" {
 #define MOE_WTYPE_F32 0
 #define MOE_WTYPE_BF16 1
 #define MOE_WTYPE_MXFP4 2
+/* NVFP4: e2m1 codes [rows][K/2] (low nibble first), one OCP E4M3FN scale per
+ * 16 elements [rows][K/16], one fp32 scale per matrix; value = e2m1 * E4M3 *
+ * fp32 scale.  Decode only (prefill and the host expert kernel return
+ * MOE_EUNSUPPORTED): CDNA4's scaled MFMA takes an e8m0 scale per 32. */
+#define MOE_WTYPE_NVFP4 3
 
 /* Layer description.  hidden (H) and inter (I) must be multiples of 32
  * (MXFP4 blocks) and of 8 (BF16 16-byte vectors); 1 <= top_k <= n_experts
@@ -71,7 +76,7 @@ typedef struct moe_desc {
   int32_t top_k;        /* k: experts per token                              */
   int32_t has_shared;   /* 1: a shared expert also runs on every token, w=1  */
   int32_t renorm_topk;  /* 1: divide the k gate weights by their sum         */
-  int32_t wtype;        /* expert weights: MOE_WTYPE_BF16 or MOE_WTYPE_MXFP4 */
+  int32_t wtype;        /* expert weights: MOE_WTYPE_BF16, _MXFP4 or _NVFP4  */
   int32_t router_wtype; /* router weights: MOE_WTYPE_F32 or MOE_WTYPE_BF16   */
 } moe_desc;
 
@@ -84,6 +89,8 @@ typedef struct moe_desc {
  *   MXFP4: [0] gate codes [I][H/2], [1] gate scales [I][H/32],
  *          [2] up codes [I][H/2],   [3] up scales [I][H/32],
  *          [4] down codes [H][I/2], [5] down scales [H][I/32].
+ *   NVFP4: as MXFP4 with scales [rows][K/16] (E4M3), followed at offset
+ *          offsets[5] + H*I/16 by the fp32 scales of gate, up and down.
  * Section offsets are 16-byte aligned; *bytes is a multiple of 256.
  * moe_pack_expert writes this layout.
  * Returns MOE_EINVAL for a bad descriptor. */

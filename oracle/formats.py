@@ -22,6 +22,18 @@ X = floor(log2 a) - 2 (2 = the largest e2m1 exponent), clamped to
 grid with round-to-nearest, ties to the even code, saturating at +-6, sign
 kept (so -0 encodes as code 8).
 
+NVFP4 (the pages' format for their GLM and laptop builds, "FreeToken 753b
+Model Explained", "Performance Benchmarks and Model Fit"; not defined there)
+follows the public NVIDIA definition: e2m1 elements in blocks of 16 along K,
+each block with an FP8 E4M3 scale (OCP E4M3FN: bias 7, 3 mantissa bits,
+max 448, no infinities, 0x7F/0xFF NaN), and one fp32 scale per matrix.
+Encoding (a reading; the steps are stated in fp32 so that an implementation
+can reproduce them exactly): g = amax(matrix) / 2688 (= 6 * 448; g = 1 for
+an all-zero matrix); per block t = amax(block) / (6 * g), rounded to E4M3
+with round-to-nearest-even, saturating at 448; with d = E4M3(scale) * g
+(fp32 product) each element v / d (fp32 quotient) is rounded to e2m1 as for
+MXFP4; a block whose scale is 0 has all codes 0.  Value = e2m1 * E4M3 * g.
+
 BF16 values are the top 16 bits of an IEEE binary32; fp32 -> bf16 uses
 round-to-nearest-even (NaN kept quiet).
 
@@ -34,7 +46,12 @@ Pins (tests/test_oracle_formats.py):
     >= 4 (the scale rule then reproduces the scale);
   * a block whose max is exactly 2^n gets scale byte n - 2 + 127;
   * ``bf16_round`` against PyTorch-CPU's fp32 -> bf16 cast (library routine)
-    on random and edge values.
+    on random and edge values;
+  * ``e4m3_decode`` on all 256 codes and ``e4m3_round`` on random values and
+    every tie against PyTorch-CPU's float8_e4m3fn casts (library routine);
+  * NVFP4: every code is the nearest e2m1 grid value to its quotient (brute
+    force), scales and the global scale follow the stated fp32 steps, and
+    values built exactly on the grid encode back to themselves.
 """
 
 import numpy as np
@@ -168,3 +185,66 @@ def bf16_decode(bits):
     """bf16 bit patterns (uint16) -> exact fp64 values."""
     bits = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16
     return bits.view(np.float32).astype(np.float64)
+
+
+def e4m3_decode(s):
+    """Value of each FP8 E4M3FN byte (OCP) as fp64; 0x7F / 0xFF are NaN."""
+    s = np.asarray(s, dtype=np.int64)
+    sign = np.where(s & 0x80, -1.0, 1.0)
+    e = (s >> 3) & 0xF
+    m = (s & 7).astype(np.float64)
+    val = np.where(e == 0, m * 2.0 ** -9,
+                   np.ldexp(1.0 + m / 8.0, (e - 7).astype(np.int64)))
+    val = np.where((s & 0x7F) == 0x7F, np.nan, val)
+    return sign * val
+
+
+# non-negative E4M3 magnitudes of codes 0 .. 126, increasing with the code
+_E4M3_MAG = e4m3_decode(np.arange(127))
+
+
+def e4m3_round(t):
+    """Non-negative values -> E4M3 codes (0 .. 126): nearest magnitude, a tie
+    going to the even code, values above 448 saturating to 448 (0x7E)."""
+    t = np.asarray(t, dtype=np.float64)
+    flat = np.minimum(t.reshape(-1), 448.0)
+    if np.any(flat < 0) or np.any(np.isnan(flat)):
+        raise ValueError("E4M3 scales are rounded from non-negative values")
+    hi = np.clip(np.searchsorted(_E4M3_MAG, flat, side="left"), 0, 126)
+    lo = np.clip(hi - 1, 0, 126)
+    d_lo = np.abs(flat - _E4M3_MAG[lo])
+    d_hi = np.abs(_E4M3_MAG[hi] - flat)
+    take_hi = (d_hi < d_lo) | ((d_hi == d_lo) & ((hi & 1) == 0))
+    return np.where(take_hi, hi, lo).astype(np.uint8).reshape(t.shape)
+
+
+def nvfp4_encode(v):
+    """Quantise values [rows, K] (K % 16 == 0) to NVFP4 with the fp32 steps
+    above.  Returns (codes_u8 [rows, K/2], scales_u8 [rows, K/16], g fp32)."""
+    v = np.asarray(v, dtype=np.float32)
+    if v.ndim != 2 or v.shape[1] % 16:
+        raise ValueError("expected [rows, K] with K a multiple of 16")
+    rows, K = v.shape
+    amax_t = np.float32(np.max(np.abs(v))) if v.size else np.float32(0)
+    g = np.float32(amax_t / np.float32(2688.0)) if amax_t > 0 else np.float32(1.0)
+    blocks = v.reshape(rows, K // 16, 16)
+    amax_b = np.max(np.abs(blocks), axis=-1).astype(np.float32)
+    t = (amax_b / np.float32(np.float32(6.0) * g)).astype(np.float32)
+    scales = e4m3_round(t.astype(np.float64))
+    d = (e4m3_decode(scales).astype(np.float32) * g).astype(np.float32)
+    safe = np.where(d > 0, d, np.float32(1.0)).astype(np.float32)
+    q = (blocks / safe[..., None]).astype(np.float32)
+    codes = e2m1_round(q.astype(np.float64))
+    codes = np.where((d > 0)[..., None], codes, np.uint8(0))
+    return pack_nibbles(codes.reshape(rows, K)), scales, g
+
+
+def nvfp4_decode(codes_u8, scales_u8, g):
+    """Exact fp64 values of an NVFP4 matrix: e2m1 * E4M3 scale * g."""
+    codes = unpack_nibbles(codes_u8)
+    rows, K = codes.shape
+    scales_u8 = np.asarray(scales_u8, dtype=np.uint8)
+    if scales_u8.shape != (rows, K // 16) or K % 16:
+        raise ValueError("scale shape must be [rows, K/16]")
+    scale = np.repeat(e4m3_decode(scales_u8), 16, axis=1)
+    return e2m1_decode(codes) * scale * float(np.float32(g))

@@ -20,6 +20,7 @@ MOE_ECACHE = -5
 WTYPE_F32 = 0
 WTYPE_BF16 = 1
 WTYPE_MXFP4 = 2
+WTYPE_NVFP4 = 3
 
 MODE_ROUTE = 0
 MODE_DECODE = 1

@@ -29,6 +29,9 @@ def expert_bytes(hidden, inter, wtype):
         return 3 * hidden * inter * 4
     if wtype == "mxfp4":
         return 2 * mxfp4_matrix_bytes(inter, hidden) + mxfp4_matrix_bytes(hidden, inter)
+    if wtype == "nvfp4":
+        # e2m1 codes, an E4M3 byte per 16 elements, an fp32 scale per matrix
+        return 3 * (hidden * inter // 2 + hidden * inter // 16 + 4)
     raise ValueError(wtype)
 
 

@@ -39,7 +39,7 @@ int check_desc(const moe_desc* d) {
     return set_error(MOE_EINVAL, "n_experts %d outside [1, 1024]", d->n_experts);
   if (d->top_k < 1 || d->top_k > d->n_experts || d->top_k > 64)
     return set_error(MOE_EINVAL, "top_k %d outside [1, min(E, 64)]", d->top_k);
-  if (d->wtype != MOE_WTYPE_BF16 && d->wtype != MOE_WTYPE_MXFP4)
+  if (d->wtype != MOE_WTYPE_BF16 && d->wtype != MOE_WTYPE_MXFP4 && d->wtype != MOE_WTYPE_NVFP4)
     return set_error(MOE_EUNSUPPORTED, "expert weight type %d not supported", d->wtype);
   if (d->router_wtype != MOE_WTYPE_BF16 && d->router_wtype != MOE_WTYPE_F32)
     return set_error(MOE_EUNSUPPORTED, "router weight type %d not supported", d->router_wtype);
@@ -57,14 +57,15 @@ void layout(const moe_desc* d, size_t off[6], size_t* bytes) {
     off[3] = off[4] = off[5] = 0;
     *bytes = align_up(3 * I * H * 2);
   } else {
-    const size_t cg = I * H / 2, sg = I * H / 32;
+    const bool nv = d->wtype == MOE_WTYPE_NVFP4;
+    const size_t cg = I * H / 2, sg = I * H / (nv ? 16 : 32);
     off[0] = 0;
     off[1] = cg;
     off[2] = cg + sg;
     off[3] = 2 * cg + sg;
     off[4] = 2 * cg + 2 * sg;
     off[5] = 3 * cg + 2 * sg;
-    *bytes = align_up(3 * cg + 3 * sg);
+    *bytes = align_up(3 * cg + 3 * sg + (nv ? 16 : 0));   // NVFP4: three fp32 scales
   }
 }
 
@@ -226,6 +227,8 @@ static int decode_impl(const moe_desc* desc, const void* x, const void* w_router
   f.stamps = reinterpret_cast<unsigned long long*>(b + L.st);
   f.y = y; f.expert_bytes = (int64_t)bytes;
   for (int i = 0; i < 6; ++i) f.off[i] = (int64_t)off[i];
+  f.goff = desc->wtype == MOE_WTYPE_NVFP4
+               ? (int64_t)(off[5] + (size_t)desc->hidden * desc->inter / 16) : 0;
   f.H = desc->hidden; f.I = desc->inter; f.E = desc->n_experts; f.k = desc->top_k;
   f.wtype = desc->wtype;
   // launches of at most decode_max_tokens(H) tokens, in stream order, the
@@ -349,6 +352,13 @@ int moe_pack_expert(const moe_desc* desc, const void* gate, const void* up, cons
       err = moe::launch_pack_bf16(up, sb, I, H, reinterpret_cast<uint16_t*>(b + off[1]), s);
     if (err == hipSuccess)
       err = moe::launch_pack_bf16(down, sb, H, I, reinterpret_cast<uint16_t*>(b + off[2]), s);
+  } else if (desc->wtype == MOE_WTYPE_NVFP4) {
+    float* gs = reinterpret_cast<float*>(b + off[5] + (size_t)H * I / 16);
+    err = moe::launch_quantize_nvfp4(gate, sb, I, H, b + off[0], b + off[1], gs + 0, s);
+    if (err == hipSuccess)
+      err = moe::launch_quantize_nvfp4(up, sb, I, H, b + off[2], b + off[3], gs + 1, s);
+    if (err == hipSuccess)
+      err = moe::launch_quantize_nvfp4(down, sb, H, I, b + off[4], b + off[5], gs + 2, s);
   } else {
     err = moe::launch_quantize_mxfp4(gate, sb, I, H, H, b + off[0], b + off[1], s);
     if (err == hipSuccess)

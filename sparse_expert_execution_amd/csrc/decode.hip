@@ -6,6 +6,7 @@ namespace moe {
 namespace dec {
 hipError_t launch_bf16(DecArgs& a, hipStream_t st);
 hipError_t launch_mxfp4(DecArgs& a, hipStream_t st);
+hipError_t launch_nvfp4(DecArgs& a, hipStream_t st);
 }  // namespace dec
 
 using namespace dec;
@@ -54,13 +55,15 @@ hipError_t launch_decode(const DecodeLaunch& f, hipStream_t st) {
   a.y = f.y;
   a.expert_bytes = f.expert_bytes;
   for (int i = 0; i < 6; ++i) a.off[i] = f.off[i];
+  a.goff = f.goff;
   a.T = f.T; a.H = f.H; a.I = f.I; a.E = f.E; a.k = f.k; a.renorm = f.renorm;
   a.route = f.w_router ? 1 : 0;
   const int epv = elems_per_vector(f.wtype);
   a.lx = (f.H / epv + 63) / 64;
   if (!down_map(f.I / epv, &a.lr, &a.nv)) return hipErrorInvalidValue;
   a.G = 0;
-  return f.wtype == 1 ? launch_bf16(a, st) : launch_mxfp4(a, st);
+  if (f.wtype == 1) return launch_bf16(a, st);
+  return f.wtype == 3 ? launch_nvfp4(a, st) : launch_mxfp4(a, st);
 }
 
 }  // namespace moe

@@ -94,6 +94,7 @@ struct DecArgs {
   float* y;                // [T][H]
   int64_t expert_bytes;
   int64_t off[6];
+  int64_t goff;            // NVFP4: offset of the gate, up, down fp32 scales
   int T, H, I, E, k, renorm;
   int G;                   // workgroups in the grid, all resident at once
   int route;               // 0: ids and w are inputs
@@ -727,7 +728,8 @@ __device__ void stage_x(const DecArgs& a, DecLds& S) {
 template <int LXC>
 struct GuBuf {
   uint4 g[LXC], u[LXC];
-  uint32_t gs[LXC], us[LXC];
+  uint32_t gs[LXC], us[LXC];   // MXFP4: e8m0 byte; NVFP4: two E4M3 bytes
+  float gg, ug;                // NVFP4: the matrices' fp32 scales
 };
 
 // row i of the gate and up matrices of the expert at base, this lane's vectors
@@ -745,13 +747,24 @@ __device__ __forceinline__ void gu_load(const DecArgs& a, const uint8_t* base, i
       if (WT == 1) {
         b.g[l] = ldg16(base + a.off[0] + ((int64_t)i * a.H + (int64_t)v * 8) * 2);
         b.u[l] = ldg16(base + a.off[1] + ((int64_t)i * a.H + (int64_t)v * 8) * 2);
-      } else {
+      } else if (WT == 2) {
         b.g[l] = ldg16(base + a.off[0] + (int64_t)i * (a.H / 2) + (int64_t)v * 16);
         b.u[l] = ldg16(base + a.off[2] + (int64_t)i * (a.H / 2) + (int64_t)v * 16);
         b.gs[l] = (base + a.off[1])[(int64_t)i * (a.H / 32) + v];
         b.us[l] = (base + a.off[3])[(int64_t)i * (a.H / 32) + v];
+      } else {
+        b.g[l] = ldg16(base + a.off[0] + (int64_t)i * (a.H / 2) + (int64_t)v * 16);
+        b.u[l] = ldg16(base + a.off[2] + (int64_t)i * (a.H / 2) + (int64_t)v * 16);
+        b.gs[l] = *reinterpret_cast<const uint16_t*>(base + a.off[1] +
+                                                     (int64_t)i * (a.H / 16) + 2 * v);
+        b.us[l] = *reinterpret_cast<const uint16_t*>(base + a.off[3] +
+                                                     (int64_t)i * (a.H / 16) + 2 * v);
       }
     }
+  }
+  if (WT == 3) {
+    b.gg = *reinterpret_cast<const float*>(base + a.goff);
+    b.ug = *reinterpret_cast<const float*>(base + a.goff + 4);
   }
 }
 
@@ -785,12 +798,24 @@ __device__ __forceinline__ float gu_dot(const DecArgs& a, const DecLds& S, const
         const uint4 t4 = S.g.xs[(t * CPV + c) * nvh + v];
         xp[4 * c] = t4.x; xp[4 * c + 1] = t4.y; xp[4 * c + 2] = t4.z; xp[4 * c + 3] = t4.w;
       }
-      gp = fmaf(dot_fp4_bf16_block(b.g[l], xp), e8m0_to_f32(b.gs[l]), gp);
-      up = fmaf(dot_fp4_bf16_block(b.u[l], xp), e8m0_to_f32(b.us[l]), up);
+      if (WT == 2) {
+        gp = fmaf(dot_fp4_bf16_block(b.g[l], xp), e8m0_to_f32(b.gs[l]), gp);
+        up = fmaf(dot_fp4_bf16_block(b.u[l], xp), e8m0_to_f32(b.us[l]), up);
+      } else {
+        float s0, s1;
+        dot_fp4_bf16_halves(b.g[l], xp, s0, s1);
+        gp = fmaf(s0, e4m3_to_f32(b.gs[l] & 0xffu), fmaf(s1, e4m3_to_f32(b.gs[l] >> 8), gp));
+        dot_fp4_bf16_halves(b.u[l], xp, s0, s1);
+        up = fmaf(s0, e4m3_to_f32(b.us[l] & 0xffu), fmaf(s1, e4m3_to_f32(b.us[l] >> 8), up));
+      }
     }
   }
-  const float gsum = wave_sum_dpp(gp);
-  const float usum = wave_sum_dpp(up);
+  float gsum = wave_sum_dpp(gp);
+  float usum = wave_sum_dpp(up);
+  if (WT == 3) {
+    gsum *= b.gg;
+    usum *= b.ug;
+  }
   return gsum / (1.0f + expf(-gsum)) * usum;
 }
 
@@ -904,7 +929,7 @@ struct DnCur {
   int s, ns;           // the step in it, its steps
   int e0, n;           // its entries
   int tokH[CE];        // token * H of each entry
-  float gw[CE];        // gate weight of each entry
+  float gw[CE];        // gate weight of each entry (NVFP4: times the down scale)
   const uint8_t* base; // the unit's weights
 };
 
@@ -926,6 +951,11 @@ __device__ __forceinline__ void dn_enter(const DecArgs& a, const DecLds& S, cons
     c.gw[i] = uni(S.p.ent_gw[en]);
   }
   c.base = unit_base(a, uni(S.p.unit_slot[uni(S.p.vu_unit[v])]));
+  if (a.goff > 0) {                          // NVFP4: fold the down matrix's scale in
+    const float gd = *reinterpret_cast<const float*>(c.base + a.goff + 8);
+#pragma unroll
+    for (int i = 0; i < CE; ++i) c.gw[i] *= gd;
+  }
 }
 
 // the segment holding row d (any row of the pass)
@@ -998,15 +1028,18 @@ __device__ __forceinline__ void dn_load(const DecArgs& a, const DnLane& L, const
       b.q[n] = ldg16(c.base + a.off[2] + ((int64_t)r * a.I + (int64_t)v * 8) * 2);
     } else {
       b.q[n] = ldg16(c.base + a.off[4] + (int64_t)r * (a.I / 2) + (int64_t)v * 16);
-      const int so = r * (a.I / 32) + v;
+      const int so = WT == 2 ? r * (a.I / 32) + v : r * (a.I / 16) + 2 * v;
       b.s[n] = *reinterpret_cast<const uint32_t*>(c.base + a.off[5] + (so & ~3));
     }
   }
 }
 
-// the scale byte of vector v of row r within its loaded word
+// the scale byte (MXFP4) or the two scale bytes (NVFP4) of vector v of row r
+// within its loaded word
+template <int WT>
 __device__ __forceinline__ uint32_t dn_scale(const DecArgs& a, int r, int v, uint32_t word) {
-  return (word >> (((r * (a.I / 32) + v) & 3) * 8)) & 0xffu;
+  if (WT == 2) return (word >> (((r * (a.I / 32) + v) & 3) * 8)) & 0xffu;
+  return (word >> (((r * (a.I / 16) + 2 * v) & 3) * 8)) & 0xffffu;
 }
 
 // y results of a wave to memory (fp32 atomics; index -1: none; an index past
@@ -1035,25 +1068,31 @@ __device__ __forceinline__ float wdot_h(const uint4 q, uint32_t sc, const float4
     s = fmaf(bf16_lo(q.w), h1.z, s);
     return fmaf(bf16_hi(q.w), h1.w, s);
   } else {
+    // MXFP4: one sum times the e8m0 scale; NVFP4: the two 16-element halves
+    // (words 0-1, 2-3) each times its E4M3 scale
     const uint32_t w[4] = {q.x, q.y, q.z, q.w};
-    float acc = 0.f;
+    float acc[2] = {0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
+      const int hx = WT == 2 ? 0 : i >> 1;
       const float4 ha = h4[2 * i], hc = h4[2 * i + 1];
       const v2f c0 = fp4x2_to_f32x2<0>(w[i]);
       const v2f c1 = fp4x2_to_f32x2<1>(w[i]);
       const v2f c2 = fp4x2_to_f32x2<2>(w[i]);
       const v2f c3 = fp4x2_to_f32x2<3>(w[i]);
-      acc = fmaf(c0.x, ha.x, acc);
-      acc = fmaf(c0.y, ha.y, acc);
-      acc = fmaf(c1.x, ha.z, acc);
-      acc = fmaf(c1.y, ha.w, acc);
-      acc = fmaf(c2.x, hc.x, acc);
-      acc = fmaf(c2.y, hc.y, acc);
-      acc = fmaf(c3.x, hc.z, acc);
-      acc = fmaf(c3.y, hc.w, acc);
+      float a = acc[hx];
+      a = fmaf(c0.x, ha.x, a);
+      a = fmaf(c0.y, ha.y, a);
+      a = fmaf(c1.x, ha.z, a);
+      a = fmaf(c1.y, ha.w, a);
+      a = fmaf(c2.x, hc.x, a);
+      a = fmaf(c2.y, hc.y, a);
+      a = fmaf(c3.x, hc.z, a);
+      a = fmaf(c3.y, hc.w, a);
+      acc[hx] = a;
     }
-    return acc * e8m0_to_f32(sc);
+    if (WT == 2) return acc[0] * e8m0_to_f32(sc);
+    return fmaf(acc[0], e4m3_to_f32(sc & 0xffu), acc[1] * e4m3_to_f32(sc >> 8));
   }
 }
 
@@ -1104,7 +1143,7 @@ __device__ __forceinline__ void dn_compute(const DecArgs& a, const DecLds& S, co
   uint32_t sc[NVC];
 #pragma unroll
   for (int nn = 0; nn < NVC; ++nn)
-    sc[nn] = WT == 1 ? 0u : dn_scale(a, r, L.j + (nn < a.nv ? a.lr * nn : 0), b.s[nn]);
+    sc[nn] = WT == 1 ? 0u : dn_scale<WT>(a, r, L.j + (nn < a.nv ? a.lr * nn : 0), b.s[nn]);
 #pragma unroll
   for (int i = 0; i < CE; ++i) {
     if (i >= c.n) break;

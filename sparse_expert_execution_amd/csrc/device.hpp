@@ -47,6 +47,53 @@ __device__ __forceinline__ float e8m0_to_f32(uint32_t s) {
   return __uint_as_float(s << 23);
 }
 
+// OCP E4M3FN byte -> fp32 (bias 7; exponent 0: m * 2^-9; NaN codes are never
+// produced by the encoder and are not special-cased)
+__device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
+  const uint32_t e = (b >> 3) & 15u, m = b & 7u;
+  const float v = e == 0 ? (float)m * 0.001953125f : __uint_as_float(((e + 120u) << 23) | (m << 20));
+  return (b & 0x80u) ? -v : v;
+}
+
+// non-negative fp32 -> E4M3 code with round-to-nearest-even, saturating at
+// 448 (0x7E)
+__device__ __forceinline__ uint32_t e4m3_rne(float t) {
+  if (!(t < 448.f)) return 0x7Eu;
+  const uint32_t bits = __float_as_uint(t);
+  const int ex = (int)((bits >> 23) & 0xffu) - 127;
+  if (ex < -6) return (uint32_t)rintf(t * 512.f);      // subnormal steps of 2^-9
+  uint32_t m3 = (bits >> 20) & 7u;
+  const uint32_t rem = bits & 0xfffffu;
+  if (rem > 0x80000u || (rem == 0x80000u && (m3 & 1u))) ++m3;
+  const uint32_t code = ((uint32_t)(ex + 7) << 3) + m3;  // a mantissa carry bumps the exponent
+  return code > 0x7Eu ? 0x7Eu : code;
+}
+
+// sums over the two 16-element halves of one 16-byte e2m1 block times 32 bf16
+// x values (16 packed pairs), fp32 accumulation, no scale applied
+__device__ __forceinline__ void dot_fp4_bf16_halves(const uint4 q, const uint32_t* xp, float& s0,
+                                                    float& s1) {
+  float a0 = 0.f, a1 = 0.f;
+  a0 = dot2_bf16(fp4x2_to_bf16x2<0>(q.x), xp[0], a0);
+  a0 = dot2_bf16(fp4x2_to_bf16x2<1>(q.x), xp[1], a0);
+  a0 = dot2_bf16(fp4x2_to_bf16x2<2>(q.x), xp[2], a0);
+  a0 = dot2_bf16(fp4x2_to_bf16x2<3>(q.x), xp[3], a0);
+  a0 = dot2_bf16(fp4x2_to_bf16x2<0>(q.y), xp[4], a0);
+  a0 = dot2_bf16(fp4x2_to_bf16x2<1>(q.y), xp[5], a0);
+  a0 = dot2_bf16(fp4x2_to_bf16x2<2>(q.y), xp[6], a0);
+  a0 = dot2_bf16(fp4x2_to_bf16x2<3>(q.y), xp[7], a0);
+  a1 = dot2_bf16(fp4x2_to_bf16x2<0>(q.z), xp[8], a1);
+  a1 = dot2_bf16(fp4x2_to_bf16x2<1>(q.z), xp[9], a1);
+  a1 = dot2_bf16(fp4x2_to_bf16x2<2>(q.z), xp[10], a1);
+  a1 = dot2_bf16(fp4x2_to_bf16x2<3>(q.z), xp[11], a1);
+  a1 = dot2_bf16(fp4x2_to_bf16x2<0>(q.w), xp[12], a1);
+  a1 = dot2_bf16(fp4x2_to_bf16x2<1>(q.w), xp[13], a1);
+  a1 = dot2_bf16(fp4x2_to_bf16x2<2>(q.w), xp[14], a1);
+  a1 = dot2_bf16(fp4x2_to_bf16x2<3>(q.w), xp[15], a1);
+  s0 = a0;
+  s1 = a1;
+}
+
 // sum over the 32 e2m1 values of one 16-byte block times 32 bf16 x values
 // (x given as 16 packed bf16 pairs), fp32 accumulation, no scale applied.
 __device__ __forceinline__ float dot_fp4_bf16_block(const uint4 q, const uint32_t* xp) {

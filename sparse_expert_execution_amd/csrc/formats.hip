@@ -58,6 +58,67 @@ __global__ __launch_bounds__(256) void quantize_kernel(const void* __restrict__ 
   scales[r * nb + b] = (uint8_t)sbyte;
 }
 
+// ---- NVFP4: e2m1 elements, an E4M3 scale per 16, an fp32 scale per matrix.
+// The steps follow the encoder's fp32 definition: g = amax / 2688 (1 for a
+// zero matrix); per block t = amax_b / (6 g) rounded to E4M3 (nearest even,
+// saturating); d = E4M3(t) * g; codes = e2m1(v / d), all 0 when d = 0.
+__device__ __forceinline__ float load_elem(const void* src, int src_bf16, int64_t i) {
+  return src_bf16 ? __uint_as_float((uint32_t)static_cast<const uint16_t*>(src)[i] << 16)
+                  : static_cast<const float*>(src)[i];
+}
+
+__global__ void nvfp4_clear_kernel(float* slot) { *slot = 0.f; }
+
+// matrix amax into *slot (fp32 bits compare like unsigned ints when >= 0)
+__global__ __launch_bounds__(256) void nvfp4_amax_kernel(const void* __restrict__ src,
+                                                         int src_bf16, int64_t n, float* slot) {
+  __shared__ float red[256];
+  float m = 0.f;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
+    m = fmaxf(m, fabsf(load_elem(src, src_bf16, i)));
+  red[threadIdx.x] = m;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if ((int)threadIdx.x < w) red[threadIdx.x] = fmaxf(red[threadIdx.x], red[threadIdx.x + w]);
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) atomicMax(reinterpret_cast<unsigned int*>(slot), __float_as_uint(red[0]));
+}
+
+__device__ __forceinline__ float nvfp4_global(float amax) { return amax > 0.f ? amax / 2688.f : 1.f; }
+
+// one thread per 16-element block
+__global__ __launch_bounds__(256) void nvfp4_quant_kernel(const void* __restrict__ src,
+                                                          int src_bf16, int rows, int K,
+                                                          uint8_t* __restrict__ codes,
+                                                          uint8_t* __restrict__ scales,
+                                                          const float* __restrict__ amax_slot) {
+  const int nb = K / 16;
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid >= (int64_t)rows * nb) return;
+  const int64_t r = gid / nb;
+  const int b = (int)(gid % nb);
+  const float g = nvfp4_global(*amax_slot);
+  float v[16];
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    v[i] = load_elem(src, src_bf16, r * K + (int64_t)b * 16 + i);
+    amax = fmaxf(amax, fabsf(v[i]));
+  }
+  const uint32_t sbyte = e4m3_rne(amax / (6.f * g));
+  const float d = e4m3_to_f32(sbyte) * g;
+  uint32_t packed[2] = {0, 0};
+  if (d > 0.f) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) packed[i / 8] |= e2m1_code(v[i] / d) << (4 * (i % 8));
+  }
+  *reinterpret_cast<uint2*>(codes + r * (K / 2) + (int64_t)b * 8) = make_uint2(packed[0], packed[1]);
+  scales[r * nb + b] = (uint8_t)sbyte;
+}
+
+__global__ void nvfp4_final_kernel(float* slot) { *slot = nvfp4_global(*slot); }
+
 // fp32 -> bf16, round to nearest even (NaN stays a quiet NaN)
 __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
   const uint32_t u = __float_as_uint(f);
@@ -147,6 +208,21 @@ __global__ void fill_i32_kernel(int32_t* dst, int32_t value, int64_t n) {
 }
 
 }  // namespace
+
+hipError_t launch_quantize_nvfp4(const void* src, int src_bf16, int rows, int K, uint8_t* codes,
+                                 uint8_t* scales, float* g, hipStream_t st) {
+  if (rows <= 0 || K <= 0 || K % 16) return hipErrorInvalidValue;
+  const int64_t n = (int64_t)rows * K;
+  hipLaunchKernelGGL(nvfp4_clear_kernel, dim3(1), dim3(1), 0, st, g);
+  const int64_t blocks = (n + 256 * 16 - 1) / (256 * 16);
+  hipLaunchKernelGGL(nvfp4_amax_kernel, dim3((unsigned)(blocks < 2048 ? blocks : 2048)), dim3(256),
+                     0, st, src, src_bf16, n, g);
+  const int64_t nb = (int64_t)rows * (K / 16);
+  hipLaunchKernelGGL(nvfp4_quant_kernel, dim3((unsigned)((nb + 255) / 256)), dim3(256), 0, st, src,
+                     src_bf16, rows, K, codes, scales, g);
+  hipLaunchKernelGGL(nvfp4_final_kernel, dim3(1), dim3(1), 0, st, g);
+  return hipGetLastError();
+}
 
 hipError_t launch_quantize_mxfp4(const void* src, int src_bf16, int rows, int K, int64_t ld,
                                  uint8_t* codes, uint8_t* scales, hipStream_t st) {

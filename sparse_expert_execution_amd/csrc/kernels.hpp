@@ -22,6 +22,7 @@ struct DecodeLaunch {
   float* y;
   int64_t expert_bytes;
   int64_t off[6];
+  int64_t goff;           // NVFP4: offset of the three fp32 matrix scales, else 0
   int T, H, I, E, k, wtype;
 };
 
@@ -77,6 +78,9 @@ hipError_t launch_prefill(const PrefillLaunch& p, hipStream_t st);
 // formats / merge
 hipError_t launch_quantize_mxfp4(const void* src, int src_bf16, int rows, int K, int64_t ld,
                                  uint8_t* codes, uint8_t* scales, hipStream_t st);
+// NVFP4: codes [rows][K/2], E4M3 scales [rows][K/16], fp32 matrix scale at g
+hipError_t launch_quantize_nvfp4(const void* src, int src_bf16, int rows, int K, uint8_t* codes,
+                                 uint8_t* scales, float* g, hipStream_t st);
 hipError_t launch_pack_bf16(const void* src, int src_bf16, int rows, int K, uint16_t* dst,
                             hipStream_t st);
 hipError_t launch_dequant_mxfp4(const uint8_t* codes, const uint8_t* scales,

@@ -23,7 +23,7 @@ def _stream(stream=None):
 
 def make_desc(hidden, inter, n_experts, top_k, has_shared=False, renorm=False,
               wtype="mxfp4", router_wtype="bf16"):
-    wt = {"bf16": _lib.WTYPE_BF16, "mxfp4": _lib.WTYPE_MXFP4}[wtype]
+    wt = {"bf16": _lib.WTYPE_BF16, "mxfp4": _lib.WTYPE_MXFP4, "nvfp4": _lib.WTYPE_NVFP4}[wtype]
     rt = {"f32": _lib.WTYPE_F32, "bf16": _lib.WTYPE_BF16}[router_wtype]
     return MoeDesc(hidden, inter, n_experts, top_k, int(has_shared), int(renorm), wt, rt)
 

@@ -72,6 +72,8 @@ def oracle_weights(name, layer, e, wtype, seed=0):
             out.append(formats.bf16_decode(formats.bf16_round(a)))
         elif wtype == "mxfp4":
             out.append(formats.mxfp4_decode(*formats.mxfp4_encode(a)))
+        elif wtype == "nvfp4":
+            out.append(formats.nvfp4_decode(*formats.nvfp4_encode(a)))
         else:
             out.append(a.astype(np.float64))
     return tuple(out)

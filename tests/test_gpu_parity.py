@@ -13,7 +13,7 @@ import pytest
 import torch
 
 import synth
-from helpers import GpuLayer, bf16_to_f64, oracle_router, oracle_weights
+from helpers import GpuLayer, bf16_to_f64, desc_for, oracle_router, oracle_weights
 from oracle import cache as ocache
 from oracle import formats, layer as olayer
 
@@ -81,6 +81,52 @@ def test_quantize_bit_exact(ops):
         rc, rs = formats.mxfp4_encode(a.astype(np.float64))
         assert np.array_equal(s.cpu().numpy(), rs)
         assert np.array_equal(c.cpu().numpy(), rc)
+
+
+def _nvfp4_sections(ops, desc, blk):
+    """(codes, scales, g) of gate, up and down from a packed NVFP4 block."""
+    off, _ = ops.expert_layout(desc)
+    H, I = desc.hidden, desc.inter
+    b = blk.cpu().numpy()
+    gs = b[off[5] + H * I // 16:off[5] + H * I // 16 + 12].view(np.float32)
+    out = []
+    for m, (rows, K) in enumerate([(I, H), (I, H), (H, I)]):
+        c = b[off[2 * m]:off[2 * m] + rows * K // 2].reshape(rows, K // 2)
+        sc = b[off[2 * m + 1]:off[2 * m + 1] + rows * K // 16].reshape(rows, K // 16)
+        out.append((c, sc, gs[m]))
+    return out
+
+
+def test_nvfp4_pack_bit_exact(ops):
+    """moe_pack_expert with NVFP4 weights against the oracle encoder: codes,
+    E4M3 scales and the fp32 matrix scales, byte for byte (edge-case rows in
+    the gate matrix, synthetic experts of two shapes)."""
+    _say("nvfp4 pack")
+    rng = np.random.default_rng(13)
+    cases = []
+    gate = (rng.standard_normal((128, 256)) * 0.02).astype(np.float32)
+    edge = _encode_cases()
+    gate[:edge.shape[0]] = edge[:, :256]
+    gate[-1, :16] = 0.0                                   # an all-zero block
+    cases.append(("tiny", [torch.from_numpy(gate).cuda(),
+                           torch.from_numpy((rng.standard_normal((128, 256)) * 3).astype(
+                               np.float32)).cuda(),
+                           torch.from_numpy((rng.standard_normal((256, 128)) * 1e-3).astype(
+                               np.float32)).cuda()]))
+    cases.append(("dsv4_mxfp4_decode",
+                  list(synth.expert_weights("dsv4_mxfp4_decode", 0, 5, device="cuda",
+                                            as_dtype=torch.float32))))
+    for name, mats in cases:
+        desc = desc_for(name, "nvfp4")
+        _, eb = ops.expert_layout(desc)
+        blk = torch.zeros(eb, dtype=torch.uint8, device="cuda")
+        ops.pack_expert(desc, blk, *mats)
+        torch.cuda.synchronize()
+        for m, (c, sc, g) in zip(mats, _nvfp4_sections(ops, desc, blk)):
+            rc, rs, rg = formats.nvfp4_encode(m.cpu().numpy())
+            assert np.float32(g).tobytes() == np.float32(rg).tobytes(), name
+            assert np.array_equal(sc, rs), name
+            assert np.array_equal(c, rc), name
 
 
 def test_merge_exact(ops):
@@ -315,7 +361,10 @@ def _check_ids(L, x, gi, gw, renorm=False):
                                           ("qwen_bf16_decode", 16, None),
                                           ("ragged_decode", 3, None),
                                           ("ragged_decode", 9, None),
-                                          ("glm_cache_decode", 1, None)])
+                                          ("glm_cache_decode", 1, None),
+                                          ("tiny", 4, "nvfp4"),
+                                          ("ragged_decode", 9, "nvfp4"),
+                                          ("qwen_bf16_decode", 4, "nvfp4")])
 def test_route_decode(ops, name, T, wtype):
     """Router + experts + combine in one call (one persistent kernel for T <= 4)."""
     _say("route_decode", name, T, wtype)
@@ -354,6 +403,29 @@ def test_route_decode_dsv4_full_sampled(ops, T, sample):
     ref = _oracle_out(L, x, gi, gw, tokens=sample)
     assert olayer.row_rel_error(y.cpu().numpy()[sample], ref) < TOL
     assert _counters_clear(ws, _launches(L, T))
+
+
+def test_route_decode_dsv4_nvfp4_sampled(ops):
+    """DeepSeek-shaped layer with NVFP4 experts (and the shared expert), one
+    token: router + experts + combine against the oracle."""
+    _say("route_decode dsv4 nvfp4")
+    L = GpuLayer("dsv4_mxfp4_decode", layer=3, wtype="nvfp4")
+    x = L.tokens(1)
+    ids, w, y, ws = _route_decode(ops, L, x)
+    gi, gw = ids.cpu().numpy(), w.cpu().numpy()
+    _check_ids(L, x, gi, gw)
+    ref = _oracle_out(L, x, gi, gw)
+    assert olayer.row_rel_error(y.cpu().numpy(), ref) < TOL
+
+
+def test_nvfp4_prefill_unsupported(ops):
+    L = GpuLayer("tiny", wtype="nvfp4")
+    x = L.tokens(4)
+    ids, w = _route_gpu(ops, L, x)
+    y = torch.empty((4, L.s["hidden"]), dtype=torch.float32, device="cuda")
+    with pytest.raises(ops._lib.MoeError) as ei:
+        ops.prefill(L.desc, x, ids, w, L.pool, y, ops.workspace(L.desc, 4, 2))
+    assert ei.value.status == ops._lib.MOE_EUNSUPPORTED
 
 
 def test_route_decode_partial_subset(ops):

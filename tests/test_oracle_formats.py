@@ -145,3 +145,68 @@ def test_bf16_decode_exact():
     ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
     ok = ~np.isnan(ref)
     assert np.array_equal(vals[ok], ref[ok])
+
+
+# ------------------------------------------------------------------ NVFP4
+def test_e4m3_decode_matches_torch_float8_all_codes():
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).float().numpy().astype(np.float64)
+    got = formats.e4m3_decode(codes)
+    assert np.array_equal(np.isnan(ref), np.isnan(got))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(ref[ok], got[ok])
+    assert got[0x7E] == 448.0 and got[0x01] == 2.0 ** -9 and got[0x08] == 2.0 ** -6
+
+
+def test_e4m3_round_matches_torch_cast_with_ties():
+    rng = np.random.default_rng(11)
+    mags = formats.e4m3_decode(np.arange(127))
+    mids = ((mags[:-1] + mags[1:]) / 2).astype(np.float32)   # every tie
+    t = np.concatenate([rng.uniform(0, 448, 50000), rng.uniform(0, 0.05, 50000),
+                        mids, mags.astype(np.float32)]).astype(np.float32)
+    ref = torch.from_numpy(t).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(formats.e4m3_round(t.astype(np.float64)), ref)
+    assert formats.e4m3_round(np.array([1000.0]))[0] == 0x7E      # saturation
+
+
+def _nearest_e2m1_brute(q):
+    """Nearest e2m1 magnitude by exhaustive search, ties to the even code."""
+    grid = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+    out = np.empty(q.shape, dtype=np.uint8)
+    for i, x in np.ndenumerate(q):
+        a = min(abs(float(x)), 6.0)
+        best = min(range(8), key=lambda c: (abs(a - grid[c]), c & 1))
+        out[i] = best | (8 if np.signbit(x) else 0)
+    return out
+
+
+def test_nvfp4_steps_and_nearest_codes():
+    rng = np.random.default_rng(12)
+    v = (rng.normal(0, 0.02, (8, 64)) * rng.uniform(0.1, 10, (8, 1))).astype(np.float32)
+    codes_u8, scales, g = formats.nvfp4_encode(v)
+    assert g == np.float32(np.float32(np.abs(v).max()) / np.float32(2688.0))
+    blocks = v.reshape(8, 4, 16)
+    amax_b = np.abs(blocks).max(-1).astype(np.float32)
+    t = (amax_b / np.float32(np.float32(6.0) * g)).astype(np.float32)
+    ref_s = torch.from_numpy(t).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(scales, ref_s)
+    d = (formats.e4m3_decode(scales).astype(np.float32) * g).astype(np.float32)
+    q = (blocks / d[..., None]).astype(np.float32)
+    codes = formats.unpack_nibbles(codes_u8).reshape(8, 4, 16)
+    assert np.array_equal(codes, _nearest_e2m1_brute(q))
+    # values are e2m1 * scale * g
+    dec = formats.nvfp4_decode(codes_u8, scales, g)
+    ref = formats.e2m1_decode(codes.reshape(8, 64)) * np.repeat(
+        formats.e4m3_decode(scales), 16, axis=1) * float(g)
+    assert np.array_equal(dec, ref)
+
+
+def test_nvfp4_zero_and_on_grid_round_trip():
+    codes_u8, scales, g = formats.nvfp4_encode(np.zeros((2, 32), np.float32))
+    assert g == 1.0 and not scales.any() and not codes_u8.any()
+    # a block holding +-6, 4, ... at scale 1 with the matrix max 6 * 448 * g
+    grid = np.array([6, -6, 4, -4, 3, 2, 1.5, 1, 0.5, 0, -0.5, -1, -1.5, -2, -3, 6],
+                    np.float32)
+    v = np.stack([grid * np.float32(448.0), grid]).astype(np.float32)   # two rows
+    codes_u8, scales, g = formats.nvfp4_encode(v)
+    assert np.array_equal(formats.nvfp4_decode(codes_u8, scales, g), v.astype(np.float64))
