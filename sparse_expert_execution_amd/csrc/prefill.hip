@@ -230,9 +230,14 @@ __device__ __forceinline__ int pair_token(const GemmArgs& a, int p) {
 // global memory straight into LDS (global_load_lds, 16 bytes a lane) in
 // fragment order: for each 16-row slice, lane l's 16 bytes are row l % 16,
 // K block l / 16, exactly what the lane feeds the MFMA, so a fragment is one
-// conflict-free 16-byte LDS read.  Scale bytes go to LDS as one dword (the
-// step's 4 K blocks) per row.  kStages - 1 steps are in flight (about 100 KB
-// per CU, one workgroup per CU); each step lives in its own LDS variable.  8
+// conflict-free 16-byte LDS read.  Scale bytes: when K is a multiple of 512
+// (SG), each row's 16 scale bytes of four steps are copied at once, one
+// 16-byte copy per row every fourth step into a double-buffered scale group;
+// otherwise one dword (the step's 4 K blocks) per row and step.  A copy that
+// serves 64 rows touches 64 cache lines, so grouping the scales cuts the
+// tile's line requests several-fold.  kStages - 1 steps are in flight (about
+// 100 KB per CU, one workgroup per CU); each step lives in its own LDS
+// variable.  8
 // waves (two per SIMD, so one's matrix work covers the other's LDS waits) as
 // 2 (64 rows) x 4 (64 B rows); a wave holds 4 x 4 16x16 accumulators.
 //   GEMM1: A = MXFP4(x) rows gathered by token, B = [gate rows c0..c0+127 ;
@@ -243,11 +248,18 @@ constexpr int kBM = 128, kBN = 256;
 constexpr int kGemmThreads = 512;   // 8 waves, two per SIMD
 constexpr int kStages = 5;
 
+template <bool SG>
 struct Stage {
   uint4 a[(kBM / 16) * 64];         // 8 slices x 64 lanes x 16 bytes
   uint4 b[(kBN / 16) * 64];         // 16 slices
-  uint32_t as[kBM];                 // 4 scale bytes (the step's K blocks) per row
-  uint32_t bs[kBN];
+  uint32_t as[SG ? 1 : kBM];        // 4 scale bytes (the step's K blocks) per row
+  uint32_t bs[SG ? 1 : kBN];
+};
+// scale bytes of four consecutive steps (16 K blocks) per row
+template <bool SG>
+struct ScaleGroup {
+  uint4 as[SG ? kBM : 1];
+  uint4 bs[SG ? kBN : 1];
 };
 
 __device__ __forceinline__ void dma16(const void* g, void* lds) {
@@ -285,9 +297,11 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)p;
 }
 
-template <int MODE>
+template <int MODE, bool SG>
 __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(GemmArgs a) {
+  using Stage = moe::Stage<SG>;
   __shared__ Stage st0, st1, st2, st3, st4;
+  __shared__ ScaleGroup<SG> sg0, sg1;
   auto stage = [&](int s) -> Stage& {
     return s == 0 ? st0 : (s == 1 ? st1 : (s == 2 ? st2 : (s == 3 ? st3 : st4)));
   };
@@ -314,8 +328,10 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(GemmArgs a) {
   const int wm = wv & 1, wn = wv >> 1;         // 2 (64 rows) x 4 (64 B rows)
   const int fr = lane & 15, fk = lane >> 4;
 
-  // copy sources of this lane: A slice wv; B slices 2 wv, 2 wv + 1; scale
-  // dwords of A rows 64 (wv & 1) + lane and of B rows 64 (wv & 3) + lane
+  // copy sources of this lane: A slice wv; B slices 2 wv, 2 wv + 1; scales:
+  // SG: waves 0-1 A rows 64 wv + lane, waves 2-5 B rows 64 (wv - 2) + lane,
+  // waves 6-7 none; else dwords of A rows 64 (wv & 1) + lane and of B rows
+  // 64 (wv & 3) + lane
   auto a_row_ptrs = [&](int r, const uint8_t*& c, const uint8_t*& sc) {
     const bool ok = r < seg_end;
     const int rr = ok ? r : row0;
@@ -347,21 +363,39 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(GemmArgs a) {
 #pragma unroll
     for (int j = 0; j < 2; ++j) b_row_ptrs((2 * wv + j) * 16 + fr, bc[j], dummy);
     const uint8_t* c;
-    a_row_ptrs(row0 + (wv & 1) * 64 + lane, c, as_src);
-    b_row_ptrs((wv & 3) * 64 + lane, c, bs_src);
+    if constexpr (SG) {
+      as_src = bs_src = nullptr;
+      if (wv < 2) a_row_ptrs(row0 + wv * 64 + lane, c, as_src);
+      else if (wv < 6) b_row_ptrs((wv - 2) * 64 + lane, c, bs_src);
+    } else {
+      a_row_ptrs(row0 + (wv & 1) * 64 + lane, c, as_src);
+      b_row_ptrs((wv & 3) * 64 + lane, c, bs_src);
+    }
   }
-  // every wave issues the same number of copies per step (5), so one count
-  // covers all: the scale dwords are copied by several waves (the same bytes
-  // to the same place)
-  auto issue = [&](int kt, Stage& S) {
+  // Without SG every wave issues the same number of copies per step (5), so
+  // one count covers all: the scale dwords are copied by several waves (the
+  // same bytes to the same place).  With SG a wave issues 3 code copies per
+  // step, and waves 0-5 one scale copy ahead of the codes of a group's first
+  // step (real steps only): the codes' count then covers it, since copies
+  // complete in issue order.
+  auto issue = [&](int kt, Stage& S, bool real) {
     const int k0 = kt * 128;
+    if constexpr (SG) {
+      if (real && (kt & 3) == 0 && wv < 6) {
+        ScaleGroup<SG>& G = ((kt >> 2) & 1) ? sg1 : sg0;
+        if (wv < 2) dma16(as_src + (kt >> 2) * 16, &G.as[wv * 64]);
+        else dma16(bs_src + (kt >> 2) * 16, &G.bs[(wv - 2) * 64]);
+      }
+    }
     dma16(ac[0] + k0 / 2 + fk * 16, &S.a[wv * 64]);
 #pragma unroll
     for (int j = 0; j < 2; ++j) dma16(bc[j] + k0 / 2 + fk * 16, &S.b[(2 * wv + j) * 64]);
-    dma4(as_src + k0 / 32, &S.as[(wv & 1) * 64]);
-    dma4(bs_src + k0 / 32, &S.bs[(wv & 3) * 64]);
+    if constexpr (!SG) {
+      dma4(as_src + k0 / 32, &S.as[(wv & 1) * 64]);
+      dma4(bs_src + k0 / 32, &S.bs[(wv & 3) * 64]);
+    }
   };
-  constexpr int kCopies = 5;                   // copies per wave per step
+  constexpr int kCopies = SG ? 3 : 5;          // copies per wave per step (codes, scales)
 
   v4f acc[4][4];
 #pragma unroll
@@ -369,7 +403,19 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(GemmArgs a) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  auto compute = [&](const Stage& S) {
+  // LDS byte address of row 0's scale dword of step kt
+  auto scale_base = [&](const Stage& S, int kt, bool b_side) -> uint32_t {
+    if constexpr (SG) {
+      const ScaleGroup<SG>& G = ((kt >> 2) & 1) ? sg1 : sg0;
+      return (b_side ? lds_addr(&G.bs[0]) : lds_addr(&G.as[0])) + (kt & 3) * 4;
+    } else {
+      return b_side ? lds_addr(&S.bs[0]) : lds_addr(&S.as[0]);
+    }
+  };
+  constexpr uint32_t kScaleRowBytes = SG ? 16 : 4;
+
+  auto compute = [&](const Stage& S, int kt) {
+    const uint32_t asb = scale_base(S, kt, false), bsb = scale_base(S, kt, true);
     Frag fa[4];
     {
       uint32_t qa[4], sa[4], sc[4];
@@ -378,7 +424,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(GemmArgs a) {
       for (int ms = 0; ms < 4; ++ms) {
         const int sl = wm * 4 + ms;
         qa[ms] = lds_addr(&S.a[sl * 64 + lane]);
-        sa[ms] = lds_addr(&S.as[sl * 16 + fr]);
+        sa[ms] = asb + (sl * 16 + fr) * kScaleRowBytes;
       }
       lds_frag4(qa, sa, q, sc);
 #pragma unroll
@@ -396,7 +442,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(GemmArgs a) {
         // each (n-slices 0, 1 gate and 2, 3 up)
         const int sl = MODE == 1 ? (ns >> 1) * 8 + wn * 2 + (ns & 1) : wn * 4 + ns;
         qa[ns] = lds_addr(&S.b[sl * 64 + lane]);
-        sa[ns] = lds_addr(&S.bs[sl * 16 + fr]);
+        sa[ns] = bsb + (sl * 16 + fr) * kScaleRowBytes;
       }
       lds_frag4(qa, sa, q, sc);
 #pragma unroll
@@ -413,7 +459,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(GemmArgs a) {
   const int nk = K / 128;
   // prologue: steps 0 .. kStages-2 (a step past the end re-reads the last)
 #pragma unroll
-  for (int s = 0; s < kStages - 1; ++s) issue(s < nk ? s : nk - 1, stage(s));
+  for (int s = 0; s < kStages - 1; ++s) issue(s < nk ? s : nk - 1, stage(s), s < nk);
   for (int kt0 = 0; kt0 < nk; kt0 += kStages) {
 #pragma unroll
     for (int s = 0; s < kStages; ++s) {
@@ -425,8 +471,8 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(GemmArgs a) {
         asm volatile("s_waitcnt vmcnt(%0)" ::"n"((kStages - 2) * kCopies) : "memory");
         __builtin_amdgcn_s_barrier();
         const int kn = kt + kStages - 1;
-        issue(kn < nk ? kn : nk - 1, stage((s + kStages - 1) % kStages));
-        compute(stage(s));
+        issue(kn < nk ? kn : nk - 1, stage((s + kStages - 1) % kStages), kn < nk);
+        compute(stage(s), kt);
       }
     }
   }
@@ -581,9 +627,20 @@ hipError_t launch_prefill(const PrefillLaunch& p, hipStream_t st) {
   {
     const int groups = (p.max_tiles + 7) / 8;
     const int nt1 = p.I / (kBN / 2), nt2 = (p.H + kBN - 1) / kBN;
-    hipLaunchKernelGGL(gemm_kernel<1>, dim3(groups * 8 * nt1), dim3(kGemmThreads), 0, st, g);
+    // K a multiple of 512: scales copied four steps at a time
+    if (p.H % 512 == 0)
+      hipLaunchKernelGGL((gemm_kernel<1, true>), dim3(groups * 8 * nt1), dim3(kGemmThreads), 0,
+                         st, g);
+    else
+      hipLaunchKernelGGL((gemm_kernel<1, false>), dim3(groups * 8 * nt1), dim3(kGemmThreads), 0,
+                         st, g);
     if ((err = hipGetLastError()) != hipSuccess) return err;
-    hipLaunchKernelGGL(gemm_kernel<2>, dim3(groups * 8 * nt2), dim3(kGemmThreads), 0, st, g);
+    if (p.I % 512 == 0)
+      hipLaunchKernelGGL((gemm_kernel<2, true>), dim3(groups * 8 * nt2), dim3(kGemmThreads), 0,
+                         st, g);
+    else
+      hipLaunchKernelGGL((gemm_kernel<2, false>), dim3(groups * 8 * nt2), dim3(kGemmThreads), 0,
+                         st, g);
   }
   if ((err = hipGetLastError()) != hipSuccess) return err;
   {

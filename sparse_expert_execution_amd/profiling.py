@@ -11,7 +11,8 @@
     python -m sparse_expert_execution_amd.profiling run-prefill <workload>
         [--tokens T] [--calls N]
         Builds one synthetic layer (every expert resident) and makes N
-        moe_route + moe_prefill calls over T tokens, for a kernel trace.
+        moe_route + moe_prefill calls over T tokens, then the same two
+        calibration launches, for a kernel trace or the counters.
 
     python -m sparse_expert_execution_amd.profiling summarize --name NAME
         --stats run_kernel_stats.csv --fetch fetch.csv --write write.csv
@@ -20,7 +21,8 @@
         profiles/NAME.traffic.json (HBM bytes per decode launch, scaled by the
         calibration, with a hash of the kernel sources it was taken on).
 
-The traffic is per launch of the decode kernel: FETCH_SIZE and WRITE_SIZE are
+The traffic is per launch of the kernel named by --kernel (the decode kernel
+by default); every kernel of the run gets a row of its own.  FETCH_SIZE and WRITE_SIZE are
 KiB per dispatch summed over the L2 channels; each is multiplied by
 known_bytes / (counter * 1024) of its calibration kernel.
 """
@@ -35,6 +37,7 @@ import sys
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 DECODE_SOURCES = ["decode_impl.hpp", "decode_launch.hpp", "decode.hip", "decode_bf16.hip",
                   "decode_mxfp4.hip", "device.hpp"]
+PREFILL_SOURCES = ["prefill.hip", "device.hpp"]
 PROBE_BYTES = 256 << 20
 COPY_BYTES = 256 << 20
 
@@ -78,7 +81,13 @@ def cmd_run(args):
         pool, sh, wr, x = layers[c % len(layers)]
         ops.route_decode(desc, x, wr, ids, w, pool, y, ws, shared=sh)
     torch.cuda.synchronize()
-    # calibration: a read of PROBE_BYTES, a copy writing COPY_BYTES
+    _calibrate(torch, ops)
+    print(f"profiling run: {args.calls} decode calls of {args.workload} T={T}, probe "
+          f"{PROBE_BYTES} B, copy {COPY_BYTES} B", flush=True)
+
+
+def _calibrate(torch, ops):
+    """A read of PROBE_BYTES and a copy writing COPY_BYTES, for the counters."""
     buf = torch.empty(PROBE_BYTES, dtype=torch.uint8, device="cuda")
     buf.fill_(1)
     out = torch.zeros(1, dtype=torch.int32, device="cuda")
@@ -89,8 +98,6 @@ def cmd_run(args):
     torch.cuda.synchronize()
     dst.copy_(src)
     torch.cuda.synchronize()
-    print(f"profiling run: {args.calls} decode calls of {args.workload} T={T}, probe "
-          f"{PROBE_BYTES} B, copy {COPY_BYTES} B", flush=True)
 
 
 def cmd_run_prefill(args):
@@ -123,6 +130,7 @@ def cmd_run_prefill(args):
         ops.route(desc, x, wr, ids, w, rws)
         ops.prefill(desc, x, ids, w, pool, y, ws, shared=sh)
     torch.cuda.synchronize()
+    _calibrate(torch, ops)
     print(f"profiling run: {args.calls} route + prefill calls of {args.workload} T={T}",
           flush=True)
 
@@ -163,7 +171,7 @@ def cmd_summarize(args):
         return
     fetch = _counter_rows(args.fetch, "FETCH_SIZE")
     write = _counter_rows(args.write, "WRITE_SIZE")
-    dec = lambda n: "decode_kernel" in n
+    dec = lambda n: args.kernel in n
     probe = lambda n: "read_probe" in n
     copy = lambda n: "copy" in n.lower() or "elementwise" in n.lower()
     f_dec = _mean([v for n, v in fetch if dec(n)])
@@ -175,7 +183,8 @@ def cmd_summarize(args):
     fetch_b = f_dec * 1024 * f_scale if f_dec and f_scale else None
     write_b = w_dec * 1024 * w_scale if w_dec is not None and w_scale else None
     total = (fetch_b or 0) + (write_b or 0) if fetch_b is not None else None
-    rec = {"name": args.name, "source_hash": source_hash(),
+    sources = DECODE_SOURCES if "decode" in args.kernel else PREFILL_SOURCES
+    rec = {"name": args.name, "kernel": args.kernel, "source_hash": source_hash(sources),
            "bytes_per_launch": total, "fetch_bytes_per_launch": fetch_b,
            "write_bytes_per_launch": write_b, "alg_bytes_per_launch": args.alg_bytes,
            "fetch_scale": f_scale, "write_scale": w_scale,
@@ -187,14 +196,24 @@ def cmd_summarize(args):
         json.dump(rec, f, indent=1)
     lines = [f"# {args.name}", "", "Kernel trace (rocprofv3 --kernel-trace --stats):", "",
              f"    {args.cmd_stats}", ""] + _stats_table(stats)
-    lines += ["", "HBM traffic of the decode kernel (rocprofv3 --pmc, one counter per run):", "",
+    per = []
+    for name in sorted({n for n, _ in fetch if not probe(n) and not copy(n)}):
+        fk = _mean([v for n, v in fetch if n == name])
+        wk = _mean([v for n, v in write if n == name])
+        per.append(f"| {name[:72]} | {fk * 1024 * f_scale / 1e6:.1f} | "
+                   f"{(wk or 0) * 1024 * (w_scale or 0) / 1e6:.1f} |")
+    lines += ["", f"HBM traffic of `{args.kernel}` (rocprofv3 --pmc, one counter per run):", "",
               f"    {args.cmd_fetch}", f"    {args.cmd_write}", "",
               f"- FETCH_SIZE per launch: {f_dec} KiB raw; read-probe calibration "
               f"{f_probe} KiB for {PROBE_BYTES} B -> scale {f_scale}",
               f"- WRITE_SIZE per launch: {w_dec} KiB raw; copy calibration {w_copy} KiB for "
               f"{COPY_BYTES} B -> scale {w_scale}",
               f"- traffic per launch: {total} B (algorithmic {args.alg_bytes} B)",
-              f"- kernel sources hash: {rec['source_hash']}"]
+              f"- kernel sources hash: {rec['source_hash']}", "",
+              "Scaled HBM traffic per dispatch, every kernel of the run:", "",
+              "| kernel | fetch MB | write MB |", "|---|---|---|"] + per
+    if args.note:
+        lines += ["", args.note]
     with open(os.path.join(ROOT, "profiles", f"{args.name}.md"), "w") as f:
         f.write("\n".join(lines) + "\n")
     print(json.dumps(rec))
@@ -219,6 +238,8 @@ def main():
     s.add_argument("--write", default=None)
     s.add_argument("--note", default="")
     s.add_argument("--alg-bytes", type=float, default=None)
+    s.add_argument("--kernel", default="decode_kernel",
+                   help="name fragment of the kernel whose traffic is recorded")
     s.add_argument("--cmd-stats", default="")
     s.add_argument("--cmd-fetch", default="")
     s.add_argument("--cmd-write", default="")
