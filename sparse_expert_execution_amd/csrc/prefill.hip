@@ -225,41 +225,47 @@ __device__ __forceinline__ int pair_token(const GemmArgs& a, int p) {
 
 // ---- 5/6: grouped GEMMs on LDS tiles ----------------------------------------------
 // One workgroup computes a 128-row (sorted pairs of one expert) x 256-column
-// tile of A . B^T, K in steps of 128 (one MFMA deep).  The A tile (128 rows x
-// 64 code bytes) and the B tile (256 weight rows) of a step are copied from
-// global memory straight into LDS (global_load_lds, 16 bytes a lane) in
-// fragment order: for each 16-row slice, lane l's 16 bytes are row l % 16,
-// K block l / 16, exactly what the lane feeds the MFMA, so a fragment is one
-// conflict-free 16-byte LDS read.  Scale bytes: when K is a multiple of 512
-// (SG), each row's 16 scale bytes of four steps are copied at once, one
-// 16-byte copy per row every fourth step into a double-buffered scale group;
-// otherwise one dword (the step's 4 K blocks) per row and step.  A copy that
-// serves 64 rows touches 64 cache lines, so grouping the scales cuts the
-// tile's line requests several-fold.  kStages - 1 steps are in flight (about
-// 100 KB per CU, one workgroup per CU); each step lives in its own LDS
-// variable.  8
-// waves (two per SIMD, so one's matrix work covers the other's LDS waits) as
-// 2 (64 rows) x 4 (64 B rows); a wave holds 4 x 4 16x16 accumulators.
+// tile of A . B^T on v_mfma_scale_f32_16x16x128_f8f6f4 (K 128 per MFMA step).
+// Operands reach LDS by global_load_lds copies (16 bytes a lane, no
+// registers) several steps ahead of the matrix work; each buffer is its own
+// LDS variable so the compiler can count the copies.  8 waves (two per SIMD,
+// so one's matrix work covers the other's LDS waits) as 2 (64 rows) x 4
+// (64 B rows); a wave holds 4 x 4 16x16 accumulators.
 //   GEMM1: A = MXFP4(x) rows gathered by token, B = [gate rows c0..c0+127 ;
 //          up rows c0..c0+127]; epilogue h = silu(g) * u -> MXFP4 along I.
 //   GEMM2: A = MXFP4(h) rows (sorted order), B = down rows n0..n0+255;
 //          epilogue writes the pair's partial output row.
+// Two copy schemes:
+//   wide (K a multiple of 512): a buffer holds two steps (K 256) and a copy
+//     moves 8 rows x 128 bytes, whole cache lines.  Piece p (16 bytes) of
+//     row i of a copy's 8 rows lands in slot 8 i + (p ^ (4 j + i / 2)), j
+//     the copy's half of its 16-row slice, so each 16-lane group of a
+//     fragment read meets 16 distinct bank groups.  The scale bytes of four
+//     steps (16 per row) come in one copy per row, into a double-buffered
+//     scale group.  3 buffers, 2 ahead.
+//   narrow (otherwise): a buffer holds one step; a copy moves 16 rows x 64
+//     bytes in fragment order (lane l: row l % 16, K block l / 16), and the
+//     step's scale dword of each row rides along.  5 buffers, 4 ahead.
+// A copy that serves 64 rows with 4 or 16 bytes each touches 64 cache lines;
+// whole-line copies and grouped scales are what make the wide scheme faster.
 constexpr int kBM = 128, kBN = 256;
 constexpr int kGemmThreads = 512;   // 8 waves, two per SIMD
-constexpr int kStages = 5;
+constexpr int kStages = 5;          // narrow
+constexpr int kWStages = 3;         // wide
 
-template <bool SG>
-struct Stage {
+struct Stage {                      // narrow: one step
   uint4 a[(kBM / 16) * 64];         // 8 slices x 64 lanes x 16 bytes
   uint4 b[(kBN / 16) * 64];         // 16 slices
-  uint32_t as[SG ? 1 : kBM];        // 4 scale bytes (the step's K blocks) per row
-  uint32_t bs[SG ? 1 : kBN];
+  uint32_t as[kBM];                 // 4 scale bytes (the step's K blocks) per row
+  uint32_t bs[kBN];
 };
-// scale bytes of four consecutive steps (16 K blocks) per row
-template <bool SG>
-struct ScaleGroup {
-  uint4 as[SG ? kBM : 1];
-  uint4 bs[SG ? kBN : 1];
+struct WStage {                     // wide: two steps, a slice is 2 copies of 1 KB
+  uint4 a[(kBM / 16) * 128];
+  uint4 b[(kBN / 16) * 128];
+};
+struct ScaleGroup {                 // scale bytes of four steps (16 K blocks) per row
+  uint4 as[kBM];
+  uint4 bs[kBN];
 };
 
 __device__ __forceinline__ void dma16(const void* g, void* lds) {
@@ -297,197 +303,114 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)p;
 }
 
-template <int MODE, bool SG>
-__global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(GemmArgs a) {
-  using Stage = moe::Stage<SG>;
-  __shared__ Stage st0, st1, st2, st3, st4;
-  __shared__ ScaleGroup<SG> sg0, sg1;
-  auto stage = [&](int s) -> Stage& {
-    return s == 0 ? st0 : (s == 1 ? st1 : (s == 2 ? st2 : (s == 3 ? st3 : st4)));
-  };
-  const int H = a.H, I = a.I;
-  const int K = MODE == 1 ? H : I;
-  const int nout = MODE == 1 ? I : H;          // output columns of the whole GEMM
+struct Tile {
+  int row0, seg_end, col0;
+  const uint8_t* base;              // the expert's block
+};
+
+// Workgroup ids go round-robin over the 8 XCDs, each with its own L2.  Ids
+// are grouped so that the nt column tiles of one row tile run together on
+// one XCD: the row tile's A operand is then fetched from HBM once and served
+// from that L2 to the other nt - 1 workgroups.
+template <int MODE>
+__device__ __forceinline__ bool gemm_tile(const GemmArgs& a, Tile& t) {
+  const int nout = MODE == 1 ? a.I : a.H;      // output columns of the whole GEMM
   const int bn = MODE == 1 ? kBN / 2 : kBN;    // output columns of one workgroup
-  // Workgroup ids go round-robin over the 8 XCDs, each with its own L2.  Ids
-  // are grouped so that the nt column tiles of one row tile run together on
-  // one XCD: the row tile's A operand is then fetched from HBM once and served
-  // from that L2 to the other nt - 1 workgroups.
   const int nt = (nout + bn - 1) / bn;
   const int gid = blockIdx.x, per_group = 8 * nt;
   const int rem = gid % per_group;
   const int tile = (gid / per_group) * 8 + (rem & 7);
-  const int col0 = (rem >> 3) * bn;
-  const int n_tiles = a.tiles[0];
-  if (tile >= n_tiles) return;
+  if (tile >= a.tiles[0]) return false;
   const int bin = a.tiles[1 + 2 * tile];
-  const int row0 = a.tiles[2 + 2 * tile];
-  const int seg_end = a.seg_start[bin + 1];
-  const uint8_t* base = bin_base(a, bin);
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int wm = wv & 1, wn = wv >> 1;         // 2 (64 rows) x 4 (64 B rows)
-  const int fr = lane & 15, fk = lane >> 4;
+  t.row0 = a.tiles[2 + 2 * tile];
+  t.seg_end = a.seg_start[bin + 1];
+  t.col0 = (rem >> 3) * bn;
+  t.base = bin_base(a, bin);
+  return true;
+}
 
-  // copy sources of this lane: A slice wv; B slices 2 wv, 2 wv + 1; scales:
-  // SG: waves 0-1 A rows 64 wv + lane, waves 2-5 B rows 64 (wv - 2) + lane,
-  // waves 6-7 none; else dwords of A rows 64 (wv & 1) + lane and of B rows
-  // 64 (wv & 3) + lane
-  auto a_row_ptrs = [&](int r, const uint8_t*& c, const uint8_t*& sc) {
-    const bool ok = r < seg_end;
-    const int rr = ok ? r : row0;
-    if (MODE == 1) {
-      const int t = pair_token(a, a.sorted_pair[rr]);
-      c = a.xq_codes + (int64_t)t * (H / 2);
-      sc = a.xq_scales + (int64_t)t * (H / 32);
-    } else {
-      c = a.hq_codes + (int64_t)rr * (I / 2);
-      sc = a.hq_scales + (int64_t)rr * (I / 32);
-    }
-  };
-  auto b_row_ptrs = [&](int rt, const uint8_t*& c, const uint8_t*& sc) {
-    // rt: row of the B tile
-    int mat, n;
-    if (MODE == 1) { mat = rt >> 7; n = col0 + (rt & 127); }
-    else { mat = 2; n = col0 + rt; }
-    const int nn = n < nout ? n : 0;
-    c = base + a.off[2 * mat] + (int64_t)nn * (K / 2);
-    sc = base + a.off[2 * mat + 1] + (int64_t)nn * (K / 32);
-  };
-  const uint8_t* ac[1];
-  const uint8_t* bc[2];
-  const uint8_t* as_src;
-  const uint8_t* bs_src;
+// codes and scales of A row r (a sorted position; rows past the segment read
+// the tile's first row, whose results are dropped)
+template <int MODE>
+__device__ __forceinline__ void a_row(const GemmArgs& a, const Tile& t, int r,
+                                      const uint8_t*& c, const uint8_t*& sc) {
+  const int rr = r < t.seg_end ? r : t.row0;
+  if (MODE == 1) {
+    const int tok = pair_token(a, a.sorted_pair[rr]);
+    c = a.xq_codes + (int64_t)tok * (a.H / 2);
+    sc = a.xq_scales + (int64_t)tok * (a.H / 32);
+  } else {
+    c = a.hq_codes + (int64_t)rr * (a.I / 2);
+    sc = a.hq_scales + (int64_t)rr * (a.I / 32);
+  }
+}
+
+// codes and scales of row rt of the B tile (GEMM1: gate rows, then up rows)
+template <int MODE>
+__device__ __forceinline__ void b_row(const GemmArgs& a, const Tile& t, int rt,
+                                      const uint8_t*& c, const uint8_t*& sc) {
+  const int K = MODE == 1 ? a.H : a.I;
+  const int nout = MODE == 1 ? a.I : a.H;
+  int mat, n;
+  if (MODE == 1) { mat = rt >> 7; n = t.col0 + (rt & 127); }
+  else { mat = 2; n = t.col0 + rt; }
+  const int nn = n < nout ? n : 0;
+  c = t.base + a.off[2 * mat] + (int64_t)nn * (K / 2);
+  sc = t.base + a.off[2 * mat + 1] + (int64_t)nn * (K / 32);
+}
+
+// the wave's 4 x 4 MFMAs of one step from fragment and scale addresses
+template <int MODE>
+__device__ __forceinline__ void mma_step(const uint32_t (&aq)[4], const uint32_t (&as)[4],
+                                         const uint32_t (&bq)[4], const uint32_t (&bs)[4],
+                                         int fk, v4f (&acc)[4][4]) {
+  Frag fa[4];
   {
-    const uint8_t* dummy;
-    a_row_ptrs(row0 + wv * 16 + fr, ac[0], dummy);
+    u32x4 q[4];
+    uint32_t sc[4];
+    lds_frag4(aq, as, q, sc);
 #pragma unroll
-    for (int j = 0; j < 2; ++j) b_row_ptrs((2 * wv + j) * 16 + fr, bc[j], dummy);
-    const uint8_t* c;
-    if constexpr (SG) {
-      as_src = bs_src = nullptr;
-      if (wv < 2) a_row_ptrs(row0 + wv * 64 + lane, c, as_src);
-      else if (wv < 6) b_row_ptrs((wv - 2) * 64 + lane, c, bs_src);
-    } else {
-      a_row_ptrs(row0 + (wv & 1) * 64 + lane, c, as_src);
-      b_row_ptrs((wv & 3) * 64 + lane, c, bs_src);
+    for (int ms = 0; ms < 4; ++ms) {
+      fa[ms].q = make_uint4(q[ms].x, q[ms].y, q[ms].z, q[ms].w);
+      fa[ms].s = (sc[ms] >> (8 * fk)) & 0xffu;
     }
   }
-  // Without SG every wave issues the same number of copies per step (5), so
-  // one count covers all: the scale dwords are copied by several waves (the
-  // same bytes to the same place).  With SG a wave issues 3 code copies per
-  // step, and waves 0-5 one scale copy ahead of the codes of a group's first
-  // step (real steps only): the codes' count then covers it, since copies
-  // complete in issue order.
-  auto issue = [&](int kt, Stage& S, bool real) {
-    const int k0 = kt * 128;
-    if constexpr (SG) {
-      if (real && (kt & 3) == 0 && wv < 6) {
-        ScaleGroup<SG>& G = ((kt >> 2) & 1) ? sg1 : sg0;
-        if (wv < 2) dma16(as_src + (kt >> 2) * 16, &G.as[wv * 64]);
-        else dma16(bs_src + (kt >> 2) * 16, &G.bs[(wv - 2) * 64]);
-      }
-    }
-    dma16(ac[0] + k0 / 2 + fk * 16, &S.a[wv * 64]);
+  u32x4 q[4];
+  uint32_t sc[4];
+  lds_frag4(bq, bs, q, sc);
 #pragma unroll
-    for (int j = 0; j < 2; ++j) dma16(bc[j] + k0 / 2 + fk * 16, &S.b[(2 * wv + j) * 64]);
-    if constexpr (!SG) {
-      dma4(as_src + k0 / 32, &S.as[(wv & 1) * 64]);
-      dma4(bs_src + k0 / 32, &S.bs[(wv & 3) * 64]);
-    }
-  };
-  constexpr int kCopies = SG ? 3 : 5;          // copies per wave per step (codes, scales)
-
-  v4f acc[4][4];
+  for (int ns = 0; ns < 4; ++ns) {
+    Frag fb;
+    fb.q = make_uint4(q[ns].x, q[ns].y, q[ns].z, q[ns].w);
+    fb.s = (sc[ns] >> (8 * fk)) & 0xffu;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
-
-  // LDS byte address of row 0's scale dword of step kt
-  auto scale_base = [&](const Stage& S, int kt, bool b_side) -> uint32_t {
-    if constexpr (SG) {
-      const ScaleGroup<SG>& G = ((kt >> 2) & 1) ? sg1 : sg0;
-      return (b_side ? lds_addr(&G.bs[0]) : lds_addr(&G.as[0])) + (kt & 3) * 4;
-    } else {
-      return b_side ? lds_addr(&S.bs[0]) : lds_addr(&S.as[0]);
-    }
-  };
-  constexpr uint32_t kScaleRowBytes = SG ? 16 : 4;
-
-  auto compute = [&](const Stage& S, int kt) {
-    const uint32_t asb = scale_base(S, kt, false), bsb = scale_base(S, kt, true);
-    Frag fa[4];
-    {
-      uint32_t qa[4], sa[4], sc[4];
-      u32x4 q[4];
-#pragma unroll
-      for (int ms = 0; ms < 4; ++ms) {
-        const int sl = wm * 4 + ms;
-        qa[ms] = lds_addr(&S.a[sl * 64 + lane]);
-        sa[ms] = asb + (sl * 16 + fr) * kScaleRowBytes;
-      }
-      lds_frag4(qa, sa, q, sc);
-#pragma unroll
-      for (int ms = 0; ms < 4; ++ms) {
-        fa[ms].q = make_uint4(q[ms].x, q[ms].y, q[ms].z, q[ms].w);
-        fa[ms].s = (sc[ms] >> (8 * fk)) & 0xffu;
-      }
-    }
-    {
-      uint32_t qa[4], sa[4], sc[4];
-      u32x4 q[4];
-#pragma unroll
-      for (int ns = 0; ns < 4; ++ns) {
-        // GEMM1: slices 0..7 gate, 8..15 up; wave wn takes 32 h columns of
-        // each (n-slices 0, 1 gate and 2, 3 up)
-        const int sl = MODE == 1 ? (ns >> 1) * 8 + wn * 2 + (ns & 1) : wn * 4 + ns;
-        qa[ns] = lds_addr(&S.b[sl * 64 + lane]);
-        sa[ns] = bsb + (sl * 16 + fr) * kScaleRowBytes;
-      }
-      lds_frag4(qa, sa, q, sc);
-#pragma unroll
-      for (int ns = 0; ns < 4; ++ns) {
-        Frag fb;
-        fb.q = make_uint4(q[ns].x, q[ns].y, q[ns].z, q[ns].w);
-        fb.s = (sc[ns] >> (8 * fk)) & 0xffu;
-#pragma unroll
-        for (int ms = 0; ms < 4; ++ms) acc[ms][ns] = mfma_fp4(fa[ms], fb, acc[ms][ns]);
-      }
-    }
-  };
-
-  const int nk = K / 128;
-  // prologue: steps 0 .. kStages-2 (a step past the end re-reads the last)
-#pragma unroll
-  for (int s = 0; s < kStages - 1; ++s) issue(s < nk ? s : nk - 1, stage(s), s < nk);
-  for (int kt0 = 0; kt0 < nk; kt0 += kStages) {
-#pragma unroll
-    for (int s = 0; s < kStages; ++s) {
-      const int kt = kt0 + s;
-      if (kt < nk) {
-        // this wave's copies of step kt are done once at most the later
-        // kStages-2 steps' copies are outstanding; the barrier makes every
-        // wave's copies visible and frees the buffer step kt-1 used
-        asm volatile("s_waitcnt vmcnt(%0)" ::"n"((kStages - 2) * kCopies) : "memory");
-        __builtin_amdgcn_s_barrier();
-        const int kn = kt + kStages - 1;
-        issue(kn < nk ? kn : nk - 1, stage((s + kStages - 1) % kStages), kn < nk);
-        compute(stage(s), kt);
-      }
-    }
+    for (int ms = 0; ms < 4; ++ms) acc[ms][ns] = mfma_fp4(fa[ms], fb, acc[ms][ns]);
   }
+}
 
+// B slice read by n-slice ns of wave column wn.  GEMM1: slices 0..7 gate,
+// 8..15 up; wave wn takes 32 h columns of each (n-slices 0, 1 gate and 2, 3
+// up).  GEMM2: 4 consecutive slices.
+template <int MODE>
+__device__ __forceinline__ int b_slice(int wn, int ns) {
+  return MODE == 1 ? (ns >> 1) * 8 + wn * 2 + (ns & 1) : wn * 4 + ns;
+}
+
+template <int MODE>
+__device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, const Tile& t,
+                                              v4f (&acc)[4][4], int wm, int wn, int lane) {
+  const int H = a.H, I = a.I;
   if (MODE == 1) {
     // h = silu(g) * u; each row's 32-column block (gate and up n-slice
     // pairs) to MXFP4
-    const int c0 = col0 + wn * 32;             // first h column of this wave
+    const int c0 = t.col0 + wn * 32;             // first h column of this wave
 #pragma unroll
     for (int ms = 0; ms < 4; ++ms) {
       {
         constexpr int blk = 0;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int r = row0 + wm * 64 + ms * 16 + d_row(lane, i);
+          const int r = t.row0 + wm * 64 + ms * 16 + d_row(lane, i);
           const float g0 = acc[ms][0][i], g1 = acc[ms][1][i];
           const float u0 = acc[ms][2][i], u1 = acc[ms][3][i];
           const float h0 = g0 / (1.0f + expf(-g0)) * u0;
@@ -506,7 +429,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(GemmArgs a) {
           const uint32_t n1 = __shfl_xor(q1, 1, kWave);
           const int c = d_col(lane);
           const int cb = c0 + blk * 32;         // first column of the block
-          if (r < seg_end) {
+          if (r < t.seg_end) {
             uint8_t* dst = a.hq_codes + (int64_t)r * (I / 2) + cb / 2;
             if ((c & 1) == 0) {
               dst[c >> 1] = (uint8_t)(q0 | (n0 << 4));
@@ -523,19 +446,221 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(GemmArgs a) {
     for (int ms = 0; ms < 4; ++ms) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int r = row0 + wm * 64 + ms * 16 + d_row(lane, i);
-        if (r >= seg_end) continue;
+        const int r = t.row0 + wm * 64 + ms * 16 + d_row(lane, i);
+        if (r >= t.seg_end) continue;
         const int p = a.sorted_pair[r];
         int prow;
         if (p < nr) prow = (p / a.k) * (a.k + 1) + (p % a.k);
         else prow = (p - nr) * (a.k + 1) + a.k;
-        float* dst = a.partial + (int64_t)prow * H + col0 + wn * 64 + d_col(lane);
+        float* dst = a.partial + (int64_t)prow * H + t.col0 + wn * 64 + d_col(lane);
 #pragma unroll
         for (int ns = 0; ns < 4; ++ns)
-          if (col0 + wn * 64 + ns * 16 < H) dst[ns * 16] = acc[ms][ns][i];
+          if (t.col0 + wn * 64 + ns * 16 < H) dst[ns * 16] = acc[ms][ns][i];
       }
     }
   }
+}
+
+template <int MODE>
+__global__ __launch_bounds__(kGemmThreads, 1) void gemm_kernel(GemmArgs a) {
+  __shared__ Stage st0, st1, st2, st3, st4;
+  auto stage = [&](int s) -> Stage& {
+    return s == 0 ? st0 : (s == 1 ? st1 : (s == 2 ? st2 : (s == 3 ? st3 : st4)));
+  };
+  Tile t;
+  if (!gemm_tile<MODE>(a, t)) return;
+  const int K = MODE == 1 ? a.H : a.I;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int wm = wv & 1, wn = wv >> 1;         // 2 (64 rows) x 4 (64 B rows)
+  const int fr = lane & 15, fk = lane >> 4;
+
+  // copy sources of this lane: A slice wv; B slices 2 wv, 2 wv + 1; scale
+  // dwords of A rows 64 (wv & 1) + lane and of B rows 64 (wv & 3) + lane
+  const uint8_t* ac;
+  const uint8_t* bc[2];
+  const uint8_t* as_src;
+  const uint8_t* bs_src;
+  {
+    const uint8_t* dummy;
+    a_row<MODE>(a, t, t.row0 + wv * 16 + fr, ac, dummy);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) b_row<MODE>(a, t, (2 * wv + j) * 16 + fr, bc[j], dummy);
+    const uint8_t* c;
+    a_row<MODE>(a, t, t.row0 + (wv & 1) * 64 + lane, c, as_src);
+    b_row<MODE>(a, t, (wv & 3) * 64 + lane, c, bs_src);
+  }
+  // every wave issues the same number of copies per step (5), so one count
+  // covers all: the scale dwords are copied by several waves (the same bytes
+  // to the same place)
+  auto issue = [&](int kt, Stage& S) {
+    const int k0 = kt * 128;
+    dma16(ac + k0 / 2 + fk * 16, &S.a[wv * 64]);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) dma16(bc[j] + k0 / 2 + fk * 16, &S.b[(2 * wv + j) * 64]);
+    dma4(as_src + k0 / 32, &S.as[(wv & 1) * 64]);
+    dma4(bs_src + k0 / 32, &S.bs[(wv & 3) * 64]);
+  };
+  constexpr int kCopies = 5;                   // copies per wave per step
+
+  v4f acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  auto compute = [&](const Stage& S) {
+    uint32_t aq[4], as[4], bq[4], bs[4];
+#pragma unroll
+    for (int ms = 0; ms < 4; ++ms) {
+      const int sl = wm * 4 + ms;
+      aq[ms] = lds_addr(&S.a[sl * 64 + lane]);
+      as[ms] = lds_addr(&S.as[sl * 16 + fr]);
+    }
+#pragma unroll
+    for (int ns = 0; ns < 4; ++ns) {
+      const int sl = b_slice<MODE>(wn, ns);
+      bq[ns] = lds_addr(&S.b[sl * 64 + lane]);
+      bs[ns] = lds_addr(&S.bs[sl * 16 + fr]);
+    }
+    mma_step<MODE>(aq, as, bq, bs, fk, acc);
+  };
+
+  const int nk = K / 128;
+  // prologue: steps 0 .. kStages-2 (a step past the end re-reads the last)
+#pragma unroll
+  for (int s = 0; s < kStages - 1; ++s) issue(s < nk ? s : nk - 1, stage(s));
+  for (int kt0 = 0; kt0 < nk; kt0 += kStages) {
+#pragma unroll
+    for (int s = 0; s < kStages; ++s) {
+      const int kt = kt0 + s;
+      if (kt < nk) {
+        // this wave's copies of step kt are done once at most the later
+        // kStages-2 steps' copies are outstanding; the barrier makes every
+        // wave's copies visible and frees the buffer step kt-1 used
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"((kStages - 2) * kCopies) : "memory");
+        __builtin_amdgcn_s_barrier();
+        const int kn = kt + kStages - 1;
+        issue(kn < nk ? kn : nk - 1, stage((s + kStages - 1) % kStages));
+        compute(stage(s));
+      }
+    }
+  }
+  gemm_epilogue<MODE>(a, t, acc, wm, wn, lane);
+}
+
+template <int MODE>
+__global__ __launch_bounds__(kGemmThreads, 1) void gemm_wide_kernel(GemmArgs a) {
+  __shared__ WStage ws0, ws1, ws2;
+  __shared__ ScaleGroup sg0, sg1;
+  auto stage = [&](int s) -> WStage& { return s == 0 ? ws0 : (s == 1 ? ws1 : ws2); };
+  Tile t;
+  if (!gemm_tile<MODE>(a, t)) return;
+  const int K = MODE == 1 ? a.H : a.I;
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = wv & 1, wn = wv >> 1;
+  const int fr = lane & 15, fk = lane >> 4;
+
+  // copy lanes: row ci = lane / 8 of the copy's 8 rows; its piece is
+  // (lane % 8) ^ (4 j + ci / 2), so lane l lands in slot l = 8 ci + (lane % 8)
+  const int ci = lane >> 3;
+  const uint8_t* ac[2];              // A slice wv, halves j = 0, 1
+  const uint8_t* bc[4];              // B slices 2 wv + (q >> 1), halves q & 1
+  const uint8_t* ssrc = nullptr;     // scales: waves 0-1 A rows, 2-5 B rows
+  {
+    const uint8_t* dummy;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int p = (lane & 7) ^ (4 * j + (ci >> 1));
+      a_row<MODE>(a, t, t.row0 + wv * 16 + 8 * j + ci, ac[j], dummy);
+      ac[j] += p * 16;
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int j = q & 1;
+      const int p = (lane & 7) ^ (4 * j + (ci >> 1));
+      b_row<MODE>(a, t, (2 * wv + (q >> 1)) * 16 + 8 * j + ci, bc[q], dummy);
+      bc[q] += p * 16;
+    }
+    const uint8_t* c;
+    if (wv < 2) a_row<MODE>(a, t, t.row0 + wv * 64 + lane, c, ssrc);
+    else if (wv < 6) b_row<MODE>(a, t, (wv - 2) * 64 + lane, c, ssrc);
+  }
+  // Double step m = K steps 2m, 2m+1 = code bytes [128 m, 128 m + 128) of a
+  // row.  Every wave issues 6 code copies per double step; on even m, waves
+  // 0-5 first copy scale group m / 2 (K steps 2m .. 2m+3, row bytes
+  // [16 (m/2), +16)), real steps only: copies complete in issue order, so the
+  // codes' count covers it.
+  auto issue = [&](int m, WStage& S, bool real) {
+    if (real && (m & 1) == 0 && wv < 6) {
+      ScaleGroup& G = ((m >> 1) & 1) ? sg1 : sg0;
+      if (wv < 2) dma16(ssrc + (m >> 1) * 16, &G.as[wv * 64]);
+      else dma16(ssrc + (m >> 1) * 16, &G.bs[(wv - 2) * 64]);
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) dma16(ac[j] + m * 128, &S.a[(wv * 2 + j) * 64]);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) dma16(bc[q] + m * 128, &S.b[((2 * wv + (q >> 1)) * 2 + (q & 1)) * 64]);
+  };
+  constexpr int kWCopies = 6;
+
+  // fragment slot of this lane in its slice (uint4 units) for sub-step u:
+  // row fr = 8 j + i, piece 4 u + fk
+  uint32_t fo[2];
+  {
+    const int j = fr >> 3, i = fr & 7;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) fo[u] = j * 64 + 8 * i + ((4 * u + fk) ^ (4 * j + (i >> 1)));
+  }
+
+  v4f acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  auto compute = [&](const WStage& S, int m) {
+    const ScaleGroup& G = ((m >> 1) & 1) ? sg1 : sg0;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const uint32_t so = ((2 * m + u) & 3) * 4;   // the step's dword in a row's 16 bytes
+      uint32_t aq[4], as[4], bq[4], bs[4];
+#pragma unroll
+      for (int ms = 0; ms < 4; ++ms) {
+        const int sl = wm * 4 + ms;
+        aq[ms] = lds_addr(&S.a[sl * 128 + fo[u]]);
+        as[ms] = lds_addr(&G.as[sl * 16 + fr]) + so;
+      }
+#pragma unroll
+      for (int ns = 0; ns < 4; ++ns) {
+        const int sl = b_slice<MODE>(wn, ns);
+        bq[ns] = lds_addr(&S.b[sl * 128 + fo[u]]);
+        bs[ns] = lds_addr(&G.bs[sl * 16 + fr]) + so;
+      }
+      mma_step<MODE>(aq, as, bq, bs, fk, acc);
+    }
+  };
+
+  const int nd = K / 256;                      // K % 512 == 0: nd even, >= 2
+  issue(0, ws0, true);
+  issue(1, ws1, true);
+  for (int m0 = 0; m0 < nd; m0 += kWStages) {
+#pragma unroll
+    for (int s = 0; s < kWStages; ++s) {
+      const int m = m0 + s;
+      if (m < nd) {
+        // this wave's copies of double step m are done once at most the next
+        // one's are outstanding; the barrier makes every wave's copies
+        // visible and frees the buffers double step m-1 used
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"((kWStages - 2) * kWCopies) : "memory");
+        __builtin_amdgcn_s_barrier();
+        const int mn = m + kWStages - 1;
+        issue(mn < nd ? mn : nd - 1, stage((s + kWStages - 1) % kWStages), mn < nd);
+        compute(stage(s), m);
+      }
+    }
+  }
+  gemm_epilogue<MODE>(a, t, acc, wm, wn, lane);
 }
 
 // ---- 7: combine ------------------------------------------------------------------
@@ -627,20 +752,18 @@ hipError_t launch_prefill(const PrefillLaunch& p, hipStream_t st) {
   {
     const int groups = (p.max_tiles + 7) / 8;
     const int nt1 = p.I / (kBN / 2), nt2 = (p.H + kBN - 1) / kBN;
-    // K a multiple of 512: scales copied four steps at a time
+    // K a multiple of 512: two-step buffers, whole-line copies, grouped scales
     if (p.H % 512 == 0)
-      hipLaunchKernelGGL((gemm_kernel<1, true>), dim3(groups * 8 * nt1), dim3(kGemmThreads), 0,
-                         st, g);
+      hipLaunchKernelGGL(gemm_wide_kernel<1>, dim3(groups * 8 * nt1), dim3(kGemmThreads), 0, st,
+                         g);
     else
-      hipLaunchKernelGGL((gemm_kernel<1, false>), dim3(groups * 8 * nt1), dim3(kGemmThreads), 0,
-                         st, g);
+      hipLaunchKernelGGL(gemm_kernel<1>, dim3(groups * 8 * nt1), dim3(kGemmThreads), 0, st, g);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     if (p.I % 512 == 0)
-      hipLaunchKernelGGL((gemm_kernel<2, true>), dim3(groups * 8 * nt2), dim3(kGemmThreads), 0,
-                         st, g);
+      hipLaunchKernelGGL(gemm_wide_kernel<2>, dim3(groups * 8 * nt2), dim3(kGemmThreads), 0, st,
+                         g);
     else
-      hipLaunchKernelGGL((gemm_kernel<2, false>), dim3(groups * 8 * nt2), dim3(kGemmThreads), 0,
-                         st, g);
+      hipLaunchKernelGGL(gemm_kernel<2>, dim3(groups * 8 * nt2), dim3(kGemmThreads), 0, st, g);
   }
   if ((err = hipGetLastError()) != hipSuccess) return err;
   {
