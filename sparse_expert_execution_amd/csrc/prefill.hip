@@ -141,8 +141,11 @@ __global__ __launch_bounds__(1024) void sort_scan_kernel(SortArgs a) {
   const int nb = a.E + 1;
   int* tot = sh;            // [nb]
   int* ntile = sh + nb;     // [nb]
+  // one thread per bin walks the chunks; the loops are unrolled so that many
+  // of its loads are in flight at once
   for (int b = threadIdx.x; b < nb; b += blockDim.x) {
     int s = 0;
+#pragma unroll 16
     for (int c = 0; c < a.n_chunks; ++c) s += a.chunk_counts[(int64_t)c * nb + b];
     tot[b] = s;
     ntile[b] = (s + kMT - 1) / kMT;
@@ -166,10 +169,16 @@ __global__ __launch_bounds__(1024) void sort_scan_kernel(SortArgs a) {
     const int end = (b + 1 < nb) ? tot[b + 1] : a.seg_start[nb];
     a.seg_start[b] = start;
     int pos = start;
-    for (int c = 0; c < a.n_chunks; ++c) {
-      const int n = a.chunk_counts[(int64_t)c * nb + b];
-      a.chunk_counts[(int64_t)c * nb + b] = pos;
-      pos += n;
+    for (int c0 = 0; c0 < a.n_chunks; c0 += 16) {
+      int n[16];                   // all loads of a batch before its stores
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        n[i] = c0 + i < a.n_chunks ? a.chunk_counts[(int64_t)(c0 + i) * nb + b] : 0;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        if (c0 + i < a.n_chunks) a.chunk_counts[(int64_t)(c0 + i) * nb + b] = pos;
+        pos += n[i];
+      }
     }
     int ti = ntile[b];
     for (int r0 = start; r0 < end; r0 += kMT, ++ti) {
