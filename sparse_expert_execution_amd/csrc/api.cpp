@@ -103,9 +103,9 @@ PrefillWs prefill_ws(const moe_desc* d, int T) {
 }
 
 // route workspace: [0, 256) ticket counter, then router logits z [T][E].
-// decode workspace: [0, 8192) counters and the launch generation, then z
-// [T][E] and h [T*k + T][I] (8 bytes each: the fp32 value and the launch
-// generation it belongs to) and
+// decode workspace: [0, 8192) counters and the launch generation, then
+// kZCopies copies of z [T][E] and h [T*k + T][I] (8 bytes each: the fp32
+// value and the launch generation it belongs to) and
 // per-workgroup phase stamps (written only when timing is switched on).  The
 // whole workspace must be zero before its first use; every call leaves the
 // counters zero.
@@ -116,7 +116,8 @@ constexpr size_t kDecodeHeader = 8192;
 RouteWs route_ws(const moe_desc* d, int T, bool decode) {
   RouteWs w;
   w.z = decode ? kDecodeHeader : kAlign;
-  w.h = align_up(w.z + (size_t)T * d->n_experts * (decode ? 8 : 4));
+  w.h = align_up(w.z + (decode ? moe::kZCopies * moe::decode_z_copy_bytes(T, d->n_experts)
+                              : (size_t)T * d->n_experts * 4));
   w.st = decode ? align_up(w.h + (size_t)(T * d->top_k + T) * d->inter * 8) : w.h;
   w.total = decode ? w.st + moe::kDecodeStampBytes : w.h;
   return w;
@@ -223,6 +224,7 @@ static int decode_impl(const moe_desc* desc, const void* x, const void* w_router
   f.pool = slot_pool; f.shared = shared_expert;
   f.hdr = reinterpret_cast<unsigned*>(b);
   f.z = reinterpret_cast<uint64_t*>(b + L.z);
+  f.zstride = (int64_t)(moe::decode_z_copy_bytes(T, desc->n_experts) / 8);
   f.h = reinterpret_cast<uint64_t*>(b + L.h);
   f.stamps = reinterpret_cast<unsigned long long*>(b + L.st);
   f.y = y; f.expert_bytes = (int64_t)bytes;

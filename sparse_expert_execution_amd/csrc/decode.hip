@@ -50,6 +50,7 @@ hipError_t launch_decode(const DecodeLaunch& f, hipStream_t st) {
   a.shared = static_cast<const uint8_t*>(f.shared);
   a.hdr = f.hdr;
   a.z = f.z;
+  a.zstride = f.zstride;
   a.h = f.h;
   a.st = f.stamps;
   a.y = f.y;

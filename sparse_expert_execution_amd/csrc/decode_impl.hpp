@@ -88,7 +88,8 @@ struct DecArgs {
   const uint8_t* pool;
   const uint8_t* shared;
   unsigned* hdr;
-  uint64_t* z;             // [T][E] logits tagged with the launch's generation
+  uint64_t* z;             // kZCopies x [T][E] logits tagged with the generation
+  int64_t zstride;         // uint64 words between the copies
   uint64_t* h;             // [T*k + T][I] h values tagged with the generation
   unsigned long long* st;  // [workgroup][16] phase stamps
   float* y;                // [T][H]
@@ -174,6 +175,13 @@ __device__ void wait_count(const DecArgs& a, unsigned* count, unsigned target) {
 __device__ __forceinline__ void z_store(uint64_t* p, float z, unsigned gen) {
   __hip_atomic_store(p, ((uint64_t)gen << 32) | __float_as_uint(z), __ATOMIC_RELAXED,
                      __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Every logit is written to kZCopies copies of z, and workgroup b polls copy
+// b % kZCopies: all workgroups poll the logits at once, and a single copy's
+// few cache lines would queue their requests at one memory channel.
+__device__ __forceinline__ const uint64_t* zcopy(const DecArgs& a) {
+  return a.z + (int64_t)(blockIdx.x % kZCopies) * a.zstride;
 }
 
 // one wave: logits of expert lane + 64 i of row zt into v (-inf past E)
@@ -364,7 +372,8 @@ __device__ void router_items_run(const DecArgs& a, const DecLds& S, int item, Ro
     for (int tt = 0; tt < kRTG; ++tt) {
       if (t0 + tt >= a.T) break;
       const float z = wave_sum_dpp(acc[tt]);
-      if (lane == 0) z_store(a.z + (int64_t)(t0 + tt) * a.E + e, z, gen);
+      if (lane < kZCopies)
+        z_store(a.z + lane * a.zstride + (int64_t)(t0 + tt) * a.E + e, z, gen);
     }
   }
 }
@@ -407,7 +416,7 @@ __device__ void rank_topk(const DecArgs& a, DecLds& S, unsigned gen) {
     const int t = i / E4, e = i - t * E4;
     float z = -INFINITY;
     if (e < E) {
-      const uint64_t* p = a.z + (int64_t)t * E + e;
+      const uint64_t* p = zcopy(a) + (int64_t)t * E + e;
       unsigned spins = 0;
       uint64_t q = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       while ((unsigned)(q >> 32) != gen) {
@@ -583,7 +592,7 @@ __device__ void build_units(const DecArgs& a, DecLds& S, bool route, bool timing
   } else if (route) {
     for (int t = wave; t < T; t += kW) {
       float v[M];
-      z_load<M>(a, a.z + (int64_t)t * E, gen, v);
+      z_load<M>(a, zcopy(a) + (int64_t)t * E, gen, v);
       stamp(timing, a, 6);
       topk_select<M>(v, E, k, a.renorm, &L.ids[t * k], &L.w[t * k]);
     }

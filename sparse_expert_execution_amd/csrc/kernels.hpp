@@ -16,7 +16,8 @@ struct DecodeLaunch {
   const void* pool;
   const void* shared;
   unsigned* hdr;          // counter header (zero before first use)
-  uint64_t* z;            // [T][E] generation-tagged logits
+  uint64_t* z;            // kZCopies copies of [T][E] generation-tagged logits
+  int64_t zstride;        // uint64 words from one copy to the next
   uint64_t* h;            // [T*k + T][I] generation-tagged h
   unsigned long long* stamps;  // [kMaxWorkgroups][16] phase stamps (timing only)
   float* y;
@@ -62,6 +63,13 @@ hipError_t launch_route_large(const void* x, const void* w_router, int router_f3
 
 // per-workgroup phase stamps at the end of the decode workspace
 constexpr size_t kDecodeStampBytes = 1024 * 16 * 8;
+// copies of the decode logits (each read by every kZCopies-th workgroup)
+constexpr int kZCopies = 16;
+// bytes of one copy: [T][E] uint64, rounded to 4 KB, plus 256 B so that the
+// copies start at different offsets within a page
+inline size_t decode_z_copy_bytes(int T, int E) {
+  return (((size_t)T * E * 8 + 4095) & ~(size_t)4095) + 256;
+}
 
 // decode: router (optional) + experts + combine in one kernel, at most
 // decode_max_tokens(H) tokens per launch
