@@ -64,7 +64,7 @@ hipError_t launch_route_large(const void* x, const void* w_router, int router_f3
 // per-workgroup phase stamps at the end of the decode workspace
 constexpr size_t kDecodeStampBytes = 1024 * 16 * 8;
 // copies of the decode logits (each read by every kZCopies-th workgroup)
-constexpr int kZCopies = 16;
+constexpr int kZCopies = 64;
 // bytes of one copy: [T][E] uint64, rounded to 4 KB, plus 256 B so that the
 // copies start at different offsets within a page
 inline size_t decode_z_copy_bytes(int T, int E) {
