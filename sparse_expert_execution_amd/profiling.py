@@ -177,7 +177,9 @@ def cmd_summarize(args):
     f_dec = _mean([v for n, v in fetch if dec(n)])
     f_probe = _mean([v for n, v in fetch if probe(n)])
     w_dec = _mean([v for n, v in write if dec(n)])
-    w_copy = max([v for n, v in write if copy(n)] or [0.0]) or None
+    # the calibration copy is the run's last copy kernel (earlier fills of
+    # weights and workspaces also match the name test)
+    w_copy = ([v for n, v in write if copy(n)] or [0.0])[-1] or None
     f_scale = PROBE_BYTES / (f_probe * 1024) if f_probe else None
     w_scale = COPY_BYTES / (w_copy * 1024) if w_copy else None
     fetch_b = f_dec * 1024 * f_scale if f_dec and f_scale else None
