@@ -417,7 +417,8 @@ int moe_probe_bandwidths(const void* pinned_host, void* dev, size_t bytes,
  *   y          host [T][H] float, overwritten
  *   n_threads  host threads (0 = all hardware threads); a persistent pool
  *              is kept between calls.
- * Blocks the caller.  The shared expert is not part of this call. */
+ * Weights: BF16, MXFP4 or NVFP4 blocks.  Blocks the caller.  The shared
+ * expert is not part of this call. */
 int moe_host_experts(const moe_desc* desc, const void* x, int32_t T,
                      const int32_t* ids, const float* w, const uint8_t* include,
                      const void* host_pool, const int32_t* host_index,

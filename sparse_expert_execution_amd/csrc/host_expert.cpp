@@ -13,9 +13,10 @@
 // pool of threads by rows: the gate/up rows of an expert, then its down rows
 // (each thread owns whole output rows, so there are no atomics and the
 // result does not depend on the thread count).  Row dots use AVX-512 or
-// AVX2/FMA when the CPU has them: an MXFP4 code is decoded by a permute over
-// the sixteen signed e2m1 values (AVX-512) or over the eight magnitudes plus
-// the sign bit (AVX2).
+// AVX2/FMA when the CPU has them: an MXFP4 or NVFP4 code is decoded by a
+// permute over the sixteen signed e2m1 values (AVX-512) or over the eight
+// magnitudes plus the sign bit (AVX2); an NVFP4 row scales each 16-element
+// sum by its E4M3 byte and the row's total by the matrix's fp32 scale.
 #include <immintrin.h>
 
 #include <atomic>
@@ -136,6 +137,15 @@ inline float e8m0(uint8_t s) {
 
 const float kE2m1[8] = {0.f, 0.5f, 1.f, 1.5f, 2.f, 3.f, 4.f, 6.f};
 
+// OCP FP8 E4M3FN byte: sign, 4 exponent bits (bias 7), 3 mantissa bits;
+// exponent 0 is subnormal (m / 8 * 2^-6).  The block scales written by the
+// packer are non-negative and at most 448.
+inline float e4m3(uint8_t s) {
+  const int e = (s >> 3) & 15, m = s & 7;
+  const float mag = e == 0 ? (float)m * 0x1p-9f : std::ldexp(1.0f + (float)m * 0.125f, e - 7);
+  return (s & 0x80) ? -mag : mag;
+}
+
 // ---- row dots: a weight row against an fp32 vector of length K --------------------
 float dot_mxfp4_scalar(const uint8_t* codes, const uint8_t* scales, const float* v, int K) {
   float acc = 0.f;
@@ -149,6 +159,24 @@ float dot_mxfp4_scalar(const uint8_t* codes, const uint8_t* scales, const float*
       s += a * v[b * 32 + 2 * j] + c * v[b * 32 + 2 * j + 1];
     }
     acc += s * e8m0(scales[b]);
+  }
+  return acc;
+}
+
+// NVFP4 row: e2m1 codes, an E4M3 scale per 16 elements (the matrix's fp32
+// scale is applied by the caller)
+float dot_nvfp4_scalar(const uint8_t* codes, const uint8_t* scales, const float* v, int K) {
+  float acc = 0.f;
+  for (int b = 0; b < K / 16; ++b) {
+    float s = 0.f;
+    for (int j = 0; j < 8; ++j) {
+      const uint8_t byte = codes[b * 8 + j];
+      const uint8_t lo = byte & 15, hi = byte >> 4;
+      const float a = (lo & 8) ? -kE2m1[lo & 7] : kE2m1[lo & 7];
+      const float c = (hi & 8) ? -kE2m1[hi & 7] : kE2m1[hi & 7];
+      s += a * v[b * 16 + 2 * j] + c * v[b * 16 + 2 * j + 1];
+    }
+    acc += s * e4m3(scales[b]);
   }
   return acc;
 }
@@ -197,6 +225,32 @@ __attribute__((target("avx2,fma"))) float dot_mxfp4_avx2(const uint8_t* codes,
   return hsum256(acc);
 }
 
+__attribute__((target("avx2,fma"))) float dot_nvfp4_avx2(const uint8_t* codes,
+                                                          const uint8_t* scales, const float* v,
+                                                          int K) {
+  const __m256 lut = _mm256_setr_ps(0.f, 0.5f, 1.f, 1.5f, 2.f, 3.f, 4.f, 6.f);
+  const __m128i m15 = _mm_set1_epi8(15);
+  __m256 acc = _mm256_setzero_ps();
+  for (int b = 0; b < K / 32; ++b) {          // two 16-element scale blocks
+    const __m128i raw = _mm_loadu_si128(reinterpret_cast<const __m128i*>(codes + b * 16));
+    const __m128i lo = _mm_and_si128(raw, m15);
+    const __m128i hi = _mm_and_si128(_mm_srli_epi16(raw, 4), m15);
+    const __m128i c0 = _mm_unpacklo_epi8(lo, hi);   // codes 0..15
+    const __m128i c1 = _mm_unpackhi_epi8(lo, hi);   // codes 16..31
+    const float* x = v + b * 32;
+    __m256 s0 = _mm256_mul_ps(decode8(c0, lut), _mm256_loadu_ps(x));
+    s0 = _mm256_fmadd_ps(decode8(_mm_srli_si128(c0, 8), lut), _mm256_loadu_ps(x + 8), s0);
+    __m256 s1 = _mm256_mul_ps(decode8(c1, lut), _mm256_loadu_ps(x + 16));
+    s1 = _mm256_fmadd_ps(decode8(_mm_srli_si128(c1, 8), lut), _mm256_loadu_ps(x + 24), s1);
+    acc = _mm256_fmadd_ps(s0, _mm256_set1_ps(e4m3(scales[2 * b])), acc);
+    acc = _mm256_fmadd_ps(s1, _mm256_set1_ps(e4m3(scales[2 * b + 1])), acc);
+  }
+  float r = hsum256(acc);
+  if (K % 32) r += dot_nvfp4_scalar(codes + (K / 32) * 16, scales + (K / 32) * 2,
+                                    v + (K / 32) * 32, K % 32);
+  return r;
+}
+
 __attribute__((target("avx2,fma"))) float dot_bf16_avx2(const uint16_t* w, const float* v,
                                                          int K) {
   __m256 acc0 = _mm256_setzero_ps(), acc1 = _mm256_setzero_ps();
@@ -235,6 +289,31 @@ __attribute__((target("avx512f,avx512bw"))) float dot_mxfp4_avx512(const uint8_t
     acc = _mm512_fmadd_ps(s, _mm512_set1_ps(e8m0(scales[b])), acc);
   }
   return _mm512_reduce_add_ps(acc);
+}
+
+__attribute__((target("avx512f,avx512bw"))) float dot_nvfp4_avx512(const uint8_t* codes,
+                                                                    const uint8_t* scales,
+                                                                    const float* v, int K) {
+  const __m512 lut = _mm512_setr_ps(0.f, 0.5f, 1.f, 1.5f, 2.f, 3.f, 4.f, 6.f, -0.f, -0.5f, -1.f,
+                                    -1.5f, -2.f, -3.f, -4.f, -6.f);
+  const __m128i m15 = _mm_set1_epi8(15);
+  __m512 acc = _mm512_setzero_ps();
+  for (int b = 0; b < K / 32; ++b) {          // two 16-element scale blocks
+    const __m128i raw = _mm_loadu_si128(reinterpret_cast<const __m128i*>(codes + b * 16));
+    const __m128i lo = _mm_and_si128(raw, m15);
+    const __m128i hi = _mm_and_si128(_mm_srli_epi16(raw, 4), m15);
+    const __m512 w0 = _mm512_permutexvar_ps(_mm512_cvtepu8_epi32(_mm_unpacklo_epi8(lo, hi)), lut);
+    const __m512 w1 = _mm512_permutexvar_ps(_mm512_cvtepu8_epi32(_mm_unpackhi_epi8(lo, hi)), lut);
+    const float* x = v + b * 32;
+    acc = _mm512_fmadd_ps(_mm512_mul_ps(w0, _mm512_loadu_ps(x)),
+                          _mm512_set1_ps(e4m3(scales[2 * b])), acc);
+    acc = _mm512_fmadd_ps(_mm512_mul_ps(w1, _mm512_loadu_ps(x + 16)),
+                          _mm512_set1_ps(e4m3(scales[2 * b + 1])), acc);
+  }
+  float r = _mm512_reduce_add_ps(acc);
+  if (K % 32) r += dot_nvfp4_scalar(codes + (K / 32) * 16, scales + (K / 32) * 2,
+                                    v + (K / 32) * 32, K % 32);
+  return r;
 }
 
 __attribute__((target("avx512f,avx512bw"))) float dot_bf16_avx512(const uint16_t* w,
@@ -277,6 +356,19 @@ float row_dot(const moe_desc* d, const Layout& L, const uint8_t* blk, int m, int
     if (have_avx2()) return dot_mxfp4_avx2(codes, scales, v, K);
     return dot_mxfp4_scalar(codes, scales, v, K);
   }
+  if (d->wtype == MOE_WTYPE_NVFP4) {
+    // codes [rows][K/2], E4M3 scales [rows][K/16]; the three fp32 matrix
+    // scales follow the down scales
+    const uint8_t* codes = blk + L.off[2 * m] + (size_t)r * (K / 2);
+    const uint8_t* scales = blk + L.off[2 * m + 1] + (size_t)r * (K / 16);
+    float g;
+    std::memcpy(&g, blk + L.off[5] + (size_t)d->hidden * d->inter / 16 + 4 * m, 4);
+    float acc;
+    if (have_avx512()) acc = dot_nvfp4_avx512(codes, scales, v, K);
+    else if (have_avx2()) acc = dot_nvfp4_avx2(codes, scales, v, K);
+    else acc = dot_nvfp4_scalar(codes, scales, v, K);
+    return acc * g;
+  }
   const uint16_t* w = reinterpret_cast<const uint16_t*>(blk + L.off[m]) + (size_t)r * K;
   if (have_avx512()) return dot_bf16_avx512(w, v, K);
   if (have_avx2()) return dot_bf16_avx2(w, v, K);
@@ -303,8 +395,9 @@ int moe_host_experts(const moe_desc* desc, const void* x, int32_t T, const int32
   if (T == 0) return MOE_OK;
   if (T < 0) return set_error(MOE_EINVAL, "T < 0");
   if (!x || !ids || !w || !host_pool || !y) return set_error(MOE_EINVAL, "null pointer");
-  if (desc->wtype != MOE_WTYPE_MXFP4 && desc->wtype != MOE_WTYPE_BF16)
-    return set_error(MOE_EUNSUPPORTED, "host experts run BF16 or MXFP4 weights");
+  if (desc->wtype != MOE_WTYPE_MXFP4 && desc->wtype != MOE_WTYPE_BF16 &&
+      desc->wtype != MOE_WTYPE_NVFP4)
+    return set_error(MOE_EUNSUPPORTED, "host experts run BF16, MXFP4 or NVFP4 weights");
   const int H = desc->hidden, I = desc->inter, E = desc->n_experts, k = desc->top_k;
   Layout L;
   layout(desc, L.off, &L.bytes);

@@ -1,8 +1,9 @@
 """The host side of the exact split (moe_host_experts) against the fp64 oracle,
 on the CPU.  Expert blocks are assembled here from seeded fp32 draws with the
-oracle's own BF16 / MXFP4 encoders, in the documented block layout (gate
-codes, gate scales, up codes, up scales, down codes, down scales; BF16: gate,
-up, down), so nothing on the input or expected side comes from the library.
+oracle's own BF16 / MXFP4 / NVFP4 encoders, in the documented block layout
+(gate codes, gate scales, up codes, up scales, down codes, down scales, and
+for NVFP4 the three fp32 matrix scales; BF16: gate, up, down), so nothing on
+the input or expected side comes from the library.
 """
 
 import os
@@ -30,17 +31,24 @@ def ops():
 
 def _block(mats, wtype):
     """One expert block in the documented layout, plus the exact fp64 values."""
-    parts, exact = [], []
+    parts, exact, gs = [], [], []
     for m in mats:
         a = m.numpy()
         if wtype == "bf16":
             bits = formats.bf16_round(a)
             parts.append(bits.astype(np.uint16).view(np.uint8).ravel())
             exact.append(formats.bf16_decode(bits))
+        elif wtype == "nvfp4":
+            codes, scales, g = formats.nvfp4_encode(a)
+            parts += [codes.ravel(), scales.ravel()]
+            gs.append(g)
+            exact.append(formats.nvfp4_decode(codes, scales, g))
         else:
             codes, scales = formats.mxfp4_encode(a)
             parts += [codes.ravel(), scales.ravel()]
             exact.append(formats.mxfp4_decode(codes, scales))
+    if wtype == "nvfp4":            # the three fp32 matrix scales after the down scales
+        parts.append(np.array(gs + [0.0], dtype=np.float32).view(np.uint8))
     raw = np.concatenate(parts)
     pad = (-raw.size) % 256
     return np.concatenate([raw, np.zeros(pad, np.uint8)]), tuple(exact)
@@ -88,6 +96,7 @@ def _expect(x, ids, w, exact, include=None):
 
 
 @pytest.mark.parametrize("name,wtype,T", [("tiny", "bf16", 4), ("tiny", "mxfp4", 4),
+                                          ("tiny", "nvfp4", 4), ("ragged_decode", "nvfp4", 5),
                                           ("ragged_decode", "mxfp4", 5),
                                           ("ragged_prefill", "mxfp4", 9),
                                           ("small_cache", "mxfp4", 1)])
