@@ -241,7 +241,7 @@ def prefill_stream_record(ops, Lp, host_pool, lb, T, n_layers, buffers):
             "layer_bytes": lb, "stream_GBps": lb * n_layers / (ms * 1e-3) / 1e9}
 
 
-def cache_record(ops, steps_limit=None, resize_at=None):
+def cache_record(ops, steps_limit=None, resize_at=None, q_sweep=None, sweep_steps=32):
     """Expert-cache decode: 64 LRU slots over a 256-expert pinned host pool,
     Zipf(1.1) trace drifting every 32 steps, q = q* from the measured PCIe
     rate and the measured host expert-kernel rate.  Per step: fills on a side
@@ -249,7 +249,11 @@ def cache_record(ops, steps_limit=None, resize_at=None):
     over the other misses (moe_host_experts on the host cores, while the GPU
     works), then the exact merge on the GPU.  resize_at {step: n_slots}:
     elastic rebuilds of the cache before those steps (shrinking in place,
-    growing into a pool allocated before the timed loop)."""
+    growing into a pool allocated before the timed loop).  q_sweep [q, ...]:
+    afterwards, the first sweep_steps steps again from a cold cache with each
+    fixed q (clamped per step to the misses and free slots): µs per step, the
+    fills, and the largest difference of y from the q = first-entry run (the
+    split is exact, so y should not depend on q beyond rounding)."""
     name = "glm_cache_decode"
     s = synth.SHAPES[name]
     H, I, E, k, slots = s["hidden"], s["inter"], s["n_experts"], s["top_k"], s["slots"]
@@ -334,6 +338,45 @@ def cache_record(ops, steps_limit=None, resize_at=None):
     torch.cuda.synchronize()
     wall = time.time() - wall0
     ms = t_start.elapsed_time(t_end)
+    sweep = {}
+    if q_sweep:
+        ys_ref = None
+        for qf in q_sweep:
+            pool_q = torch.empty(slots * eb, dtype=torch.uint8, device="cuda")
+            table_q = torch.empty((1, E), dtype=torch.int32, device="cuda")
+            cq = ops.ExpertCache(host_pool, 1, E, eb, pool_q, slots, table_q)
+            ys = torch.empty((sweep_steps, H), dtype=torch.float32, device="cuda")
+            hp = torch.zeros((sweep_steps, H), dtype=torch.float32).pin_memory()
+            n_fill = 0
+            a0 = torch.cuda.Event(enable_timing=True)
+            a1 = torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            a0.record(comp)
+            for st in range(sweep_steps):
+                plan = cq.plan(0, ids_tr[st], w_tr[st], qf)
+                n_fill += plan.q
+                cq.fill(plan, side, comp)
+                ops.decode(desc, xs[st:st + 1], d_ids[st:st + 1], d_w[st:st + 1], pool_q,
+                           ys[st:st + 1], ws, slot_of=table_q[0])
+                cq.release(plan, comp)
+                host = set(int(e) for e in ops.plan_dict(plan)["host"])
+                if host:
+                    inc = torch.tensor([[int(e) in host for e in ids_tr[st]]],
+                                       dtype=torch.uint8)
+                    ops.host_experts(desc, xs_host[st:st + 1], h_ids[st:st + 1],
+                                     h_w[st:st + 1], host_pool, hp[st:st + 1], include=inc)
+                dev_part.copy_(hp[st:st + 1], non_blocking=True)
+                ops.merge_partials(ys[st:st + 1], dev_part, ys[st:st + 1])
+            a1.record(comp)
+            torch.cuda.synchronize()
+            yc = ys.cpu().double()
+            if ys_ref is None:
+                ys_ref = yc
+            diff = float(((yc - ys_ref).abs().amax(dim=1) /
+                          ys_ref.abs().amax(dim=1).clamp_min(1e-30)).max())
+            sweep[str(qf)] = {"us_per_step": a0.elapsed_time(a1) * 1e3 / sweep_steps,
+                              "filled": n_fill, "max_rel_diff_y": diff}
+            del cq
     return {
         "steps": steps, "slots": slots, "us_per_step": ms * 1e3 / steps,
         "wall_us_per_step": wall * 1e6 / steps,
@@ -348,6 +391,7 @@ def cache_record(ops, steps_limit=None, resize_at=None):
             "rebuild_ms": [a.elapsed_time(b) for _, _, a, b in rebuild_ev],
             "miss_rate_per_budget": [m / max(1, h + m) for h, m in phases]}
            if rebuild_ev else {}),
+        **({"q_sweep_cold_steps": sweep_steps, "q_sweep": sweep} if sweep else {}),
     }
 
 
@@ -486,7 +530,7 @@ def main():
             details["prefill_error"] = repr(ex)
         try:
             log("cache decode trace")
-            details["glm_cache_decode"] = cache_record(ops)
+            details["glm_cache_decode"] = cache_record(ops, q_sweep=[0, 1, 2, 4, 8])
             log(json.dumps(details["glm_cache_decode"]))
         except Exception as ex:
             details["glm_cache_decode_error"] = repr(ex)

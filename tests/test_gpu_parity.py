@@ -639,15 +639,16 @@ def test_cache_elastic_rebuild_keeps_outputs(ops):
         assert olayer.row_rel_error(y.cpu().numpy(), full) < TOL, st
 
 
-def test_cache_trace_with_host_experts_merges_to_full_layer(ops):
+@pytest.mark.parametrize("wtype", ["mxfp4", "nvfp4"])
+def test_cache_trace_with_host_experts_merges_to_full_layer(ops, wtype):
     """The whole split: GPU partial over resident + filled experts, host
     partial over the other misses from moe_host_experts reading the pinned
     pool, merged on the GPU, equals the full layer (oracle)."""
-    _say("cache trace + host experts")
+    _say("cache trace + host experts", wtype)
     name = "small_cache"
     s = synth.SHAPES[name]
     E, k, slots, steps = s["n_experts"], s["top_k"], s["slots"], 24
-    L = GpuLayer(name)
+    L = GpuLayer(name, wtype=wtype)
     eb = L.expert_bytes
     host_pool = torch.empty(E * eb, dtype=torch.uint8).pin_memory()
     host_pool.copy_(L.pool.cpu())
