@@ -39,6 +39,8 @@ DECODE_SOURCES = ["decode_impl.hpp", "decode_launch.hpp", "decode.hip", "decode_
                   "decode_mxfp4.hip", "device.hpp"]
 PREFILL_SOURCES = ["prefill.hip", "device.hpp"]
 PROBE_BYTES = 256 << 20
+SIMDS = 256 * 4                     # MI355X: 256 compute units x 4 SIMDs
+XCDS = 8                            # GRBM_GUI_ACTIVE comes summed over the 8 XCDs
 COPY_BYTES = 256 << 20
 
 
@@ -214,6 +216,23 @@ def cmd_summarize(args):
               f"- kernel sources hash: {rec['source_hash']}", "",
               "Scaled HBM traffic per dispatch, every kernel of the run:", "",
               "| kernel | fetch MB | write MB |", "|---|---|---|"] + per
+    if args.mfma:
+        lines += ["", "Matrix-core counters per dispatch (rocprofv3 --pmc "
+                  "SQ_INSTS_VALU_MFMA_MOPS_F6F4 SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE):", "",
+                  f"    {args.cmd_mfma}", "",
+                  "busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / "
+                  f"{XCDS} XCDs x {SIMDS} SIMDs); FP4 TFLOP executed = MOPS_F6F4 x 512 / 1e12 "
+                  "(padding rows of partly filled tiles included)", "",
+                  "| kernel | FP4 TFLOP executed | MFMA busy |", "|---|---|---|"]
+        mops = _counter_rows(args.mfma, "SQ_INSTS_VALU_MFMA_MOPS_F6F4")
+        busy = _counter_rows(args.mfma, "SQ_VALU_MFMA_BUSY_CYCLES")
+        gui = _counter_rows(args.mfma, "GRBM_GUI_ACTIVE")
+        for name in sorted({n for n, _ in mops if "gemm" in n}):
+            mo = _mean([v for n, v in mops if n == name])
+            bu = _mean([v for n, v in busy if n == name])
+            gu = _mean([v for n, v in gui if n == name])
+            frac = bu / (gu / XCDS * SIMDS) if bu is not None and gu else float("nan")
+            lines.append(f"| {name[:72]} | {mo * 512 / 1e12:.3f} | {100 * frac:.1f}% |")
     if args.note:
         lines += ["", args.note]
     with open(os.path.join(ROOT, "profiles", f"{args.name}.md"), "w") as f:
@@ -245,6 +264,8 @@ def main():
     s.add_argument("--cmd-stats", default="")
     s.add_argument("--cmd-fetch", default="")
     s.add_argument("--cmd-write", default="")
+    s.add_argument("--mfma", default=None, help="counter csv of the matrix-core pass")
+    s.add_argument("--cmd-mfma", default="")
     a = ap.parse_args()
     if a.cmd == "run":
         cmd_run(a)
