@@ -44,6 +44,10 @@ SHAPES = {
     "ragged_prefill": dict(hidden=512, inter=256, n_experts=13, top_k=4,
                            shared=True, wtype="mxfp4", tokens=(1, 77, 700),
                            layers=1),
+    # prefill with K = H not a multiple of 512 (the narrow GEMM scheme) and
+    # K = I one (the wide scheme)
+    "mixed_prefill": dict(hidden=640, inter=1024, n_experts=9, top_k=3, shared=True,
+                          wtype="mxfp4", tokens=(150, 400), layers=1),
     "small_cache": dict(hidden=256, inter=128, n_experts=32, top_k=4,
                         shared=False, wtype="mxfp4", tokens=(1,), layers=2,
                         slots=8, steps=64, zipf=1.1, drift=16),

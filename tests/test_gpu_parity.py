@@ -443,7 +443,8 @@ def test_route_decode_partial_subset(ops):
 
 # ---------------------------------------------------------------- prefill
 @pytest.mark.parametrize("name,T", [("tiny", 4), ("tiny", 300), ("ragged_prefill", 1),
-                                    ("ragged_prefill", 77), ("ragged_prefill", 700)])
+                                    ("ragged_prefill", 77), ("ragged_prefill", 700),
+                                    ("mixed_prefill", 150), ("mixed_prefill", 400)])
 def test_prefill_small(ops, name, T):
     _say("prefill", name, T)
     L = GpuLayer(name, wtype="mxfp4")
