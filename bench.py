@@ -432,8 +432,19 @@ def cpu_baseline(name, T, n_layers_sample, min_seconds=10.0):
             break
     el = time.time() - t0
     per = el / (reps * n_layers_sample * T)
+    cpu = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas = sorted({f"{i.get('internal_api')} {i.get('version')}" for i in info
+                   if i.get("user_api") == "blas"})
     return {"value": per * 1e6, "unit": "us/token/layer", "cores": threads,
-            "kind": "oracle",
+            "kind": "oracle", "cpu": cpu, "blas": blas, "os_cpu_count": os.cpu_count(),
             "sample": f"{name} T={T}: route + combine of {n_layers_sample} layers "
                       f"(fp64 NumPy), repeated {reps}x over {el:.1f}s; weights decoded "
                       f"to fp64 before timing"}
