@@ -316,44 +316,6 @@ __attribute__((target("avx512f,avx512bw"))) float dot_nvfp4_avx512(const uint8_t
   return r;
 }
 
-// two MXFP4 rows against the same vector: each x load serves both rows
-__attribute__((target("avx512f,avx512bw"))) void dot2_mxfp4_avx512(
-    const uint8_t* ca, const uint8_t* sa, const uint8_t* cb, const uint8_t* sb, const float* v,
-    int K, float& ra, float& rb) {
-  const __m512 lut = _mm512_setr_ps(0.f, 0.5f, 1.f, 1.5f, 2.f, 3.f, 4.f, 6.f, -0.f, -0.5f, -1.f,
-                                    -1.5f, -2.f, -3.f, -4.f, -6.f);
-  const __m128i m15 = _mm_set1_epi8(15);
-  __m512 acca = _mm512_setzero_ps(), accb = _mm512_setzero_ps();
-  for (int b = 0; b < K / 32; ++b) {
-    const float* x = v + b * 32;
-    const __m512 x0 = _mm512_loadu_ps(x), x1 = _mm512_loadu_ps(x + 16);
-    {
-      const __m128i raw = _mm_loadu_si128(reinterpret_cast<const __m128i*>(ca + b * 16));
-      const __m128i lo = _mm_and_si128(raw, m15);
-      const __m128i hi = _mm_and_si128(_mm_srli_epi16(raw, 4), m15);
-      const __m512 w0 = _mm512_permutexvar_ps(_mm512_cvtepu8_epi32(_mm_unpacklo_epi8(lo, hi)),
-                                              lut);
-      const __m512 w1 = _mm512_permutexvar_ps(_mm512_cvtepu8_epi32(_mm_unpackhi_epi8(lo, hi)),
-                                              lut);
-      const __m512 t = _mm512_fmadd_ps(w1, x1, _mm512_mul_ps(w0, x0));
-      acca = _mm512_fmadd_ps(t, _mm512_set1_ps(e8m0(sa[b])), acca);
-    }
-    {
-      const __m128i raw = _mm_loadu_si128(reinterpret_cast<const __m128i*>(cb + b * 16));
-      const __m128i lo = _mm_and_si128(raw, m15);
-      const __m128i hi = _mm_and_si128(_mm_srli_epi16(raw, 4), m15);
-      const __m512 w0 = _mm512_permutexvar_ps(_mm512_cvtepu8_epi32(_mm_unpacklo_epi8(lo, hi)),
-                                              lut);
-      const __m512 w1 = _mm512_permutexvar_ps(_mm512_cvtepu8_epi32(_mm_unpackhi_epi8(lo, hi)),
-                                              lut);
-      const __m512 t = _mm512_fmadd_ps(w1, x1, _mm512_mul_ps(w0, x0));
-      accb = _mm512_fmadd_ps(t, _mm512_set1_ps(e8m0(sb[b])), accb);
-    }
-  }
-  ra = _mm512_reduce_add_ps(acca);
-  rb = _mm512_reduce_add_ps(accb);
-}
-
 __attribute__((target("avx512f,avx512bw"))) float dot_bf16_avx512(const uint16_t* w,
                                                                    const float* v, int K) {
   __m512 acc = _mm512_setzero_ps();
@@ -411,22 +373,6 @@ float row_dot(const moe_desc* d, const Layout& L, const uint8_t* blk, int m, int
   if (have_avx512()) return dot_bf16_avx512(w, v, K);
   if (have_avx2()) return dot_bf16_avx2(w, v, K);
   return dot_bf16_scalar(w, v, K);
-}
-
-// dots of row r1 of matrix m1 and row r2 of matrix m2 with the same v
-void row_dot2(const moe_desc* d, const Layout& L, const uint8_t* blk, int m1, int r1, int m2,
-              int r2, const float* v, float& o1, float& o2) {
-  const int K1 = m1 < 2 ? d->hidden : d->inter, K2 = m2 < 2 ? d->hidden : d->inter;
-  if (d->wtype == MOE_WTYPE_MXFP4 && K1 == K2 && have_avx512()) {
-    const int K = K1;
-    dot2_mxfp4_avx512(blk + L.off[2 * m1] + (size_t)r1 * (K / 2),
-                      blk + L.off[2 * m1 + 1] + (size_t)r1 * (K / 32),
-                      blk + L.off[2 * m2] + (size_t)r2 * (K / 2),
-                      blk + L.off[2 * m2 + 1] + (size_t)r2 * (K / 32), v, K, o1, o2);
-    return;
-  }
-  o1 = row_dot(d, L, blk, m1, r1, v);
-  o2 = row_dot(d, L, blk, m2, r2, v);
 }
 
 }  // namespace
@@ -492,8 +438,8 @@ int moe_host_experts(const moe_desc* desc, const void* x, int32_t T, const int32
       for (int r = task * kRows; r < r1; ++r) {
         for (int q = 0; q < n; ++q) {
           const float* xv = xf.data() + (size_t)en[q].first * H;
-          float g, u;
-          row_dot2(desc, L, blk, 0, r, 1, r, xv, g, u);
+          const float g = row_dot(desc, L, blk, 0, r, xv);
+          const float u = row_dot(desc, L, blk, 1, r, xv);
           h[(size_t)q * I + r] = g / (1.0f + std::exp(-g)) * u;
         }
       }
@@ -501,18 +447,10 @@ int moe_host_experts(const moe_desc* desc, const void* x, int32_t T, const int32
     // down rows -> y (each task owns its output rows)
     P.run((H + kRows - 1) / kRows, [&](int task) {
       const int r1 = std::min(H, (task + 1) * kRows);
-      for (int r = task * kRows; r < r1; r += 2) {
+      for (int r = task * kRows; r < r1; ++r) {
         for (int q = 0; q < n; ++q) {
-          const float* hv = h.data() + (size_t)q * I;
-          float* yr = y + (size_t)en[q].first * H;
-          if (r + 1 < r1) {
-            float o0, o1;
-            row_dot2(desc, L, blk, 2, r, 2, r + 1, hv, o0, o1);
-            yr[r] += en[q].second * o0;
-            yr[r + 1] += en[q].second * o1;
-          } else {
-            yr[r] += en[q].second * row_dot(desc, L, blk, 2, r, hv);
-          }
+          const float o = row_dot(desc, L, blk, 2, r, h.data() + (size_t)q * I);
+          y[(size_t)en[q].first * H + r] += en[q].second * o;
         }
       }
     });
