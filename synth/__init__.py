@@ -44,6 +44,11 @@ SHAPES = {
     "ragged_prefill": dict(hidden=512, inter=256, n_experts=13, top_k=4,
                            shared=True, wtype="mxfp4", tokens=(1, 77, 700),
                            layers=1),
+    # the largest expert count one decode launch takes (1024: 16 logits per
+    # lane in the wave top-k); H = 4096 so that the router's logits spread
+    # enough for most tokens' k-th and (k+1)-th probabilities to be apart
+    "many_experts": dict(hidden=4096, inter=128, n_experts=1024, top_k=8, shared=False,
+                         wtype="mxfp4", tokens=(1, 5, 16), layers=1),
     # prefill with K = H not a multiple of 512 (the narrow GEMM scheme) and
     # K = I one (the wide scheme)
     "mixed_prefill": dict(hidden=640, inter=1024, n_experts=9, top_k=3, shared=True,

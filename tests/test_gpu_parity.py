@@ -201,7 +201,8 @@ def _check_route(ops, name, T, renorm=False, layer=0):
                                     ("dsv4_mxfp4_decode", 16), ("dsv4_mxfp4_decode", 300),
                                     ("glm_cache_decode", 3), ("ragged_decode", 64),
                                     ("qwen_bf16_decode", 130), ("ragged_decode", 200),
-                                    ("dsv4_mxfp4_prefill", 4096)])
+                                    ("dsv4_mxfp4_prefill", 4096), ("many_experts", 1),
+                                    ("many_experts", 16), ("many_experts", 100)])
 def test_route_topk_exact(ops, name, T):
     _say("route", name, T)
     _check_route(ops, name, T)
@@ -364,7 +365,10 @@ def _check_ids(L, x, gi, gw, renorm=False):
                                           ("glm_cache_decode", 1, None),
                                           ("tiny", 4, "nvfp4"),
                                           ("ragged_decode", 9, "nvfp4"),
-                                          ("qwen_bf16_decode", 4, "nvfp4")])
+                                          ("qwen_bf16_decode", 4, "nvfp4"),
+                                          ("many_experts", 1, None),
+                                          ("many_experts", 5, None),
+                                          ("many_experts", 16, None)])
 def test_route_decode(ops, name, T, wtype):
     """Router + experts + combine in one call (one persistent kernel for T <= 4)."""
     _say("route_decode", name, T, wtype)
