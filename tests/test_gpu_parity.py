@@ -396,6 +396,23 @@ def test_route_decode(ops, name, T, wtype):
         assert _counters_clear(ws, 2 * _launches(L, T) + _launches(L, T - 1))
 
 
+@pytest.mark.parametrize("name,T,wtype", [("tiny", 4, "bf16"), ("qwen_bf16_decode", 1, None),
+                                          ("qwen_bf16_decode", 16, None),
+                                          ("ragged_decode", 9, None)])
+def test_route_decode_renorm(ops, name, T, wtype):
+    """Renormalised top-k weights in the one-kernel path: the rank and the
+    wave-arg-max top-k, the one-wave and the workgroup expert list."""
+    _say("route_decode renorm", name, T)
+    L = GpuLayer(name, wtype=wtype, renorm=True)
+    x = L.tokens(T)
+    ids, w, y, _ = _route_decode(ops, L, x)
+    gi, gw = ids.cpu().numpy(), w.cpu().numpy()
+    _check_ids(L, x, gi, gw, renorm=True)
+    assert np.allclose(gw.sum(axis=1), 1.0, atol=1e-6)
+    ref = _oracle_out(L, x, gi, gw)
+    assert olayer.row_rel_error(y.cpu().numpy(), ref) < TOL
+
+
 @pytest.mark.parametrize("T,sample", [(1, [0]), (4, [1])])
 def test_route_decode_dsv4_full_sampled(ops, T, sample):
     _say("route_decode dsv4", T)
