@@ -459,8 +459,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU: the layer runs on a single MI355X; "
-              "multi-GPU sharding is not part of this build (use --gpus 1)", file=sys.stderr)
+        print("bench.py measures one GPU: the layer runs on a single MI355X, and "
+              "sharding it across GPUs is not implemented (use --gpus 1)", file=sys.stderr)
         sys.exit(2)
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
