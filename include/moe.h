@@ -230,6 +230,11 @@ int moe_debug_mfma_fp4_tile(const uint8_t* a_codes, const uint8_t* a_scales,
                             const uint8_t* b_codes, const uint8_t* b_scales,
                             float* out, void* stream);
 
+/* moe_debug_wave_scan: out[64 w + l] = in[64 w] + ... + in[64 w + l] for
+ * w < n_waves, l < 64 (int32, device buffers of 64 n_waves), through the DPP
+ * wave scan the decode kernel builds its expert list with (test hook). */
+int moe_debug_wave_scan(const int32_t* in, int32_t* out, int32_t n_waves, void* stream);
+
 /* moe_debug_read_probe: read `bytes` (multiple of 16) of device memory with
  * 16-byte loads from `blocks` workgroups of 256 threads, 8 loads in flight
  * per thread; writes nothing unless a checksum hits a magic value.  Timed by

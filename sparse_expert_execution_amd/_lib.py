@@ -33,7 +33,7 @@ PLAN_MAX = 256
 EXPORTS = (
     "moe_expert_layout", "moe_workspace_bytes", "moe_route", "moe_decode",
     "moe_route_decode", "moe_prefill", "moe_merge_partials", "moe_quantize_mxfp4",
-    "moe_pack_expert", "moe_debug_dequant_mxfp4", "moe_debug_mfma_fp4_tile", "moe_debug_read_probe", "moe_qstar",
+    "moe_pack_expert", "moe_debug_dequant_mxfp4", "moe_debug_mfma_fp4_tile", "moe_debug_read_probe", "moe_debug_wave_scan", "moe_qstar",
     "moe_planner_create", "moe_planner_destroy", "moe_planner_set_bandwidths",
     "moe_planner_plan", "moe_planner_rollback", "moe_planner_slot_table",
     "moe_planner_resize", "moe_planner_n_slots", "moe_cache_resize",
@@ -102,6 +102,7 @@ def lib():
         "moe_debug_dequant_mxfp4": (ctypes.c_int, [P, P, I64, P, P]),
         "moe_debug_mfma_fp4_tile": (ctypes.c_int, [P, P, P, P, P, P]),
         "moe_debug_read_probe": (ctypes.c_int, [P, SZ, I32, P, P]),
+        "moe_debug_wave_scan": (ctypes.c_int, [P, P, I32, P]),
         "moe_qstar": (I32, [I32, D, D]),
         "moe_planner_create": (ctypes.c_int, [ctypes.POINTER(P), I32, I32, I32]),
         "moe_planner_destroy": (None, [P]),

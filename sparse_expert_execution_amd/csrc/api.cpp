@@ -393,6 +393,12 @@ int moe_debug_mfma_fp4_tile(const uint8_t* a_codes, const uint8_t* a_scales,
                     "moe_debug_mfma_fp4_tile");
 }
 
+int moe_debug_wave_scan(const int32_t* in, int32_t* out, int32_t n_waves, void* stream) {
+  if (!in || !out || n_waves < 1) return set_error(MOE_EINVAL, "bad wave-scan arguments");
+  return hip_status(moe::launch_wave_scan(in, out, n_waves, as_stream(stream)),
+                    "moe_debug_wave_scan");
+}
+
 int moe_debug_read_probe(const void* buf, size_t bytes, int32_t blocks, uint32_t* out,
                          void* stream) {
   if (!buf || !out || blocks < 1 || !aligned(buf, 16))

@@ -472,8 +472,14 @@ __device__ void rank_topk(const DecArgs& a, DecLds& S, unsigned gen) {
   __syncthreads();
 }
 
-// inclusive prefix sum over the lanes of a wave
+// inclusive prefix sum over the lanes of a wave (all lanes active): the DPP
+// scan, or log2(64) steps of __shfl_up.  The two are equal; which one a
+// kernel takes is a measured choice (the DPP form took the DeepSeek-shaped
+// MXFP4 T=1 call from 44.8 to 43.7 us, while the Qwen-shaped BF16 call went
+// from 28.4 to 28.8 us, i.e. code placement, not the scan, decides there).
+template <bool DPP>
 __device__ __forceinline__ int wave_scan(int v) {
+  if (DPP) return wave_scan_dpp(v);
   const int lane = threadIdx.x & 63;
 #pragma unroll
   for (int d = 1; d < 64; d <<= 1) {
@@ -491,7 +497,7 @@ __device__ __forceinline__ int wave_scan(int v) {
 // shared expert's T entries and the virtual units of the down phase.  from_zsel:
 // the gate weights come from the selected logits and the softmax statistics
 // (renormalised here when asked), else they are in L.w.
-template <int CE>
+template <int CE, bool DPP>
 __device__ void build_units_wave(const DecArgs& a, DecLds& S, bool route, bool from_zsel) {
   PlanLds& L = S.p;
   const int lane = threadIdx.x & 63;
@@ -542,7 +548,7 @@ __device__ void build_units_wave(const DecArgs& a, DecLds& S, bool route, bool f
   const bool sh = a.shared != nullptr;
   const int n_units = n_routed + (sh ? 1 : 0);
   const int c = lane < n_routed ? L.cnt[lane] : (sh && lane == n_routed ? T : 0);
-  const int incl = wave_scan(c);
+  const int incl = wave_scan<DPP>(c);
   if (lane < n_units) L.unit_start[lane] = incl - c;
   if (lane == 0) L.unit_start[n_units] = __builtin_amdgcn_readlane(incl, 63);
   if (sh && lane == n_routed) L.unit_slot[lane] = -1;
@@ -564,7 +570,7 @@ __device__ void build_units_wave(const DecArgs& a, DecLds& S, bool route, bool f
   }
   // virtual units: each unit's entries in chunks of CE
   const int nv = lane < n_units ? (c + CE - 1) / CE : 0;
-  const int vincl = wave_scan(nv);
+  const int vincl = wave_scan<DPP>(nv);
   for (int j = 0; j < nv; ++j) {
     const int q = vincl - nv + j;
     L.vu_unit[q] = lane;
@@ -581,7 +587,7 @@ __device__ void build_units_wave(const DecArgs& a, DecLds& S, bool route, bool f
 // Expert list of this launch, built the same way in every workgroup: the
 // distinct resident experts in order of first appearance over the (token,
 // rank) pairs, each with its pairs, then the shared expert.
-template <int M, int CE>
+template <int M, int CE, bool DPP>
 __device__ void build_units(const DecArgs& a, DecLds& S, bool route, bool timing, unsigned gen) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int T = a.T, k = a.k, E = a.E, P = T * k;
@@ -606,7 +612,7 @@ __device__ void build_units(const DecArgs& a, DecLds& S, bool route, bool timing
   }
   stamp(timing, a, 9);
   if (P + (a.shared ? 1 : 0) <= 64) {
-    if (wave == 0) build_units_wave<CE>(a, S, route, from_zsel);
+    if (wave == 0) build_units_wave<CE, DPP>(a, S, route, from_zsel);
     __syncthreads();
     return;
   }
@@ -1286,7 +1292,7 @@ __global__ __launch_bounds__(kT) void decode_kernel(DecArgs a) {
   stamp(timing, a, 8);
 
   // 2. the expert list
-  build_units<M, CE>(a, S, route, timing, gen);
+  build_units<M, CE, WT != 1>(a, S, route, timing, gen);
   stamp(timing, a, 1);
   const int n_routed = S.p.n_routed;
 

@@ -260,6 +260,18 @@ hipError_t launch_merge(const float* a, const float* b, float* y, size_t n, hipS
   return hipGetLastError();
 }
 
+// debug: one inclusive wave scan per 64 values
+__global__ __launch_bounds__(64) void wave_scan_kernel(const int32_t* __restrict__ in,
+                                                       int32_t* __restrict__ out) {
+  const int64_t i = (int64_t)blockIdx.x * 64 + threadIdx.x;
+  out[i] = wave_scan_dpp(in[i]);
+}
+
+hipError_t launch_wave_scan(const int32_t* in, int32_t* out, int n_waves, hipStream_t st) {
+  hipLaunchKernelGGL(wave_scan_kernel, dim3(n_waves), dim3(64), 0, st, in, out);
+  return hipGetLastError();
+}
+
 hipError_t launch_read_probe(const void* src, size_t bytes, int blocks, uint32_t* out,
                              hipStream_t st) {
   const int64_t n16 = (int64_t)(bytes / 16);

@@ -99,6 +99,7 @@ hipError_t launch_mfma_fp4_tile(const uint8_t* a_codes, const uint8_t* a_scales,
                                 const uint8_t* b_codes, const uint8_t* b_scales,
                                 float* out, hipStream_t st);
 
+hipError_t launch_wave_scan(const int32_t* in, int32_t* out, int n_waves, hipStream_t st);
 hipError_t launch_read_probe(const void* src, size_t bytes, int blocks, uint32_t* out,
                              hipStream_t st);
 

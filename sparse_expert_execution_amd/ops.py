@@ -100,6 +100,15 @@ def read_probe(buf, blocks, out, stream=None):
                                      _ptr(out), _stream(stream)), "moe_debug_read_probe")
 
 
+def wave_scan(inp, out, stream=None):
+    """Inclusive scan of each group of 64 int32 values (device tensors)."""
+    if inp.dtype != torch.int32 or out.dtype != torch.int32 or inp.numel() % 64 or \
+            out.numel() != inp.numel() or not inp.is_contiguous() or not out.is_contiguous():
+        raise ValueError("wave_scan takes contiguous int32 tensors of 64 n values")
+    check(lib().moe_debug_wave_scan(_ptr(inp), _ptr(out), inp.numel() // 64, _stream(stream)),
+          "moe_debug_wave_scan")
+
+
 def qstar(m, b_pcie, b_host):
     return lib().moe_qstar(m, b_pcie, b_host)
 

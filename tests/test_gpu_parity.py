@@ -129,6 +129,22 @@ def test_nvfp4_pack_bit_exact(ops):
             assert np.array_equal(c, rc), name
 
 
+def test_wave_scan_dpp(ops):
+    """The DPP inclusive wave scan the decode expert list uses, against a
+    prefix sum: counts, signed values, and values with every row boundary
+    set."""
+    _say("wave scan")
+    rng = np.random.default_rng(7)
+    vals = np.concatenate([rng.integers(0, 9, 64 * 16), rng.integers(-1000, 1000, 64 * 16),
+                           np.where(np.arange(64 * 4) % 16 == 15, 1 << 20, 1)]).astype(np.int32)
+    inp = torch.from_numpy(vals).cuda()
+    out = torch.empty_like(inp)
+    ops.wave_scan(inp, out)
+    torch.cuda.synchronize()
+    ref = np.cumsum(vals.reshape(-1, 64).astype(np.int64), axis=1).astype(np.int32).ravel()
+    assert np.array_equal(out.cpu().numpy(), ref)
+
+
 def test_merge_exact(ops):
     _say("merge")
     rng = np.random.default_rng(3)
