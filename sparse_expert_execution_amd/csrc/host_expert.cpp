@@ -331,6 +331,37 @@ __attribute__((target("avx512f,avx512bw"))) float dot_bf16_avx512(const uint16_t
   return s;
 }
 
+// MXFP4 row against a BF16 vector with BF16 dot products: every e2m1 value
+// is exact in BF16 and so is x, so the products are exact and only the fp32
+// sums round.  The 16 signed e2m1 values as BF16 bits, a code its index.
+__attribute__((target("avx512f,avx512bw,avx512bf16"))) float dot_mxfp4_bf16dp(
+    const uint8_t* codes, const uint8_t* scales, const uint16_t* xb, int K) {
+  const __m512i lut = _mm512_setr_epi32(
+      0x3F000000, 0x3FC03F80, 0x40404000, 0x40C04080,     // +0, 0.5, 1, 1.5, 2, 3, 4, 6
+      (int)0xBF008000, (int)0xBFC0BF80, (int)0xC040C000, (int)0xC0C0C080,   // -0 .. -6
+      0, 0, 0, 0, 0, 0, 0, 0);
+  const __m128i m15 = _mm_set1_epi8(15);
+  __m512 acc = _mm512_setzero_ps();
+  for (int b = 0; b < K / 32; ++b) {
+    const __m128i raw = _mm_loadu_si128(reinterpret_cast<const __m128i*>(codes + b * 16));
+    const __m128i lo = _mm_and_si128(raw, m15);
+    const __m128i hi = _mm_and_si128(_mm_srli_epi16(raw, 4), m15);
+    const __m256i c = _mm256_set_m128i(_mm_unpackhi_epi8(lo, hi), _mm_unpacklo_epi8(lo, hi));
+    const __m512i w = _mm512_permutexvar_epi16(_mm512_cvtepu8_epi16(c), lut);
+    const __m512i x = _mm512_loadu_si512(xb + b * 32);
+    const __m512 t = _mm512_dpbf16_ps(_mm512_setzero_ps(), (__m512bh)w, (__m512bh)x);
+    acc = _mm512_fmadd_ps(t, _mm512_set1_ps(e8m0(scales[b])), acc);
+  }
+  return _mm512_reduce_add_ps(acc);
+}
+
+bool have_avx512bf16() {
+  static const bool v = __builtin_cpu_supports("avx512f") &&
+                        __builtin_cpu_supports("avx512bw") &&
+                        __builtin_cpu_supports("avx512bf16");
+  return v;
+}
+
 bool have_avx512() {
   static const bool v = __builtin_cpu_supports("avx512f") && __builtin_cpu_supports("avx512bw");
   return v;
@@ -438,8 +469,18 @@ int moe_host_experts(const moe_desc* desc, const void* x, int32_t T, const int32
       for (int r = task * kRows; r < r1; ++r) {
         for (int q = 0; q < n; ++q) {
           const float* xv = xf.data() + (size_t)en[q].first * H;
-          const float g = row_dot(desc, L, blk, 0, r, xv);
-          const float u = row_dot(desc, L, blk, 1, r, xv);
+          float g, u;
+          if (desc->wtype == MOE_WTYPE_MXFP4 && have_avx512bf16()) {
+            // gate/up against x in BF16 (exact) with BF16 dot products
+            const uint16_t* xr = xb + (size_t)en[q].first * H;
+            g = dot_mxfp4_bf16dp(blk + L.off[0] + (size_t)r * (H / 2),
+                                 blk + L.off[1] + (size_t)r * (H / 32), xr, H);
+            u = dot_mxfp4_bf16dp(blk + L.off[2] + (size_t)r * (H / 2),
+                                 blk + L.off[3] + (size_t)r * (H / 32), xr, H);
+          } else {
+            g = row_dot(desc, L, blk, 0, r, xv);
+            u = row_dot(desc, L, blk, 1, r, xv);
+          }
           h[(size_t)q * I + r] = g / (1.0f + std::exp(-g)) * u;
         }
       }
