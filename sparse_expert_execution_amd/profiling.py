@@ -166,8 +166,8 @@ def cmd_summarize(args):
                  f"    {args.cmd_stats}", ""] + _stats_table(stats)
         if args.note:
             lines += ["", args.note]
-        os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
-        with open(os.path.join(ROOT, "profiles", f"{args.name}.md"), "w") as f:
+        os.makedirs(args.out_dir, exist_ok=True)
+        with open(os.path.join(args.out_dir, f"{args.name}.md"), "w") as f:
             f.write("\n".join(lines) + "\n")
         print("\n".join(lines))
         return
@@ -195,8 +195,8 @@ def cmd_summarize(args):
            "fetch_kib_raw": f_dec, "write_kib_raw": w_dec,
            "probe_fetch_kib": f_probe, "copy_write_kib": w_copy,
            "cmd_fetch": args.cmd_fetch, "cmd_write": args.cmd_write}
-    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
-    with open(os.path.join(ROOT, "profiles", f"{args.name}.traffic.json"), "w") as f:
+    os.makedirs(args.out_dir, exist_ok=True)
+    with open(os.path.join(args.out_dir, f"{args.name}.traffic.json"), "w") as f:
         json.dump(rec, f, indent=1)
     lines = [f"# {args.name}", "", "Kernel trace (rocprofv3 --kernel-trace --stats):", "",
              f"    {args.cmd_stats}", ""] + _stats_table(stats)
@@ -235,12 +235,12 @@ def cmd_summarize(args):
             lines.append(f"| {name[:72]} | {mo * 512 / 1e12:.3f} | {100 * frac:.1f}% |")
     if args.note:
         lines += ["", args.note]
-    with open(os.path.join(ROOT, "profiles", f"{args.name}.md"), "w") as f:
+    with open(os.path.join(args.out_dir, f"{args.name}.md"), "w") as f:
         f.write("\n".join(lines) + "\n")
     print(json.dumps(rec))
 
 
-def main():
+def main(argv=None):
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
     r = sub.add_parser("run")
@@ -265,8 +265,9 @@ def main():
     s.add_argument("--cmd-fetch", default="")
     s.add_argument("--cmd-write", default="")
     s.add_argument("--mfma", default=None, help="counter csv of the matrix-core pass")
+    s.add_argument("--out-dir", default=os.path.join(ROOT, "profiles"))
     s.add_argument("--cmd-mfma", default="")
-    a = ap.parse_args()
+    a = ap.parse_args(argv)
     if a.cmd == "run":
         cmd_run(a)
     elif a.cmd == "run-prefill":
