@@ -23,6 +23,7 @@
 #include <chrono>
 #include <condition_variable>
 #include <cmath>
+#include <cstdlib>
 #include <cstring>
 #include <functional>
 #include <mutex>
@@ -355,22 +356,29 @@ __attribute__((target("avx512f,avx512bw,avx512bf16"))) float dot_mxfp4_bf16dp(
   return _mm512_reduce_add_ps(acc);
 }
 
-bool have_avx512bf16() {
-  static const bool v = __builtin_cpu_supports("avx512f") &&
-                        __builtin_cpu_supports("avx512bw") &&
-                        __builtin_cpu_supports("avx512bf16");
+// Instruction-set level of the row dots: the best the CPU has, capped by
+// the environment variable MOE_HOST_ISA (scalar, avx2, avx512, bf16) so that
+// every path can be tested on one machine.  Read once per process.
+int host_isa() {
+  static const int v = [] {
+    int best = 0;
+    if (__builtin_cpu_supports("avx2") && __builtin_cpu_supports("fma")) best = 1;
+    if (best && __builtin_cpu_supports("avx512f") && __builtin_cpu_supports("avx512bw")) best = 2;
+    if (best == 2 && __builtin_cpu_supports("avx512bf16")) best = 3;
+    const char* cap = std::getenv("MOE_HOST_ISA");
+    if (cap) {
+      const int c = !std::strcmp(cap, "scalar") ? 0 : !std::strcmp(cap, "avx2") ? 1
+                  : !std::strcmp(cap, "avx512") ? 2 : 3;
+      if (c < best) best = c;
+    }
+    return best;
+  }();
   return v;
 }
 
-bool have_avx512() {
-  static const bool v = __builtin_cpu_supports("avx512f") && __builtin_cpu_supports("avx512bw");
-  return v;
-}
-
-bool have_avx2() {
-  static const bool v = __builtin_cpu_supports("avx2") && __builtin_cpu_supports("fma");
-  return v;
-}
+bool have_avx512bf16() { return host_isa() >= 3; }
+bool have_avx512() { return host_isa() >= 2; }
+bool have_avx2() { return host_isa() >= 1; }
 
 struct Layout {
   size_t off[6], bytes;

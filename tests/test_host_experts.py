@@ -178,3 +178,19 @@ def test_host_expert_rate_positive(ops):
     pool, _ = _pool(name, "mxfp4", range(4))
     r = ops.host_expert_rate(desc, torch.from_numpy(pool.ravel()), n_experts=4, reps=2)
     assert r > 0
+
+
+@pytest.mark.parametrize("isa", ["scalar", "avx2", "avx512"])
+def test_host_experts_every_isa_path(isa):
+    """The row-dot paths a CPU without AVX512-BF16 (or AVX-512, or AVX2) would
+    take, forced through MOE_HOST_ISA in a fresh process (the level is read
+    once per process): the oracle comparisons above must hold on each."""
+    import subprocess
+    import sys
+    env = dict(os.environ, MOE_HOST_ISA=isa)
+    r = subprocess.run([sys.executable, "-m", "pytest", os.path.join(ROOT, "tests",
+                        "test_host_experts.py"), "-q", "-k", "match_oracle",
+                        "-p", "no:cacheprovider"], env=env, capture_output=True, text=True,
+                       timeout=600, cwd=ROOT)
+    assert r.returncode == 0, r.stdout[-2000:] + r.stderr[-2000:]
+    assert " passed" in r.stdout
