@@ -201,7 +201,8 @@ __global__ __launch_bounds__(256) void sort_scatter_kernel(SortArgs a) {
   if (b < 0) return;
   int rank = 0;
   for (int q = 0; q < (int)threadIdx.x; ++q) rank += (sbin[q] == b);
-  a.sorted_pair[a.chunk_counts[(int64_t)blockIdx.x * nb + b] + rank] = p;
+  const int pos = a.chunk_counts[(int64_t)blockIdx.x * nb + b] + rank;
+  if ((unsigned)pos < (unsigned)a.n_pairs) a.sorted_pair[pos] = p;
 }
 
 struct GemmArgs {
