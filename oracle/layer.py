@@ -18,10 +18,13 @@ What the pages leave open, and the reading taken here:
   * expert: SwiGLU, o = W_d (silu(W_g x) * (W_u x)), silu(z) = z/(1+e^-z),
     no biases, no clamp;
   * shared expert (when present): always runs, weight 1, same shape;
-  * prefill precision contract: the gate/up product uses x quantised to
-    MXFP4 along H and the down product uses h quantised to MXFP4 along I
-    (the scaled FP4 matrix instructions take MXFP4 on both sides); decode
-    uses x as given (BF16) and h unrounded.
+  * prefill precision contract, MXFP4 experts: the gate/up product uses x
+    quantised to MXFP4 along H and the down product uses h quantised to
+    MXFP4 along I (the scaled FP4 matrix instructions take MXFP4 on both
+    sides); NVFP4 experts: x as given (BF16) and h rounded to BF16 (nearest
+    even) before the down product (the BF16 matrix instructions take e2m1
+    times its E4M3 block scale exactly); decode uses x as given and h
+    unrounded.
 
 Pins (tests/test_oracle_layer.py): stable-argsort special case and
 brute-force best k-subset on the tiny layer; probabilities sum to one; the
@@ -89,19 +92,34 @@ def mx_roundtrip(a):
     return formats.mxfp4_decode(codes, scales)
 
 
+def bf16_roundtrip(a):
+    """Round fp64 values to BF16 (nearest even) through their fp32 value, and
+    decode again."""
+    return formats.bf16_decode(formats.bf16_round(np.asarray(a, dtype=np.float32)))
+
+
 def expert_ffn(x, w_gate, w_up, w_down, prefill=False):
     """One SwiGLU expert on the rows of x.
 
     x [n, H]; w_gate, w_up [I, H]; w_down [H, I]; all fp64 values.
-    prefill=True applies the prefill precision contract (MXFP4 x and h).
+    prefill: False (decode contract), True or "mxfp4" (MXFP4 x and h), or
+    "bf16" (x as given, h rounded to BF16).
     Returns o [n, H] fp64 (and h [n, I] for inspection).
     """
+    if prefill not in (False, True, "mxfp4", "bf16"):
+        raise ValueError(f"unknown precision contract {prefill!r}")
+    mx = prefill is True or prefill == "mxfp4"
     x = np.asarray(x, dtype=np.float64)
-    xin = mx_roundtrip(x) if prefill else x
+    xin = mx_roundtrip(x) if mx else x
     g = xin @ np.asarray(w_gate, dtype=np.float64).T
     u = xin @ np.asarray(w_up, dtype=np.float64).T
     h = silu(g) * u
-    hin = mx_roundtrip(h) if prefill else h
+    if mx:
+        hin = mx_roundtrip(h)
+    elif prefill == "bf16":
+        hin = bf16_roundtrip(h)
+    else:
+        hin = h
     o = hin @ np.asarray(w_down, dtype=np.float64).T
     return o, h
 
