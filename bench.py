@@ -30,6 +30,7 @@ from sparse_expert_execution_amd import bytemodel as bm
 ROOT = os.path.dirname(os.path.abspath(__file__))
 HBM_PEAK = 8.0e12            # bytes/s, MI355X published
 FP4_PEAK = 10.1e15           # dense MXFP4 FLOP/s, MI355X published
+BF16_PEAK = 2.5e15           # dense BF16 FLOP/s, MI355X published
 
 
 def log(*a):
@@ -48,6 +49,18 @@ def traffic_record(name):
     if rec.get("source_hash") != profiling.source_hash():
         return None
     return rec.get("bytes_per_launch")
+
+
+class DecodeWaitExpired(RuntimeError):
+    pass
+
+
+def check_decode_status(ops, ws, what):
+    """Every decode launch on ws since the last check finished its bounded
+    waits in time; otherwise its output was wrong and the run is void."""
+    if ops.decode_status(ws) != 0:
+        raise DecodeWaitExpired(f"{what}: a wait inside the decode kernel expired "
+                                "(the device was oversubscribed); the timed outputs are wrong")
 
 
 # --------------------------------------------------------------------------
@@ -143,6 +156,8 @@ def time_decode(ops, Lw, T, steps, warmup, mode="decode"):
         one_step(evs[st])
     torch.cuda.synchronize()
     call_ms = np.array([[e[0].elapsed_time(e[1]) for e in row] for row in evs])
+    if mode == "decode":
+        check_decode_status(ops, fws, f"{Lw.name} T={T}")
     return {"total_ms": total_ms, "step_ms": total_ms / steps, "call_ms": call_ms,
             "distinct": distinct, "ids": [i.cpu().numpy() for i in ids]}
 
@@ -180,18 +195,21 @@ def prefill_record(ops, Lw, T, steps, warmup):
     pairs = T * (k + 1)
     flops = bm.expert_flops(H, I, pairs)
     distinct = r["distinct"][0] + (1 if s["shared"] else 0)
-    wbytes = distinct * bm.expert_bytes(H, I, "mxfp4")
+    wbytes = distinct * bm.expert_bytes(H, I, s["wtype"])
     io_bytes = T * H * 2 + T * H * 4
     call_s = float(np.mean(r["call_ms"])) * 1e-3
     step_s = r["step_ms"] * 1e-3
     alg_bytes = wbytes + io_bytes
     ai = flops / alg_bytes
-    bound = min(FP4_PEAK, ai * HBM_PEAK)
+    # MXFP4 runs FP4 x FP4 on the scaled matrix cores, NVFP4 BF16 x BF16
+    peak = FP4_PEAK if s["wtype"] == "mxfp4" else BF16_PEAK
+    bound = min(peak, ai * HBM_PEAK)
     return {
-        "tokens": T, "tokens_per_s": T / step_s, "step_ms": r["step_ms"],
+        "tokens": T, "weights": s["wtype"], "tokens_per_s": T / step_s, "step_ms": r["step_ms"],
         "prefill_call_us": call_s * 1e6,
         "expert_tflops": flops / call_s / 1e12,
-        "mfma_frac_of_fp4_peak": flops / call_s / FP4_PEAK,
+        "mfma_peak_tflops": peak / 1e12,
+        "mfma_frac_of_peak": flops / call_s / peak,
         "arithmetic_intensity": ai,
         "roofline_bound_tflops": bound / 1e12,
         "roofline_frac": (flops / call_s) / bound,
@@ -299,6 +317,10 @@ def cache_record(ops, steps_limit=None, resize_at=None, q_sweep=None, sweep_step
     phases = [[0, 0]]                      # [hits, misses] per budget phase
     rebuild_ev = []
     cur_pool = dev_pool
+    # events around each step's decode (the GPU part of the split)
+    dec_ev = [[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
+              for _ in range(steps)]
+    gpu_experts = []
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -322,8 +344,11 @@ def cache_record(ops, steps_limit=None, resize_at=None, q_sweep=None, sweep_step
         fills += plan.q
         qs.append(plan.q)
         cache.fill(plan, side, comp)
+        dec_ev[st][0].record(comp)
         ops.decode(desc, xs[st:st + 1], d_ids[st:st + 1], d_w[st:st + 1], cur_pool, y, ws,
                    slot_of=table[0])
+        dec_ev[st][1].record(comp)
+        gpu_experts.append(plan.n_hits + plan.q)
         cache.release(plan, comp)
         # the host side runs while the GPU works on the fills and the decode
         host = set(int(e) for e in ops.plan_dict(plan)["host"])
@@ -337,6 +362,13 @@ def cache_record(ops, steps_limit=None, resize_at=None, q_sweep=None, sweep_step
     t_end.record(comp)
     torch.cuda.synchronize()
     wall = time.time() - wall0
+    check_decode_status(ops, ws, "cache decode trace")
+    dec_s = np.array([a.elapsed_time(b) for a, b in dec_ev]) * 1e-3
+    gpu_bytes = np.array(gpu_experts, dtype=np.float64) * eb + H * 2 + H * 4
+    gpu_part = {"gpu_part_us_per_step": float(dec_s.mean() * 1e6),
+                "gpu_part_bytes_per_step": float(gpu_bytes.mean()),
+                "gpu_part_GBps": float(gpu_bytes.sum() / dec_s.sum() / 1e9),
+                "gpu_part_hbm_frac": float(gpu_bytes.sum() / dec_s.sum() / HBM_PEAK)}
     ms = t_start.elapsed_time(t_end)
     sweep = {}
     if q_sweep:
@@ -369,6 +401,7 @@ def cache_record(ops, steps_limit=None, resize_at=None, q_sweep=None, sweep_step
                 ops.merge_partials(ys[st:st + 1], dev_part, ys[st:st + 1])
             a1.record(comp)
             torch.cuda.synchronize()
+            check_decode_status(ops, ws, f"cache q sweep q={qf}")
             yc = ys.cpu().double()
             if ys_ref is None:
                 ys_ref = yc
@@ -385,7 +418,7 @@ def cache_record(ops, steps_limit=None, resize_at=None, q_sweep=None, sweep_step
         "q_hist": np.bincount(np.array(qs), minlength=k + 1).tolist(),
         "b_pcie_GBps": bp / 1e9, "b_host_read_GBps": bh / 1e9,
         "b_host_expert_kernel_GBps": bx / 1e9, "host_experts_run": host_experts,
-        "fill_GBps": fills * eb / (ms * 1e-3) / 1e9,
+        "fill_GBps": fills * eb / (ms * 1e-3) / 1e9, **gpu_part,
         **({"budgets": [slots] + [n for _, n, _, _ in rebuild_ev],
             "rebuild_at_step": [st for st, _, _, _ in rebuild_ev],
             "rebuild_ms": [a.elapsed_time(b) for _, _, a, b in rebuild_ev],
@@ -450,6 +483,144 @@ def cpu_baseline(name, T, n_layers_sample, min_seconds=10.0):
                       f"to fp64 before timing"}
 
 
+def _oracle_expert_mats(name, layer, experts, wtype, threads=16):
+    """fp64 (gate, up, down) of each expert id as the oracle decodes them,
+    prepared in parallel host threads before any timing."""
+    import concurrent.futures as cf
+    from oracle import formats
+
+    def one(e):
+        mats = synth.expert_weights(name, layer, int(e), device="cuda", as_dtype=torch.float32)
+        out = []
+        for m in mats:
+            a = m.cpu().numpy()
+            if wtype == "bf16":
+                out.append(formats.bf16_decode(formats.bf16_round(a)))
+            elif wtype == "nvfp4":
+                out.append(formats.nvfp4_decode(*formats.nvfp4_encode(a)))
+            else:
+                out.append(formats.mxfp4_decode(*formats.mxfp4_encode(a)))
+        return tuple(out)
+
+    experts = [int(e) for e in experts]
+    with cf.ThreadPoolExecutor(min(threads, max(1, len(experts)))) as ex:
+        return dict(zip(experts, ex.map(one, experts)))
+
+
+def _time_reps(fn, min_seconds):
+    reps, t0 = 0, time.time()
+    while True:
+        fn()
+        reps += 1
+        if time.time() - t0 >= min_seconds:
+            return (time.time() - t0) / reps, reps
+
+
+def _blas_threads():
+    import threadpoolctl
+    info = threadpoolctl.threadpool_info()
+    return max([i.get("num_threads", 1) for i in info] or [1])
+
+
+def oracle_layer_timing(name, T, n_sample, prefill=False, min_seconds=3.0):
+    """The fp64 oracle on layer 0 of a workload at T tokens, on a bounded
+    sample: the oracle routes all T tokens, then runs the expert FFNs and the
+    combine of the first n_sample distinct routed experts (all their pairs;
+    the shared expert too, when the layer has one, except in prefill) with
+    weights decoded to fp64 beforehand, repeated for min_seconds.  The time is
+    scaled to the whole layer by the experts run (decode: weight-read bound)
+    or by the (token, expert) pairs (prefill: FLOP bound)."""
+    from oracle import formats, layer as olayer
+    s = synth.SHAPES[name]
+    E, k, H, I = s["n_experts"], s["top_k"], s["hidden"], s["inter"]
+    x = synth.tokens(name, 0, T, device="cuda")
+    xf = formats.bf16_decode(x.cpu().view(torch.int16).numpy().view(np.uint16))
+    wr = synth.router_weights(name, 0, device="cuda", as_dtype=torch.float32).cpu().numpy()
+    wr = formats.bf16_decode(formats.bf16_round(wr))
+    r = olayer.route(xf, wr, k)
+    ids, w = r["ids"], r["w"]
+    order = list(dict.fromkeys(int(e) for e in ids.ravel()))
+    sample = order[:n_sample]
+    use_shared = bool(s["shared"]) and not prefill
+    want = sample + ([E] if use_shared else [])
+    mats = _oracle_expert_mats(name, 0, want, s["wtype"])
+    shared = mats.pop(E) if use_shared else None
+    inc = np.isin(ids, sample)
+    contract = "mxfp4" if prefill else False
+    per_rep, reps = _time_reps(
+        lambda: olayer.combine(xf, ids, w, mats, shared=shared, prefill=contract, include=inc),
+        min_seconds)
+    ebytes = bm.expert_bytes(H, I, s["wtype"])
+    n_run = len(sample) + (1 if use_shared else 0)
+    n_all = len(order) + (1 if s["shared"] else 0)
+    if prefill:
+        pairs_all = T * (k + (1 if s["shared"] else 0))
+        layer_s = per_rep * pairs_all / int(inc.sum())
+    else:
+        layer_s = per_rep * n_all / n_run
+    out = {"cores": _blas_threads(),
+           "implied_weight_GBps": n_run * ebytes / per_rep / 1e9,
+           "sample": f"{name} layer 0, T={T}: expert FFNs + combine of {len(sample)} of "
+                     f"{len(order)} routed experts ({int(inc.sum())} pairs)"
+                     f"{' and the shared expert' if use_shared else ''}, fp64 NumPy, "
+                     f"{reps} reps; scaled by {'pairs' if prefill else 'experts'} to the layer"}
+    if prefill:
+        out.update(value=T / layer_s, unit="tokens/s")
+    else:
+        out.update(value=layer_s * 1e6 / T, unit="us/token/layer")
+    return out
+
+
+def oracle_cache_timing(min_seconds=3.0):
+    """The oracle on the expert-cache workload: the full 512-step LRU
+    simulation (q* from the pages' 51.5 GB/s PCIe and 178 GB/s host rates),
+    and the FFN work of trace step 0 (8 experts, one token) scaled to a
+    32-step window."""
+    from oracle import cache as ocache, formats, layer as olayer
+    name = "glm_cache_decode"
+    s = synth.SHAPES[name]
+    E, k, H, I = s["n_experts"], s["top_k"], s["hidden"], s["inter"]
+    ids_tr, w_tr = synth.zipf_trace(E, k, s["steps"], s["zipf"], s["drift"])
+    t0 = time.time()
+    plans, _ = ocache.lru_sim(ids_tr, w_tr, s["slots"], E, b_pcie=51.5e9, b_host=178e9)
+    lru_s = time.time() - t0
+    misses = sum(len(p["misses"]) for p in plans)
+    x = synth.tokens(name, 0, 1, device="cuda")
+    xf = formats.bf16_decode(x.cpu().view(torch.int16).numpy().view(np.uint16))
+    mats = _oracle_expert_mats(name, 0, ids_tr[0], s["wtype"])
+    per_rep, reps = _time_reps(
+        lambda: olayer.combine(xf, ids_tr[:1], w_tr[:1].astype(np.float64), mats), min_seconds)
+    ebytes = bm.expert_bytes(H, I, s["wtype"])
+    return {"value": per_rep * 1e6, "unit": "us/step (FFN work of one decode step)",
+            "window_32_steps_s": 32 * per_rep, "lru_sim_512_steps_s": lru_s,
+            "lru_sim_miss_rate": misses / (s["steps"] * k),
+            "implied_weight_GBps": k * ebytes / per_rep / 1e9, "cores": _blas_threads(),
+            "sample": f"{name}: the oracle's LRU over all {s['steps']} trace steps, and the "
+                      f"expert FFNs + combine of step 0 ({k} experts, T=1), fp64 NumPy, "
+                      f"{reps} reps, weights decoded to fp64 beforehand"}
+
+
+def cpu_details():
+    """Oracle timing of every workload (a bounded sample each)."""
+    out = {}
+    jobs = [("qwen_bf16_decode_T1", lambda: oracle_layer_timing("qwen_bf16_decode", 1, 8)),
+            ("qwen_bf16_decode_T8", lambda: oracle_layer_timing("qwen_bf16_decode", 8, 16)),
+            ("dsv4_mxfp4_decode_T1", lambda: oracle_layer_timing("dsv4_mxfp4_decode", 1, 6)),
+            ("dsv4_mxfp4_decode_T4", lambda: oracle_layer_timing("dsv4_mxfp4_decode", 4, 6)),
+            ("dsv4_mxfp4_decode_T16", lambda: oracle_layer_timing("dsv4_mxfp4_decode", 16, 6)),
+            ("prefill_T4096", lambda: oracle_layer_timing("dsv4_mxfp4_prefill", 4096, 4,
+                                                          prefill=True)),
+            ("glm_cache_decode", oracle_cache_timing)]
+    for key, fn in jobs:
+        t0 = time.time()
+        try:
+            out[key] = fn()
+        except Exception as ex:          # the GPU figures stand without it
+            out[key] = {"error": repr(ex)}
+        log(f"cpu oracle {key}: {json.dumps(out[key])} ({time.time() - t0:.1f}s)")
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -494,6 +665,8 @@ def main():
                 log(f"dsv4 T={T}", json.dumps(details[f"dsv4_mxfp4_decode_T{T}"]))
             del Ld
             torch.cuda.empty_cache()
+        except DecodeWaitExpired:
+            raise
         except Exception as ex:  # keep the headline line
             details["dsv4_mxfp4_decode_error"] = repr(ex)
         try:
@@ -506,6 +679,8 @@ def main():
                 log(f"dsv4 nvfp4 T={T}", json.dumps(details[f"dsv4_nvfp4_decode_T{T}"]))
             del Ln
             torch.cuda.empty_cache()
+        except DecodeWaitExpired:
+            raise
         except Exception as ex:
             details["dsv4_nvfp4_decode_error"] = repr(ex)
         try:
@@ -516,6 +691,13 @@ def main():
                 details[f"prefill_T{T}"] = prefill_record(ops, Lp, T, max(3, args.steps // 4),
                                                           2)
                 log(f"prefill T={T}", json.dumps(details[f"prefill_T{T}"]))
+            # the same layer with NVFP4 experts (BF16 matrix cores)
+            Lpn = Layers(ops, name3, 1, wtype="nvfp4")
+            details["prefill_nvfp4_T4096"] = prefill_record(ops, Lpn, 4096,
+                                                            max(3, args.steps // 4), 2)
+            log("prefill nvfp4 T=4096", json.dumps(details["prefill_nvfp4_T4096"]))
+            del Lpn
+            torch.cuda.empty_cache()
             # full-layer streaming from a pinned host pool: two buffers vs one
             n_st = 4
             E3 = Lp.s["n_experts"]
@@ -537,18 +719,24 @@ def main():
             del host_pool
             del Lp
             torch.cuda.empty_cache()
+        except DecodeWaitExpired:
+            raise
         except Exception as ex:
             details["prefill_error"] = repr(ex)
         try:
             log("cache decode trace")
             details["glm_cache_decode"] = cache_record(ops, q_sweep=[0, 1, 2, 4, 8])
             log(json.dumps(details["glm_cache_decode"]))
+        except DecodeWaitExpired:
+            raise
         except Exception as ex:
             details["glm_cache_decode_error"] = repr(ex)
         try:
             log("cache decode trace, elastic budget 64 -> 32 -> 96 slots")
             details["glm_cache_decode_elastic"] = cache_record(ops, resize_at={170: 32, 340: 96})
             log(json.dumps(details["glm_cache_decode_elastic"]))
+        except DecodeWaitExpired:
+            raise
         except Exception as ex:
             details["glm_cache_decode_elastic_error"] = repr(ex)
 
@@ -557,6 +745,8 @@ def main():
         log("cpu baseline (oracle)")
         cpu = cpu_baseline("qwen_bf16_decode", 1, 4)
         log(json.dumps(cpu))
+        if not args.quick:
+            cpu["details"] = cpu_details()
 
     traffic = traffic_record("decode_qwen_bf16_T1")
     out = {
@@ -584,4 +774,8 @@ def main():
 
 
 if __name__ == "__main__":
-    main()
+    try:
+        main()
+    except DecodeWaitExpired as ex:
+        print(f"bench.py: {ex}", file=sys.stderr, flush=True)
+        sys.exit(3)

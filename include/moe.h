@@ -62,8 +62,11 @@ extern "C" {
 #define MOE_WTYPE_MXFP4 2
 /* NVFP4: e2m1 codes [rows][K/2] (low nibble first), one OCP E4M3FN scale per
  * 16 elements [rows][K/16], one fp32 scale per matrix; value = e2m1 * E4M3 *
- * fp32 scale.  Decode only (prefill and the host expert kernel return
- * MOE_EUNSUPPORTED): CDNA4's scaled MFMA takes an e8m0 scale per 32. */
+ * fp32 scale.  The pages name it for their GLM-5.2 and laptop builds
+ * ("FreeToken 753b Model Explained", "Performance Benchmarks and Model
+ * Fit").  Decode, prefill and the host expert kernel take it; CDNA4's scaled
+ * FP4 matrix instructions take a power-of-two scale per 32 elements, so the
+ * NVFP4 prefill runs on the BF16 matrix cores (see moe_prefill). */
 #define MOE_WTYPE_NVFP4 3
 
 /* Layer description.  hidden (H) and inter (I) must be multiples of 32
@@ -140,10 +143,15 @@ int moe_route(const moe_desc* desc, const void* x, const void* w_router,
  * FFN_e(x) = W_down (silu(W_gate x) * (W_up x)), silu(z) = z / (1 + e^-z),
  * fp32 accumulation, x as given (BF16), h in fp32.  Only experts with a slot
  * contribute: y is the partial sum over the resident subset (the GPU side of
- * the pages' exact split); non-resident pairs are skipped.  Each workgroup
- * handles one expert and a slice of I and adds its share into y with fp32
- * atomics, so the summation order (and the last bits of y) can differ
- * between runs.
+ * the pages' exact split); non-resident pairs are skipped.
+ * One persistent kernel per launch of up to moe_decode's per-launch token
+ * limit (16, fewer when x of all tokens does not fit 120 KB of LDS; a larger
+ * T is split evenly into launches in stream order).  The gate/up rows of all
+ * selected experts are split evenly over the grid, h is handed between
+ * workgroups through the workspace tagged with the launch's generation, then
+ * the down rows are split evenly and each row's gate-weighted result is
+ * added into y with an fp32 atomic, so the summation order (and the last bits
+ * of y) can differ between runs.
  *   x              device [T][H] BF16;   1 <= T <= MOE_DECODE_MAX_T
  *   ids, w         device [T][k] (from moe_route or the caller)
  *   slot_of_expert device [E] int32: slot holding expert e, -1 = not
@@ -155,38 +163,74 @@ int moe_route(const moe_desc* desc, const void* x, const void* w_router,
  *   y              device out [T][H] float, overwritten
  *   ws             device workspace, moe_workspace_bytes(.., MOE_MODE_DECODE)
  * ids outside [0, E) are an error the kernels cannot report: they are
- * skipped. */
+ * skipped.
+ * Co-residency: the grid is sized so that all its workgroups fit the device
+ * at once (at most two per compute unit, capped by occupancy), because
+ * workgroups wait for each other's logits, h and cleared y.  Every such wait
+ * is bounded: if other work keeps compute units busy past the bound (an
+ * oversubscribed device), the wait gives up, y is wrong, and the workspace's
+ * wait-expired word is set; moe_decode_status reads and clears it. */
 int moe_decode(const moe_desc* desc, const void* x, int32_t T,
                const int32_t* ids, const float* w,
                const int32_t* slot_of_expert, const void* slot_pool,
                const void* shared_expert, float* y, void* ws, size_t ws_bytes,
                void* stream);
 
-/* moe_route_decode: moe_route followed by moe_decode as one call (one
- * persistent kernel for T <= 4): the router's ids and w are written out as by
- * moe_route (the host side of a miss split needs them) and y as by
- * moe_decode.  Same arguments as moe_decode plus w_router (device, [E][H] in
- * desc->router_wtype); ids and w are outputs.  ws: moe_workspace_bytes(..,
- * MOE_MODE_DECODE).  Two kernels: the router (its workgroups also clear y)
- * and the expert kernel. */
+/* moe_route_decode: moe_route followed by moe_decode as one call: the
+ * router's dot products, softmax and top-k run inside the same persistent
+ * kernel as the experts (every workgroup takes a share of the router rows,
+ * hands its logits to all others through the workspace, and ranks the tokens
+ * itself), so one launch per batch of up to 16 tokens does the whole layer.
+ * The router's ids and w are written out as by moe_route (the host side of a
+ * miss split needs them) and y as by moe_decode.  Same arguments as
+ * moe_decode plus w_router (device, [E][H] in desc->router_wtype); ids and w
+ * are outputs.  ws: moe_workspace_bytes(.., MOE_MODE_DECODE).  The
+ * co-residency note and the wait-expired word of moe_decode apply. */
 int moe_route_decode(const moe_desc* desc, const void* x, const void* w_router,
                      int32_t T, int32_t* ids, float* w,
                      const int32_t* slot_of_expert, const void* slot_pool,
                      const void* shared_expert, float* y, void* ws,
                      size_t ws_bytes, void* stream);
 
-/* moe_prefill: the same layer for long token batches (MXFP4 weights only).
- * Pairs are counting-sorted by expert; x and h are quantised to MXFP4 on the
- * fly (x along H, h along I, same encoder as moe_quantize_mxfp4) and both
- * expert products run on the scaled FP4 matrix cores with fp32
- * accumulation.  Prefill routes nearly every expert (explainx.ai guide,
- * "Prefill: load almost every expert without idling the GPU").  Arguments as
- * moe_decode; 1 <= T <= 65536; ws of moe_workspace_bytes(.., PREFILL). */
+/* moe_decode_status: the decode workspace's wait-expired word (non-zero when
+ * a bounded wait inside a moe_decode / moe_route_decode launch on this
+ * workspace gave up, so that launch's y is wrong) is copied to *status
+ * (device int32; NULL = do not copy), then cleared when `clear` is non-zero.
+ * Enqueued on `stream` after the calls it should cover; read *status after
+ * synchronising.  The word is sticky: it stays set across calls until
+ * cleared, so one query after a run of calls covers all of them.
+ * MOE_EWORKSPACE if ws is not a decode workspace (< 8 KB or unaligned). */
+int moe_decode_status(void* ws, size_t ws_bytes, int32_t* status, int32_t clear, void* stream);
+
+/* moe_prefill: the same layer for long token batches.  Pairs are
+ * counting-sorted by expert and each expert's rows run as a grouped GEMM.
+ * MXFP4 weights: x and h are quantised to MXFP4 on the fly (x along H, h
+ * along I, same encoder as moe_quantize_mxfp4) and both expert products run
+ * on the scaled FP4 matrix cores with fp32 accumulation.  NVFP4 weights:
+ * each weight is expanded to e2m1 x E4M3 in BF16 (exact) and both products
+ * run on the BF16 matrix cores with x as given and h rounded to BF16, the
+ * fp32 matrix scales applied to the fp32 results.  The down product writes
+ * each pair's output to the workspace and a last step sums a token's pairs
+ * in rank order times their gate weights (the shared expert last, weight 1):
+ * the result does not depend on scheduling.  Prefill routes nearly every
+ * expert (explainx.ai guide, "Prefill: load almost every expert without
+ * idling the GPU").  Arguments as moe_decode; 1 <= T <= 65536; hidden and
+ * inter multiples of 128; ws of moe_workspace_bytes(.., PREFILL). */
 int moe_prefill(const moe_desc* desc, const void* x, int32_t T,
                 const int32_t* ids, const float* w,
                 const int32_t* slot_of_expert, const void* slot_pool,
                 const void* shared_expert, float* y, void* ws, size_t ws_bytes,
                 void* stream);
+
+/* moe_debug_prefill_layout: where a prefill workspace for T tokens keeps the
+ * expert sort, for tests of the sort's integers: out[0] byte offset of
+ * seg_start (int32 [E + 2]: first sorted position of each bin, bins 0..E-1
+ * the routed experts, bin E the shared expert, then the total), out[1] of
+ * the tile list (int32: the count, then (bin, first sorted position) per
+ * 128-row tile in bin order), out[2] of sorted_pair (int32: pair ids t*k + j,
+ * or T*k + t for the shared expert, stably sorted by bin; non-resident pairs
+ * left out), out[3] the tile list's capacity, out[4] the number of pairs. */
+int moe_debug_prefill_layout(const moe_desc* desc, int32_t T, int64_t out[5]);
 
 /* moe_merge_partials: y = a + b elementwise over n floats (device).  The
  * exact merge of two partial sums computed over disjoint expert subsets
@@ -217,9 +261,23 @@ int moe_pack_expert(const moe_desc* desc, const void* gate, const void* up,
 
 /* moe_debug_dequant_mxfp4: n_blocks MXFP4 blocks (codes 16 B each, one scale
  * byte each) -> 32 * n_blocks floats, value e2m1(code) * 2^(s-127) computed
- * by the same in-register decoder the expert kernels use.  Test hook. */
+ * by the fp32 in-register convert the decode kernels' down rows use (the
+ * gate/up rows' BF16 convert is checked through moe_debug_dot_fp4).  Test
+ * hook. */
 int moe_debug_dequant_mxfp4(const uint8_t* codes, const uint8_t* scales,
                             int64_t n_blocks, float* out, void* stream);
+
+/* moe_debug_dot_fp4: for every block b < n_blocks and x vector v < n_x,
+ * out[b * n_x + v] = the per-block step of the decode kernels' gate/up rows
+ * on block b and 32 BF16 values x[v][0..32): MXFP4 (wtype MOE_WTYPE_MXFP4):
+ * the 32 e2m1 codes converted to BF16 by the same in-register convert, dotted
+ * with x in fp32, times the block's e8m0 scale (scales[b]); NVFP4
+ * (MOE_WTYPE_NVFP4): the sums over the two 16-element halves, each times its
+ * E4M3 scale (scales[2b], scales[2b+1]), the matrix scale not applied.
+ * codes [n_blocks][16] bytes, x [n_x][32] BF16, all device.  With x a
+ * one-hot vector the result is one element's exact value.  Test hook. */
+int moe_debug_dot_fp4(int32_t wtype, const uint8_t* codes, const uint8_t* scales,
+                      const void* x, int64_t n_blocks, int32_t n_x, float* out, void* stream);
 
 /* moe_debug_mfma_fp4_tile: D = A . B^T for one 16 x 128 MXFP4 tile of A
  * (a_codes [16][64] bytes, a_scales [16][4]) and of B (same shapes), out
@@ -353,8 +411,8 @@ int moe_cache_release(moe_cache* c, const moe_plan* plan, void* compute_stream);
  * range disjoint from it (else MOE_EINVAL); the old pool must stay allocated
  * until compute_stream has passed this call.  Fills after the rebuild wait
  * for it.  Elastic memory management (futuresignalnews.com, "3. Elastic
- * Memory Management"; "FreeToken 753b Model Explained", "Sparse expert
- * execution"). */
+ * Memory Management"; "FreeToken 753b Model Explained", "How MoE Paging and
+ * Caching Work"). */
 int moe_cache_resize(moe_cache* c, void* dev_slot_pool, int32_t n_slots,
                      void* compute_stream);
 /* Test hook: make the next n cache_fill calls fail before any copy. */
@@ -365,9 +423,8 @@ const moe_planner* moe_cache_planner(const moe_cache* c);
 /* A long prompt routes to nearly every expert of a layer, so prefill streams
  * whole layers from the pinned host pool; with two full-layer buffers the
  * next layer is copied over PCIe while the GPU computes the current one
- * ("FreeToken 753b Model Explained", "Prefill: load almost every expert
- * without idling the GPU"; marktechpost article, full-layer double
- * buffering).  One buffer gives the pages' ablation (copy, then compute).
+ * (explainx.ai guide, "Prefill: load almost every expert without idling
+ * the GPU"; futuresignalnews.com article, "2. Semantic-Aware Caching").  One buffer gives the pages' ablation (copy, then compute).
  *   host_pool  pinned host memory, [n_layers] blocks of layer_bytes (a
  *              layer's expert blocks in slot order, e.g. its E routed experts
  *              then its shared expert)
@@ -421,7 +478,8 @@ int moe_probe_bandwidths(const void* pinned_host, void* dev, size_t bytes,
  *              (index < 0) is MOE_EINVAL.
  *   y          host [T][H] float, overwritten
  *   n_threads  host threads (0 = all hardware threads); a persistent pool
- *              is kept between calls.
+ *              is kept between calls.  Calls from several host threads are
+ *              safe: they take the pool one after another.
  * Weights: BF16, MXFP4 or NVFP4 blocks.  Blocks the caller.  The shared
  * expert is not part of this call. */
 int moe_host_experts(const moe_desc* desc, const void* x, int32_t T,

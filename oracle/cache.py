@@ -30,7 +30,7 @@ textbook LRU and brute force):
 Elastic budget: the GPU expert cache can be rebuilt under a revised slot
 budget at a scheduler safe point, without restarting or reloading the host
 pool (futuresignalnews.com, "3. Elastic Memory Management"; "FreeToken 753b
-Model Explained", "Sparse expert execution").  Readings taken (parity
+Model Explained", "How MoE Paging and Caching Work").  Readings taken (parity
 unpinned against the pages): the n' most recently used residents survive
 (ties to the lower slot) and keep their recency; a survivor whose slot is
 below n' stays there, the others move, in old-slot order, into the free slots

@@ -88,15 +88,17 @@ PrefillWs prefill_ws(const moe_desc* d, int T) {
   w.n_pairs = (int)(T * k + (d->has_shared ? T : 0));
   w.n_chunks = (w.n_pairs + moe::kPrefillChunk - 1) / moe::kPrefillChunk;
   w.max_tiles = moe::prefill_max_tiles(T, (int)k, (int)E);
+  // MXFP4 weights: MXFP4 copies of x and h; NVFP4: h in BF16 (x as given)
+  const bool nv = d->wtype == MOE_WTYPE_NVFP4;
   size_t o = 0;
-  w.xq_codes = o; o = align_up(o + T * H / 2);
-  w.xq_scales = o; o = align_up(o + T * H / 32);
+  w.xq_codes = o; o = align_up(o + (nv ? 0 : T * H / 2));
+  w.xq_scales = o; o = align_up(o + (nv ? 0 : T * H / 32));
   w.chunk_counts = o; o = align_up(o + (size_t)w.n_chunks * (E + 1) * 4);
   w.seg_start = o; o = align_up(o + (E + 2) * 4);
   w.tiles = o; o = align_up(o + (1 + 2 * (size_t)w.max_tiles) * 4);
   w.sorted_pair = o; o = align_up(o + (size_t)w.n_pairs * 4);
-  w.hq_codes = o; o = align_up(o + (size_t)w.n_pairs * I / 2);
-  w.hq_scales = o; o = align_up(o + (size_t)w.n_pairs * I / 32);
+  w.hq_codes = o; o = align_up(o + (size_t)w.n_pairs * (nv ? I * 2 : I / 2));
+  w.hq_scales = o; o = align_up(o + (nv ? 0 : (size_t)w.n_pairs * I / 32));
   w.partial = o; o = align_up(o + (size_t)T * (k + 1) * H * 4);
   w.total = o;
   return w;
@@ -283,8 +285,8 @@ int moe_prefill(const moe_desc* desc, const void* x, int32_t T, const int32_t* i
   if (T == 0) return check_desc(desc);
   int st = check_ffn_args(desc, x, T, ids, w, slot_pool, shared_expert, y);
   if (st) return st;
-  if (desc->wtype != MOE_WTYPE_MXFP4)
-    return set_error(MOE_EUNSUPPORTED, "moe_prefill runs MXFP4 expert weights only");
+  if (desc->wtype != MOE_WTYPE_MXFP4 && desc->wtype != MOE_WTYPE_NVFP4)
+    return set_error(MOE_EUNSUPPORTED, "moe_prefill runs MXFP4 or NVFP4 expert weights");
   if (desc->hidden % 128 || desc->inter % 128)
     return set_error(MOE_EUNSUPPORTED, "moe_prefill needs hidden and inter multiples of 128");
   if (T < 0 || T > 65536) return set_error(MOE_EINVAL, "prefill T %d outside [1, 65536]", T);
@@ -299,8 +301,10 @@ int moe_prefill(const moe_desc* desc, const void* x, int32_t T, const int32_t* i
   p.shared = shared_expert; p.y = y; p.expert_bytes = (int64_t)bytes;
   for (int i = 0; i < 6; ++i) p.off[i] = (int64_t)off[i];
   p.T = T; p.H = desc->hidden; p.I = desc->inter; p.E = desc->n_experts; p.k = desc->top_k;
-  p.xq_codes = b + L.xq_codes;
-  p.xq_scales = b + L.xq_scales;
+  p.nvfp4 = desc->wtype == MOE_WTYPE_NVFP4;
+  p.goff = p.nvfp4 ? (int64_t)(off[5] + (size_t)desc->hidden * desc->inter / 16) : 0;
+  p.xq_codes = p.nvfp4 ? nullptr : b + L.xq_codes;
+  p.xq_scales = p.nvfp4 ? nullptr : b + L.xq_scales;
   p.chunk_counts = reinterpret_cast<int32_t*>(b + L.chunk_counts);
   p.seg_start = reinterpret_cast<int32_t*>(b + L.seg_start);
   p.tiles = reinterpret_cast<int32_t*>(b + L.tiles);
@@ -311,6 +315,19 @@ int moe_prefill(const moe_desc* desc, const void* x, int32_t T, const int32_t* i
   p.n_chunks = L.n_chunks;
   p.max_tiles = L.max_tiles;
   return hip_status(moe::launch_prefill(p, as_stream(stream)), "moe_prefill");
+}
+
+int moe_debug_prefill_layout(const moe_desc* desc, int32_t T, int64_t out[5]) {
+  int st = check_desc(desc);
+  if (st) return st;
+  if (!out || T < 1) return set_error(MOE_EINVAL, "bad argument");
+  const PrefillWs L = prefill_ws(desc, T);
+  out[0] = (int64_t)L.seg_start;
+  out[1] = (int64_t)L.tiles;
+  out[2] = (int64_t)L.sorted_pair;
+  out[3] = L.max_tiles;
+  out[4] = L.n_pairs;
+  return MOE_OK;
 }
 
 int moe_merge_partials(const float* a, const float* b, float* y, size_t n, void* stream) {
@@ -379,6 +396,30 @@ int moe_debug_dequant_mxfp4(const uint8_t* codes, const uint8_t* scales, int64_t
     return set_error(MOE_EINVAL, "codes and out must be 16-byte aligned");
   return hip_status(moe::launch_dequant_mxfp4(codes, scales, n_blocks, out, as_stream(stream)),
                     "moe_debug_dequant_mxfp4");
+}
+
+int moe_debug_dot_fp4(int32_t wtype, const uint8_t* codes, const uint8_t* scales,
+                      const void* x, int64_t n_blocks, int32_t n_x, float* out, void* stream) {
+  if (n_blocks == 0 || n_x == 0) return MOE_OK;
+  if (wtype != MOE_WTYPE_MXFP4 && wtype != MOE_WTYPE_NVFP4)
+    return set_error(MOE_EINVAL, "moe_debug_dot_fp4 takes MXFP4 or NVFP4 blocks");
+  if (!codes || !scales || !x || !out || n_blocks < 0 || n_x < 0)
+    return set_error(MOE_EINVAL, "bad argument");
+  if (!aligned(codes, 16) || !aligned(x, 16))
+    return set_error(MOE_EINVAL, "codes and x must be 16-byte aligned");
+  return hip_status(moe::launch_dot_fp4(codes, scales, static_cast<const uint16_t*>(x), n_blocks,
+                                        n_x, wtype == MOE_WTYPE_NVFP4, out, as_stream(stream)),
+                    "moe_debug_dot_fp4");
+}
+
+int moe_decode_status(void* ws, size_t ws_bytes, int32_t* status, int32_t clear, void* stream) {
+  if (!ws || ws_bytes < kDecodeHeader || !aligned(ws, 256))
+    return set_error(MOE_EWORKSPACE, "decode status needs the decode workspace (>= %zu bytes)",
+                     kDecodeHeader);
+  if (!status && !clear) return MOE_OK;
+  return hip_status(moe::launch_decode_status(static_cast<unsigned*>(ws), status, clear != 0,
+                                              as_stream(stream)),
+                    "moe_decode_status");
 }
 
 int moe_debug_mfma_fp4_tile(const uint8_t* a_codes, const uint8_t* a_scales,

@@ -158,9 +158,9 @@ __device__ __forceinline__ int mx_block_exponent(float amax) {
   return X < -127 ? -127 : (X > 127 ? 127 : X);
 }
 
-// 2^-X as an fp32 multiplier is not always representable (X = -127 gives
-// 2^127, fine; X = 127 gives 2^-127, a denormal), so divide in two exact
-// power-of-two steps.
+// v / 2^X by ldexpf, which scales by the power of two directly (no 2^-X
+// multiplier is formed; for X = 127 it would be a denormal).  The quotient is
+// exact wherever it can decide a code: |v / 2^X| >= 0.25 is a normal number.
 __device__ __forceinline__ float mx_scale_down(float v, int X) {
   return ldexpf(v, -X);
 }

@@ -202,6 +202,46 @@ __global__ __launch_bounds__(256) void read_probe_kernel(const uint4* __restrict
   if (acc == 0x9e3779b9u) out[0] = acc;   // keeps the loads live
 }
 
+// One thread per block and x vector: the per-block step of the decode
+// kernels' gate/up rows.  MXFP4: the 32 e2m1 values converted to BF16 (scale
+// 1.0), dotted with 32 BF16 x values in fp32, times the e8m0 scale.  NVFP4:
+// the two 16-element half sums, each times its E4M3 scale.
+__global__ __launch_bounds__(256) void dot_fp4_kernel(const uint8_t* __restrict__ codes,
+                                                      const uint8_t* __restrict__ scales,
+                                                      const uint16_t* __restrict__ x,
+                                                      int64_t n_blocks, int n_x, int nvfp4,
+                                                      float* __restrict__ out) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n_blocks * n_x) return;
+  const int64_t b = i / n_x;
+  const int xv = (int)(i % n_x);
+  const uint4 q = ldg16(codes + b * 16);
+  uint32_t xp[16];
+  const uint4* xs = reinterpret_cast<const uint4*>(x + (int64_t)xv * 32);
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const uint4 v = xs[c];
+    xp[4 * c] = v.x; xp[4 * c + 1] = v.y; xp[4 * c + 2] = v.z; xp[4 * c + 3] = v.w;
+  }
+  float r;
+  if (!nvfp4) {
+    r = fmaf(dot_fp4_bf16_block(q, xp), e8m0_to_f32(scales[b]), 0.f);
+  } else {
+    float s0, s1;
+    dot_fp4_bf16_halves(q, xp, s0, s1);
+    r = fmaf(s0, e4m3_to_f32(scales[2 * b]), fmaf(s1, e4m3_to_f32(scales[2 * b + 1]), 0.f));
+  }
+  out[i] = r;
+}
+
+// The decode wait-expired word (header word 32) to *out (if given), then
+// cleared (if asked).
+__global__ void decode_status_kernel(unsigned* hdr, int32_t* out, int clear) {
+  const unsigned v = __hip_atomic_load(hdr + 32, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (out) *out = (int32_t)v;
+  if (clear) __hip_atomic_store(hdr + 32, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 __global__ void fill_i32_kernel(int32_t* dst, int32_t value, int64_t n) {
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) dst[i] = value;
@@ -247,6 +287,20 @@ hipError_t launch_dequant_mxfp4(const uint8_t* codes, const uint8_t* scales, int
   if (n_blocks == 0) return hipSuccess;
   hipLaunchKernelGGL(dequant_kernel, dim3((unsigned)((n_blocks + 255) / 256)), dim3(256), 0, st,
                      codes, scales, n_blocks, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_dot_fp4(const uint8_t* codes, const uint8_t* scales, const uint16_t* x,
+                          int64_t n_blocks, int n_x, int nvfp4, float* out, hipStream_t st) {
+  const int64_t n = n_blocks * n_x;
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(dot_fp4_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, codes,
+                     scales, x, n_blocks, n_x, nvfp4, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_status(unsigned* hdr, int32_t* out, int clear, hipStream_t st) {
+  hipLaunchKernelGGL(decode_status_kernel, dim3(1), dim3(1), 0, st, hdr, out, clear);
   return hipGetLastError();
 }
 

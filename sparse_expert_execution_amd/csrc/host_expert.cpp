@@ -104,6 +104,9 @@ class Pool {
 };
 
 std::mutex g_pool_m;
+// held by a moe_host_experts call for as long as it uses the pool: calls from
+// several host threads run one after another on it
+std::mutex g_call_m;
 Pool* g_pool = nullptr;
 int g_pool_threads = 0;
 
@@ -461,6 +464,7 @@ int moe_host_experts(const moe_desc* desc, const void* x, int32_t T, const int32
       ent[e].push_back({t, w[p]});
     }
   }
+  std::lock_guard<std::mutex> call_lock(g_call_m);
   Pool& P = pool(n_threads);
   std::vector<float> h;
   constexpr int kRows = 32;                     // rows per task

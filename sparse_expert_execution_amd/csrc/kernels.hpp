@@ -45,11 +45,31 @@ struct PrefillLaunch {
   int32_t* seg_start;    // [E+2]
   int32_t* tiles;        // [2 * max_tiles + 1]: n_tiles, then (bin, row0) pairs
   int32_t* sorted_pair;  // [n_pairs]
-  uint8_t* hq_codes;     // [n_pairs][I/2]   (sorted order)
-  uint8_t* hq_scales;    // [n_pairs][I/32]
+  uint8_t* hq_codes;     // [n_pairs][I/2]   (sorted order); NVFP4: BF16 h [n_pairs][I]
+  uint8_t* hq_scales;    // [n_pairs][I/32]; NVFP4: unused
   float* partial;        // [T][k+1][H]
+  int nvfp4;             // weights NVFP4 (x not quantised, BF16 GEMMs)
+  int64_t goff;          // NVFP4: offset of the three fp32 matrix scales
   int n_chunks, max_tiles;
 };
+
+// prefill GEMMs for NVFP4 weights (BF16 matrix cores); the sort is shared
+struct NvPrefillArgs {
+  const int32_t* slot_of;
+  const uint8_t* pool;
+  const uint8_t* shared;
+  int64_t expert_bytes;
+  int64_t off[6];
+  int64_t goff;          // offset of the gate, up, down fp32 matrix scales
+  int T, H, I, E, k;
+  const int32_t* seg_start;
+  const int32_t* tiles;
+  const int32_t* sorted_pair;
+  const uint16_t* x;     // [T][H] bf16
+  uint16_t* hb;          // [n_pairs][I] bf16 h, sorted order
+  float* partial;        // [T][k+1][H] per-pair outputs
+};
+hipError_t launch_prefill_nvfp4_gemms(const NvPrefillArgs& a, int max_tiles, hipStream_t st);
 
 // router alone: small T (one wave per expert row, the last workgroup ranks),
 // large T (tiled logits + one wave per token)
@@ -93,6 +113,11 @@ hipError_t launch_pack_bf16(const void* src, int src_bf16, int rows, int K, uint
                             hipStream_t st);
 hipError_t launch_dequant_mxfp4(const uint8_t* codes, const uint8_t* scales,
                                 int64_t n_blocks, float* out, hipStream_t st);
+// test hook: per (block, x vector) the decode gate/up block step (MXFP4 or NVFP4)
+hipError_t launch_dot_fp4(const uint8_t* codes, const uint8_t* scales, const uint16_t* x,
+                          int64_t n_blocks, int n_x, int nvfp4, float* out, hipStream_t st);
+// decode header word 32 (a wait expired) to out, optionally cleared
+hipError_t launch_decode_status(unsigned* hdr, int32_t* out, int clear, hipStream_t st);
 hipError_t launch_merge(const float* a, const float* b, float* y, size_t n,
                         hipStream_t st);
 hipError_t launch_mfma_fp4_tile(const uint8_t* a_codes, const uint8_t* a_scales,

@@ -8,7 +8,8 @@
 //
 // Precision contract: x is quantised to MXFP4 along H and h along I with the
 // library's MXFP4 encoder; both products are FP4 x FP4 with e8m0 block scales
-// on v_mfma_scale_f32_16x16x128_f8f6f4 with fp32 accumulation.
+// on v_mfma_scale_f32_16x16x128_f8f6f4 with fp32 accumulation.  NVFP4 weights
+// share steps 2-4 and 7 and run their GEMMs in prefill_nvfp4.hip.
 //
 // Pipeline (one stream, no host synchronisation):
 //   1 quantise x rows                 x [T][H] bf16 -> codes/scales
@@ -732,8 +733,8 @@ hipError_t launch_prefill(const PrefillLaunch& p, hipStream_t st) {
   const int has_shared = p.shared != nullptr;
   const int n_pairs = p.T * p.k + (has_shared ? p.T : 0);
 
-  // 1 quantise x
-  {
+  // 1 quantise x (MXFP4 weights; NVFP4 GEMMs take x as given)
+  if (!p.nvfp4) {
     const int64_t n = (int64_t)p.T * (p.H / 32);
     hipLaunchKernelGGL(quant_bf16_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
                        static_cast<const uint16_t*>(p.x), p.T, p.H, p.xq_codes, p.xq_scales);
@@ -751,6 +752,19 @@ hipError_t launch_prefill(const PrefillLaunch& p, hipStream_t st) {
   hipLaunchKernelGGL(sort_scatter_kernel, dim3(p.n_chunks), dim3(256), 0, st, s);
   if ((err = hipGetLastError()) != hipSuccess) return err;
 
+  if (p.nvfp4) {
+    NvPrefillArgs g;
+    g.slot_of = p.slot_of; g.pool = static_cast<const uint8_t*>(p.pool);
+    g.shared = static_cast<const uint8_t*>(p.shared); g.expert_bytes = p.expert_bytes;
+    for (int i = 0; i < 6; ++i) g.off[i] = p.off[i];
+    g.goff = p.goff;
+    g.T = p.T; g.H = p.H; g.I = p.I; g.E = p.E; g.k = p.k;
+    g.seg_start = p.seg_start; g.tiles = p.tiles; g.sorted_pair = p.sorted_pair;
+    g.x = static_cast<const uint16_t*>(p.x);
+    g.hb = reinterpret_cast<uint16_t*>(p.hq_codes);
+    g.partial = p.partial;
+    if ((err = launch_prefill_nvfp4_gemms(g, p.max_tiles, st)) != hipSuccess) return err;
+  } else {
   GemmArgs g;
   g.slot_of = p.slot_of; g.pool = static_cast<const uint8_t*>(p.pool);
   g.shared = static_cast<const uint8_t*>(p.shared); g.expert_bytes = p.expert_bytes;
@@ -776,6 +790,7 @@ hipError_t launch_prefill(const PrefillLaunch& p, hipStream_t st) {
       hipLaunchKernelGGL(gemm_kernel<2>, dim3(groups * 8 * nt2), dim3(kGemmThreads), 0, st, g);
   }
   if ((err = hipGetLastError()) != hipSuccess) return err;
+  }
   {
     const int64_t n = (int64_t)p.T * (p.H / 4);
     hipLaunchKernelGGL(combine_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,

@@ -2,9 +2,9 @@
 //
 // A long prompt routes to nearly every expert of a layer, so prefill moves
 // whole layers: with two full-layer buffers the next layer is copied over
-// PCIe while the GPU computes the current one ("FreeToken 753b Model
-// Explained" and explainx.ai guide, "Prefill: stream the full layer";
-// marktechpost article, full-layer double buffering).  With one buffer the
+// PCIe while the GPU computes the current one (explainx.ai guide, "Prefill:
+// load almost every expert without idling the GPU"; futuresignalnews.com
+// article, "2. Semantic-Aware Caching").  With one buffer the
 // copy of a layer and its compute run one after the other (the pages'
 // ablation).  A layer's block in the pinned host pool is copied with one
 // hipMemcpyAsync on a copy stream; HIP events order it after the buffer's

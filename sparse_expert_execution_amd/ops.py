@@ -66,10 +66,33 @@ def route_decode(desc, x, w_router, ids, w, pool, y, ws, slot_of=None, shared=No
           "moe_route_decode")
 
 
+def decode_status(ws, clear=True, stream=None):
+    """The decode workspace's wait-expired word (0: every wait inside the
+    launches on ws since the last clear finished in time), read after
+    synchronising the stream, then cleared when ``clear``."""
+    out = torch.full((1,), -1, dtype=torch.int32, device=ws.device)
+    s = stream if stream is not None else torch.cuda.current_stream()
+    check(lib().moe_decode_status(_ptr(ws), ws.numel(), _ptr(out), int(clear), _stream(s)),
+          "moe_decode_status")
+    s.synchronize()
+    return int(out.item())
+
+
 def prefill(desc, x, ids, w, pool, y, ws, slot_of=None, shared=None, stream=None):
     check(lib().moe_prefill(ctypes.byref(desc), _ptr(x), x.shape[0], _ptr(ids), _ptr(w),
                             _ptr(slot_of), _ptr(pool), _ptr(shared), _ptr(y), _ptr(ws),
                             ws.numel(), _stream(stream)), "moe_prefill")
+
+
+def prefill_sort_view(desc, T, ws):
+    """(seg_start, tiles, sorted_pair) int32 views into a prefill workspace
+    (moe_debug_prefill_layout), read after a moe_prefill call on ws."""
+    out = (ctypes.c_int64 * 5)()
+    check(lib().moe_debug_prefill_layout(ctypes.byref(desc), T, out),
+          "moe_debug_prefill_layout")
+    seg, tiles, pairs, max_tiles, n_pairs = (int(v) for v in out)
+    i32 = lambda off, n: ws[off:off + 4 * n].view(torch.int32)
+    return i32(seg, desc.n_experts + 2), i32(tiles, 1 + 2 * max_tiles), i32(pairs, n_pairs)
 
 
 def merge_partials(a, b, y, stream=None):
@@ -87,6 +110,17 @@ def quantize_mxfp4(src, codes, scales, stream=None):
 def dequant_mxfp4(codes, scales, out, stream=None):
     check(lib().moe_debug_dequant_mxfp4(_ptr(codes), _ptr(scales), scales.numel(), _ptr(out),
                                         _stream(stream)), "moe_debug_dequant_mxfp4")
+
+
+def dot_fp4(wtype, codes, scales, x, out, stream=None):
+    """Decode gate/up block step (test hook): codes [n, 16] u8, scales [n]
+    (MXFP4) or [n, 2] (NVFP4) u8, x [n_x, 32] bf16 -> out [n, n_x] float32."""
+    wt = {"mxfp4": _lib.WTYPE_MXFP4, "nvfp4": _lib.WTYPE_NVFP4}[wtype]
+    n, n_x = codes.shape[0], x.shape[0]
+    if out.numel() != n * n_x or x.shape[1] != 32 or codes.shape[1] != 16:
+        raise ValueError("dot_fp4: codes [n, 16], x [n_x, 32], out [n, n_x]")
+    check(lib().moe_debug_dot_fp4(wt, _ptr(codes), _ptr(scales), _ptr(x), n, n_x, _ptr(out),
+                                  _stream(stream)), "moe_debug_dot_fp4")
 
 
 def mfma_fp4_tile(a_codes, a_scales, b_codes, b_scales, out, stream=None):

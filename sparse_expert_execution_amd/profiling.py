@@ -240,6 +240,27 @@ def cmd_summarize(args):
     print(json.dumps(rec))
 
 
+def cmd_counters(args):
+    """Mean of every counter per dispatch, for each kernel whose name holds
+    --match, from one or more rocprofv3 --pmc counter csv files."""
+    vals = {}
+    for path in args.csv:
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if args.match not in r.get("Kernel_Name", ""):
+                    continue
+                key = (r["Kernel_Name"][:90], r["Counter_Name"])
+                vals.setdefault(key, []).append(float(r["Counter_Value"]))
+    lines = ["| kernel | counter | mean per dispatch | dispatches |", "|---|---|---|---|"]
+    for (k, c), v in sorted(vals.items()):
+        lines.append(f"| {k} | {c} | {sum(v) / len(v):.6g} | {len(v)} |")
+    text = "\n".join(lines) + "\n"
+    if args.out:
+        with open(args.out, "a") as f:
+            f.write(text)
+    print(text)
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -267,7 +288,14 @@ def main(argv=None):
     s.add_argument("--mfma", default=None, help="counter csv of the matrix-core pass")
     s.add_argument("--out-dir", default=os.path.join(ROOT, "profiles"))
     s.add_argument("--cmd-mfma", default="")
+    c = sub.add_parser("counters")
+    c.add_argument("--csv", nargs="+", required=True)
+    c.add_argument("--match", default="")
+    c.add_argument("--out", default=None)
     a = ap.parse_args(argv)
+    if a.cmd == "counters":
+        cmd_counters(a)
+        return
     if a.cmd == "run":
         cmd_run(a)
     elif a.cmd == "run-prefill":

@@ -92,3 +92,102 @@ def bf16_to_f64(x):
     """Exact values of a BF16 generator tensor (device or host)."""
     bits = x.detach().cpu().view(torch.int16).numpy().view(np.uint16)
     return formats.bf16_decode(bits)
+
+
+# ---------------------------------------------------------------------------
+# Oracle outputs at full layer sizes.  An fp64 expert of the DeepSeek- or
+# GLM-shaped layers takes 200-300 MB, so experts are decoded one at a time,
+# on access, and the selected experts are split over host threads; each
+# thread sums the pairs of its own experts with the oracle's combine (an
+# include mask), and the partial sums add up to the full output (the merge
+# the oracle is pinned to).  The slow part, the oracle's MXFP4 encode, is
+# kept per expert in a small cache of codes and scales.
+import collections
+import concurrent.futures as _cf
+import os as _os
+import threading as _threading
+
+_ENC_CACHE = collections.OrderedDict()
+_ENC_LOCK = _threading.Lock()
+_ENC_MAX = 320
+ORACLE_THREADS = min(16, _os.cpu_count() or 1)
+
+
+def _encoded(name, layer, e, wtype, seed):
+    key = (name, layer, e, wtype, seed)
+    with _ENC_LOCK:
+        if key in _ENC_CACHE:
+            _ENC_CACHE.move_to_end(key)
+            return _ENC_CACHE[key]
+    mats = synth.expert_weights(name, layer, e, device="cuda", seed=seed,
+                                as_dtype=torch.float32)
+    enc = []
+    for m in mats:
+        a = m.cpu().numpy()
+        if wtype == "mxfp4":
+            enc.append(formats.mxfp4_encode(a))
+        elif wtype == "nvfp4":
+            enc.append(formats.nvfp4_encode(a))
+        elif wtype == "bf16":
+            enc.append(formats.bf16_round(a))
+        else:
+            enc.append(a)
+    with _ENC_LOCK:
+        _ENC_CACHE[key] = enc
+        while len(_ENC_CACHE) > _ENC_MAX:
+            _ENC_CACHE.popitem(last=False)
+    return enc
+
+
+def oracle_weights_cached(name, layer, e, wtype, seed=0):
+    """oracle_weights, through the cache of encoded experts."""
+    out = []
+    for enc in _encoded(name, layer, int(e), wtype, seed):
+        if wtype == "mxfp4":
+            out.append(formats.mxfp4_decode(*enc))
+        elif wtype == "nvfp4":
+            out.append(formats.nvfp4_decode(*enc))
+        elif wtype == "bf16":
+            out.append(formats.bf16_decode(enc))
+        else:
+            out.append(enc.astype(np.float64))
+    return tuple(out)
+
+
+class LazyExperts:
+    """experts[e] -> the oracle's fp64 (gate, up, down), decoded on access and
+    not kept."""
+
+    def __init__(self, name, layer, wtype, seed=0):
+        self.name, self.layer, self.wtype, self.seed = name, layer, wtype, seed
+
+    def __getitem__(self, e):
+        return oracle_weights_cached(self.name, self.layer, int(e), self.wtype, self.seed)
+
+
+def oracle_combine(name, layer, wtype, x, ids, w, shared_id=None, prefill=False,
+                   include=None, seed=0, threads=None):
+    """olayer.combine over fp64 tokens x [T, H] with ids / w [T, k], the
+    selected experts split over host threads (the shared expert, when
+    shared_id is given, in the first part)."""
+    from oracle import layer as olayer
+    ids = np.asarray(ids)
+    inc = np.ones(ids.shape, dtype=bool) if include is None else np.asarray(include, bool)
+    experts = [int(e) for e in np.unique(ids[inc])]
+    n = max(1, min(threads or ORACLE_THREADS, len(experts)))
+    parts = [experts[i::n] for i in range(n)]
+    lazy = LazyExperts(name, layer, wtype, seed)
+
+    def run(i):
+        mask = inc & np.isin(ids, parts[i])
+        sh = None
+        if i == 0 and shared_id is not None:
+            sh = lazy[shared_id]
+        return olayer.combine(x, ids, w, lazy, shared=sh, prefill=prefill, include=mask)
+
+    with _cf.ThreadPoolExecutor(n) as ex:
+        ys = list(ex.map(run, range(n)))
+    y = ys[0]
+    for p in ys[1:]:
+        y = olayer.merge(y, p)
+    return y

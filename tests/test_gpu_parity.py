@@ -13,7 +13,7 @@ import pytest
 import torch
 
 import synth
-from helpers import GpuLayer, bf16_to_f64, desc_for, oracle_router, oracle_weights
+from helpers import GpuLayer, bf16_to_f64, desc_for, oracle_combine, oracle_router
 from oracle import cache as ocache
 from oracle import formats, layer as olayer
 
@@ -51,6 +51,51 @@ def test_dequant_bit_exact_all_codes_and_scales(ops):
         ref32 = ref.astype(np.float32)
     got = out.cpu().numpy()
     assert np.array_equal(got.view(np.uint32), ref32.view(np.uint32))
+
+
+@pytest.mark.parametrize("wtype", ["mxfp4", "nvfp4"])
+def test_dot_fp4_bit_exact_all_codes_and_scales(ops, wtype):
+    """The decode gate/up rows' block step (FP4 -> BF16 convert, fp32 dot with
+    BF16 x, then the block scale): with x one-hot at each of the 32 positions
+    the result is one element's value, bit for bit the oracle's decode, over
+    every code byte and a range of scale bytes; with random x it is the fp64
+    dot within fp32 summation error."""
+    _say("dot fp4", wtype)
+    codes = np.tile(np.arange(256, dtype=np.uint8).reshape(16, 16), (8, 1))
+    nb = codes.shape[0]
+    if wtype == "mxfp4":
+        scales = np.repeat(np.array([0, 1, 100, 120, 127, 134, 200, 254], dtype=np.uint8), 16)
+        ref = formats.mxfp4_decode(codes, scales.reshape(-1, 1))
+        sc_dev = torch.from_numpy(scales).cuda()
+    else:
+        # E4M3 scale bytes: subnormal, small, unit, large, the largest (448)
+        pairs = np.array([[1, 7], [8, 56], [56, 57], [100, 126], [120, 64], [0x3f, 0x40],
+                          [2, 0x7e], [0x30, 0x31]], dtype=np.uint8)
+        scales = np.repeat(pairs, 16, axis=0)
+        ref = formats.nvfp4_decode(codes, scales, np.float32(1.0))
+        sc_dev = torch.from_numpy(np.ascontiguousarray(scales)).cuda()
+    one_hot = np.zeros((32, 32), dtype=np.uint16)
+    one_hot[np.arange(32), np.arange(32)] = 0x3F80            # bf16 1.0
+    x = torch.from_numpy(one_hot.view(np.int16)).cuda().view(torch.bfloat16)
+    out = torch.empty((nb, 32), dtype=torch.float32, device="cuda")
+    ops.dot_fp4(wtype, torch.from_numpy(codes).cuda(), sc_dev, x, out)
+    torch.cuda.synchronize()
+    with np.errstate(over="ignore"):
+        ref32 = ref.astype(np.float32)
+    # a dot product starts from +0, so a -0 element comes out as +0
+    ref32 = ref32 + np.float32(0.0)
+    assert np.array_equal(out.cpu().numpy().view(np.uint32), ref32.view(np.uint32))
+    rng = np.random.default_rng(12)
+    xr = torch.randn((5, 32), generator=torch.Generator().manual_seed(3)).to(torch.bfloat16)
+    out = torch.empty((nb, 5), dtype=torch.float32, device="cuda")
+    ops.dot_fp4(wtype, torch.from_numpy(codes).cuda(), sc_dev, xr.cuda(), out)
+    torch.cuda.synchronize()
+    dot = ref @ bf16_to_f64(xr).T
+    scale = np.abs(ref) @ np.abs(bf16_to_f64(xr)).T
+    got = out.cpu().numpy().astype(np.float64)
+    finite = scale < 1e38                  # no fp32 overflow on the way
+    assert np.all(np.abs(got - dot)[finite] <= 64 * 2.0 ** -24 * scale[finite] + 1e-45)
+    del rng
 
 
 def _encode_cases():
@@ -187,6 +232,31 @@ def test_mfma_fp4_tile_layout(ops, scale_mode):
 
 
 # ----------------------------------------------------------------- router
+def _check_topk(r, gi, gw, k, renorm=False):
+    """GPU top-k against the oracle's routing r.  Tokens whose fp64 gap
+    between ranks k and k+1 exceeds GAP must match exactly; every token,
+    including the near-tied ones, must hold k distinct ids in descending
+    probability (within GAP), every expert clearly above the k-th probability
+    and none clearly below it, with weights equal to the oracle's p at the
+    GPU's ids (renormalised when asked)."""
+    clear = r["gap"] > GAP
+    assert np.array_equal(gi[clear], r["ids"][clear])
+    assert np.allclose(gw[clear], r["w"][clear], rtol=1e-4, atol=1e-7)
+    for t in range(gi.shape[0]):
+        p = r["p"][t]
+        sel = gi[t]
+        assert np.all((sel >= 0) & (sel < p.size)), t
+        assert np.unique(sel).size == k, ("repeated id", t, sel)
+        ps = p[sel]
+        assert np.all(ps[:-1] >= ps[1:] - GAP), ("not descending", t, ps)
+        kth = np.sort(p)[::-1][k - 1]
+        assert np.all(ps >= kth - GAP), ("below the k-th", t)
+        must = np.nonzero(p > kth + GAP)[0]
+        assert np.all(np.isin(must, sel)), ("missed a clear top-k expert", t)
+        ref_w = ps / ps.sum() if renorm else ps
+        assert np.allclose(gw[t], ref_w, rtol=1e-4, atol=1e-7), ("weights", t)
+
+
 def _check_route(ops, name, T, renorm=False, layer=0):
     s = synth.SHAPES[name]
     from helpers import desc_for
@@ -200,15 +270,7 @@ def _check_route(ops, name, T, renorm=False, layer=0):
     torch.cuda.synchronize()
     r = olayer.route(bf16_to_f64(x), oracle_router(name, layer), s["top_k"], renorm=renorm)
     gi, gw = ids.cpu().numpy(), w.cpu().numpy()
-    clear = r["gap"] > GAP
-    assert clear.mean() > 0.5
-    assert np.array_equal(gi[clear], r["ids"][clear])
-    assert np.allclose(gw[clear], r["w"][clear], rtol=1e-4, atol=1e-7)
-    # exempt tokens: the GPU's choice must still be a valid top-k set
-    for t in np.nonzero(~clear)[0]:
-        p = r["p"][t]
-        kth = np.sort(p)[::-1][s["top_k"] - 1]
-        assert np.all(p[gi[t]] >= kth - GAP)
+    _check_topk(r, gi, gw, s["top_k"], renorm)
     return gi
 
 
@@ -237,6 +299,8 @@ def _run_decode(ops, L, x, ids, w, slot_of=None, fn="decode"):
     ws = ops.workspace(L.desc, T, mode)
     getattr(ops, fn)(L.desc, x, ids, w, L.pool, y, ws, slot_of=slot_of, shared=L.shared)
     torch.cuda.synchronize()
+    if fn == "decode":
+        assert ops.decode_status(ws) == 0, "a wait inside the decode kernel expired"
     return y.cpu().numpy().astype(np.float64)
 
 
@@ -246,13 +310,9 @@ def _oracle_out(L, x, ids, w, tokens=None, include=None, prefill=False, with_sha
     xs = bf16_to_f64(x)[tok]
     ids_t, w_t = ids[tok], w[tok].astype(np.float64)
     inc = None if include is None else include[tok]
-    needed = np.unique(ids_t if inc is None else ids_t[inc])
-    experts = {int(e): oracle_weights(L.name, L.layer, int(e), L.wtype) for e in needed}
-    shared = None
-    if s["shared"] and with_shared:
-        shared = oracle_weights(L.name, L.layer, s["n_experts"], L.wtype)
-    return olayer.combine(xs, ids_t, w_t, experts, shared=shared, prefill=prefill,
-                          include=inc)
+    shared_id = s["n_experts"] if (s["shared"] and with_shared) else None
+    return oracle_combine(L.name, L.layer, L.wtype, xs, ids_t, w_t, shared_id=shared_id,
+                          prefill=prefill, include=inc)
 
 
 def _route_gpu(ops, L, x):
@@ -324,7 +384,8 @@ def test_decode_qwen_full_layer(ops, T):
     assert olayer.row_rel_error(y, ref) < TOL
 
 
-@pytest.mark.parametrize("T,sample", [(1, [0]), (4, [3]), (16, [13])])
+@pytest.mark.parametrize("T,sample", [(1, [0]), (4, [0, 1, 2, 3]),
+                                      (16, [0, 2, 5, 7, 8, 11, 13, 15])])
 def test_decode_dsv4_full_layer_sampled(ops, T, sample):
     _say("decode dsv4 full", T)
     L = GpuLayer("dsv4_mxfp4_decode", layer=7)
@@ -346,6 +407,7 @@ def _route_decode(ops, L, x, slot_of=None, ws=None):
     ops.route_decode(L.desc, x, L.w_router, ids, w, L.pool, y, ws, slot_of=slot_of,
                      shared=L.shared)
     torch.cuda.synchronize()
+    assert ops.decode_status(ws) == 0, "a wait inside the decode kernel expired"
     return ids, w, y, ws
 
 
@@ -367,9 +429,7 @@ def _counters_clear(ws, launches):
 def _check_ids(L, x, gi, gw, renorm=False):
     r = olayer.route(bf16_to_f64(x), oracle_router(L.name, L.layer), L.s["top_k"],
                      renorm=renorm)
-    clear = r["gap"] > GAP
-    assert np.array_equal(gi[clear], r["ids"][clear])
-    assert np.allclose(gw[clear], r["w"][clear], rtol=1e-4, atol=1e-7)
+    _check_topk(r, gi, gw, L.s["top_k"], renorm)
 
 
 @pytest.mark.parametrize("name,T,wtype", [("tiny", 1, "bf16"), ("tiny", 4, "mxfp4"),
@@ -429,7 +489,7 @@ def test_route_decode_renorm(ops, name, T, wtype):
     assert olayer.row_rel_error(y.cpu().numpy(), ref) < TOL
 
 
-@pytest.mark.parametrize("T,sample", [(1, [0]), (4, [1])])
+@pytest.mark.parametrize("T,sample", [(1, [0]), (4, [0, 1, 2, 3]), (16, [1, 4, 6, 9, 10, 12, 14, 15])])
 def test_route_decode_dsv4_full_sampled(ops, T, sample):
     _say("route_decode dsv4", T)
     L = GpuLayer("dsv4_mxfp4_decode", layer=11)
@@ -455,14 +515,43 @@ def test_route_decode_dsv4_nvfp4_sampled(ops):
     assert olayer.row_rel_error(y.cpu().numpy(), ref) < TOL
 
 
-def test_nvfp4_prefill_unsupported(ops):
-    L = GpuLayer("tiny", wtype="nvfp4")
-    x = L.tokens(4)
+@pytest.mark.parametrize("name,T,partial", [("tiny", 4, False), ("ragged_prefill", 1, False),
+                                            ("ragged_prefill", 77, False),
+                                            ("ragged_prefill", 700, True),
+                                            ("mixed_prefill", 400, False)])
+def test_prefill_nvfp4(ops, name, T, partial):
+    """Prefill with NVFP4 experts (BF16 matrix cores, x as given, h rounded to
+    BF16): ragged shapes, multi-tile experts and partial residency against
+    the oracle's BF16-h contract."""
+    _say("prefill nvfp4", name, T, partial)
+    L = GpuLayer(name, wtype="nvfp4")
+    E = L.s["n_experts"]
+    x = L.tokens(T)
     ids, w = _route_gpu(ops, L, x)
-    y = torch.empty((4, L.s["hidden"]), dtype=torch.float32, device="cuda")
-    with pytest.raises(ops._lib.MoeError) as ei:
-        ops.prefill(L.desc, x, ids, w, L.pool, y, ops.workspace(L.desc, 4, 2))
-    assert ei.value.status == ops._lib.MOE_EUNSUPPORTED
+    slot_of, resident = None, np.ones(E, dtype=bool)
+    if partial:
+        resident = np.arange(E) % 4 != 2
+        slot_of = torch.from_numpy(np.where(resident, np.arange(E), -1).astype(np.int32)).cuda()
+    y = _run_decode(ops, L, x, ids, w, slot_of=slot_of, fn="prefill")
+    hi, hw = ids.cpu().numpy(), w.cpu().numpy()
+    ref = _oracle_out(L, x, hi, hw, include=resident[hi] if partial else None, prefill="bf16")
+    assert olayer.row_rel_error(y, ref) < TOL
+
+
+def test_prefill_nvfp4_dsv4_sampled(ops):
+    """DeepSeek-shaped layer with NVFP4 experts at T = 4096: tokens at the
+    first and last rows of expert segments against the oracle."""
+    _say("prefill nvfp4 dsv4 4096")
+    L = GpuLayer("dsv4_mxfp4_prefill", wtype="nvfp4")
+    T = 4096
+    x = L.tokens(T)
+    ids, w = _route_gpu(ops, L, x)
+    y = _run_decode(ops, L, x, ids, w, fn="prefill")
+    assert np.all(np.isfinite(y))
+    hi, hw = ids.cpu().numpy(), w.cpu().numpy()
+    sample = _segment_sample(hi, L.s["n_experts"])
+    ref = _oracle_out(L, x, hi, hw, tokens=sample, prefill="bf16")
+    assert olayer.row_rel_error(y[sample], ref) < TOL
 
 
 def test_route_decode_partial_subset(ops):
@@ -490,6 +579,45 @@ def test_prefill_small(ops, name, T):
     y = _run_decode(ops, L, x, ids, w, fn="prefill")
     ref = _oracle_out(L, x, ids.cpu().numpy(), w.cpu().numpy(), prefill=True)
     assert olayer.row_rel_error(y, ref) < TOL
+
+
+@pytest.mark.parametrize("name,T,partial", [("tiny", 300, False), ("ragged_prefill", 700, True),
+                                            ("ragged_prefill", 1, False),
+                                            ("dsv4_mxfp4_prefill", 4096, False)])
+def test_prefill_sort_integers(ops, name, T, partial):
+    """The prefill expert sort, bit for bit against a host stable sort: the
+    segment starts, the 128-row tile list and the sorted pair ids (resident
+    routed pairs by expert, then the shared expert's), non-resident pairs
+    left out."""
+    _say("prefill sort", name, T, partial)
+    L = GpuLayer(name, wtype="mxfp4")
+    s = L.s
+    E, k = s["n_experts"], s["top_k"]
+    x = L.tokens(T)
+    ids, w = _route_gpu(ops, L, x)
+    resident = np.arange(E) % 3 != 0 if partial else np.ones(E, dtype=bool)
+    slot_of = None
+    if partial:
+        slot_of = torch.from_numpy(np.where(resident, np.arange(E), -1).astype(np.int32)).cuda()
+    y = torch.empty((T, s["hidden"]), dtype=torch.float32, device="cuda")
+    ws = ops.workspace(L.desc, T, 2)
+    ops.prefill(L.desc, x, ids, w, L.pool, y, ws, slot_of=slot_of, shared=L.shared)
+    torch.cuda.synchronize()
+    seg, tiles, pairs = (v.cpu().numpy() for v in ops.prefill_sort_view(L.desc, T, ws))
+    hi = ids.cpu().numpy().reshape(-1)
+    bins = np.where(resident[hi], hi, -1)
+    if s["shared"]:
+        bins = np.concatenate([bins, np.full(T, E)])
+    order = np.argsort(np.where(bins < 0, E + 1, bins), kind="stable")
+    kept = order[bins[order] >= 0]
+    counts = np.bincount(bins[bins >= 0], minlength=E + 1)
+    starts = np.concatenate([[0], np.cumsum(counts)])
+    assert np.array_equal(seg[:E + 2], starts)
+    assert np.array_equal(pairs[:kept.size], kept)
+    ref_tiles = [(b, starts[b] + r) for b in range(E + 1) for r in range(0, counts[b], 128)]
+    assert tiles[0] == len(ref_tiles)
+    assert np.array_equal(tiles[1:1 + 2 * len(ref_tiles)].reshape(-1, 2),
+                          np.array(ref_tiles, dtype=np.int64).reshape(-1, 2))
 
 
 def test_prefill_partial_subset(ops):
@@ -552,16 +680,40 @@ def test_prefill_layer_stream(ops, buffers):
     torch.cuda.synchronize()
 
 
-def test_prefill_dsv4_full_layer_sampled(ops):
-    _say("prefill dsv4 4096")
+def _segment_sample(ids, E, n_experts=4):
+    """Tokens at the first and last rows of expert segments of the prefill
+    sort: token 0 and T-1 (the shared expert's segment, and the rows of the
+    first and last tiles), and the first and last token routed to the lowest
+    routed expert, the highest one, the one with the most tokens and the one
+    with the fewest."""
+    T = ids.shape[0]
+    counts = np.bincount(ids.ravel(), minlength=E)
+    hit = np.nonzero(counts)[0]
+    fewest = int(hit[np.argmin(counts[hit])])
+    picks = [int(hit[0]), int(hit[-1]), int(np.argmax(counts)), fewest][:n_experts]
+    toks = {0, T - 1}
+    for e in picks:
+        rows = np.nonzero((ids == e).any(axis=1))[0]
+        toks.update((int(rows[0]), int(rows[-1])))
+    return sorted(toks)
+
+
+@pytest.mark.parametrize("T", [4096, 8192, 16384])
+def test_prefill_dsv4_full_layer_sampled(ops, T):
+    """DeepSeek-shaped layer at the pages' prefill sizes (every expert hit):
+    tokens at the first and last rows of several expert segments against the
+    oracle's prefill contract."""
+    _say("prefill dsv4", T)
     L = GpuLayer("dsv4_mxfp4_prefill")
-    T = 4096
     x = L.tokens(T)
     ids, w = _route_gpu(ops, L, x)
     y = _run_decode(ops, L, x, ids, w, fn="prefill")
     assert np.all(np.isfinite(y))
-    sample = [7, 4095]
-    ref = _oracle_out(L, x, ids.cpu().numpy(), w.cpu().numpy(), tokens=sample, prefill=True)
+    hi, hw = ids.cpu().numpy(), w.cpu().numpy()
+    sample = _segment_sample(hi, L.s["n_experts"])
+    assert len(sample) >= 8
+    _say("prefill dsv4", T, "oracle on tokens", sample)
+    ref = _oracle_out(L, x, hi, hw, tokens=sample, prefill=True)
     assert olayer.row_rel_error(y[sample], ref) < TOL
 
 
@@ -717,6 +869,120 @@ def test_cache_trace_with_host_experts_merges_to_full_layer(ops, wtype):
         torch.cuda.synchronize()
         full = _oracle_out(L, x, ids_np, w_np)
         assert olayer.row_rel_error(y.cpu().numpy(), full) < TOL, st
+
+
+def test_cache_glm_scale_steps_against_oracle(ops):
+    """GLM-scale expert cache (6144 x 2048 MXFP4 experts, 256 in a pinned
+    host pool, 64 slots) over the first 36 steps of the drifting Zipf trace
+    with q from the planner's q* rule: the device slot table equals the
+    oracle LRU after every step, and at the first (cold) and last step the
+    GPU partial (resident + filled experts) plus the host expert kernel's
+    partial (the other misses) merged on the GPU equals the oracle's full
+    layer."""
+    _say("cache glm scale")
+    name = "glm_cache_decode"
+    s = synth.SHAPES[name]
+    E, k, slots, H = s["n_experts"], s["top_k"], s["slots"], s["hidden"]
+    steps = 36
+    L = GpuLayer(name)
+    eb = L.expert_bytes
+    host_pool = torch.empty(E * eb, dtype=torch.uint8).pin_memory()
+    host_pool.copy_(L.pool.cpu())
+    dev_pool = torch.zeros(slots * eb, dtype=torch.uint8, device="cuda")
+    del L.pool
+    torch.cuda.empty_cache()
+    table = torch.zeros((1, E), dtype=torch.int32, device="cuda")
+    cache = ops.ExpertCache(host_pool, 1, E, eb, dev_pool, slots, table)
+    b_pcie, b_host = 50e9, 178e9                       # fixed rates: q* = 2 of 8 misses
+    cache.set_bandwidths(b_pcie, b_host)
+    side = torch.cuda.Stream()
+    comp = torch.cuda.current_stream()
+    ids_tr, w_tr = synth.zipf_trace(E, k, steps, s["zipf"], s["drift"])
+    oc = ocache.LRUCache(slots)
+    xs = L.tokens(steps)
+    y_host = torch.empty((1, H), dtype=torch.float32).pin_memory()
+    ws = ops.workspace(L.desc, 1, 1)
+    checked = 0
+    for st in range(steps):
+        ids_np, w_np = ids_tr[st:st + 1], w_tr[st:st + 1]
+        plan = cache.plan(0, ids_np, w_np, -1)
+        S, _ = ocache.selected_experts(ids_np, w_np)
+        m = sum((0, int(e)) not in oc.where for e in S)
+        ref_plan = oc.step(0, ids_np, w_np, ocache.qstar(m, b_pcie, b_host))
+        pd = ops.plan_dict(plan)
+        assert pd["fills"] == ref_plan["fills"] and pd["hits"] == ref_plan["hits"], st
+        cache.fill(plan, side, comp)
+        x = xs[st:st + 1]
+        ids = torch.from_numpy(ids_np.astype(np.int32)).cuda()
+        w = torch.from_numpy(w_np.astype(np.float32)).cuda()
+        y = torch.empty((1, H), dtype=torch.float32, device="cuda")
+        ops.decode(L.desc, x, ids, w, dev_pool, y, ws, slot_of=table[0])
+        cache.release(plan, comp)
+        host = set(pd["host"])
+        inc = np.array([[int(e) in host for e in ids_np[0]]], dtype=np.uint8)
+        ops.host_experts(L.desc, x.cpu(), torch.from_numpy(ids_np.astype(np.int32)),
+                         torch.from_numpy(w_np.astype(np.float32)), host_pool, y_host,
+                         include=torch.from_numpy(inc))
+        ops.merge_partials(y, y_host.cuda(non_blocking=True), y)
+        torch.cuda.synchronize()
+        assert np.array_equal(table.cpu().numpy()[0], oc.slot_of_expert(0, E)), st
+        if st in (0, steps - 1):
+            _say("cache glm scale: oracle at step", st, "hits", pd["hits"], "q", plan.q)
+            full = _oracle_out(L, x, ids_np, w_np)
+            assert olayer.row_rel_error(y.cpu().numpy(), full) < TOL, st
+            checked += 1
+    assert ops.decode_status(ws) == 0
+    assert checked == 2
+
+
+def test_cache_victim_fill_waits_for_last_use(ops):
+    """Stream order of a victim fill: a decode reads four slots behind a long
+    matrix product on the compute stream; the next step evicts exactly those
+    slots and fills them on the side stream.  The copies must wait for the
+    decode (the slots' last-use events), so the decode still sees the
+    experts it was planned with: its y equals the oracle's for them, and the
+    later step's y equals the oracle's for the new experts."""
+    _say("cache victim ordering")
+    name = "small_cache"
+    s = synth.SHAPES[name]
+    E, k, H = s["n_experts"], s["top_k"], s["hidden"]
+    L = GpuLayer(name)
+    eb = L.expert_bytes
+    host_pool = torch.empty(E * eb, dtype=torch.uint8).pin_memory()
+    host_pool.copy_(L.pool.cpu())
+    slots = k
+    dev_pool = torch.zeros(slots * eb, dtype=torch.uint8, device="cuda")
+    table = torch.zeros((1, E), dtype=torch.int32, device="cuda")
+    cache = ops.ExpertCache(host_pool, 1, E, eb, dev_pool, slots, table)
+    side = torch.cuda.Stream()
+    comp = torch.cuda.current_stream()
+    a = torch.randn((4096, 4096), device="cuda")
+    b = torch.randn((4096, 4096), device="cuda")
+    x = L.tokens(2)
+    steps = [(np.array([[0, 1, 2, 3]]), np.array([[0.4, 0.3, 0.2, 0.1]], np.float32)),
+             (np.array([[4, 5, 6, 7]]), np.array([[0.35, 0.3, 0.2, 0.15]], np.float32))]
+    ys = []
+    ws = ops.workspace(L.desc, 1, 1)
+    for i, (ids_np, w_np) in enumerate(steps):
+        plan = cache.plan(0, ids_np, w_np, k)
+        if i == 1:
+            victims = sorted(v for v in ops.plan_dict(plan)["victims"])
+            assert victims == [(0, 0), (0, 1), (0, 2), (0, 3)]
+        cache.fill(plan, side, comp)
+        if i == 0:
+            c = a
+            for _ in range(8):                  # tens of ms of work ahead of the decode
+                c = torch.mm(c, b).div_(64.0)
+        y = torch.empty((1, H), dtype=torch.float32, device="cuda")
+        ops.decode(L.desc, x[i:i + 1], torch.from_numpy(ids_np.astype(np.int32)).cuda(),
+                   torch.from_numpy(w_np).cuda(), dev_pool, y, ws, slot_of=table[0])
+        cache.release(plan, comp)
+        ys.append(y)
+    torch.cuda.synchronize()
+    assert ops.decode_status(ws) == 0
+    for i, (ids_np, w_np) in enumerate(steps):
+        ref = _oracle_out(L, x[i:i + 1], ids_np, w_np)
+        assert olayer.row_rel_error(ys[i].cpu().numpy(), ref) < TOL, i
 
 
 def test_cache_injected_fill_failure_rolls_back(ops):
