@@ -19,7 +19,7 @@
 #include <vector>
 
 #include "../../include/moe.h"
-#include "error.hpp"
+#include "hip_error.hpp"
 #include "kernels.hpp"
 #include "planner.hpp"
 

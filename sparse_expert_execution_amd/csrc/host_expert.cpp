@@ -419,10 +419,6 @@ float row_dot(const moe_desc* d, const Layout& L, const uint8_t* blk, int m, int
 
 }  // namespace
 
-// layout of one expert block (shared with the device side)
-void layout(const moe_desc* d, size_t off[6], size_t* bytes);
-int check_desc(const moe_desc* d);
-
 }  // namespace moe
 
 using namespace moe;

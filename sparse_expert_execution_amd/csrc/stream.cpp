@@ -14,7 +14,7 @@
 #include <new>
 
 #include "../../include/moe.h"
-#include "error.hpp"
+#include "hip_error.hpp"
 
 using moe::hip_status;
 using moe::set_error;
