@@ -202,6 +202,26 @@ int moe_route_decode(const moe_desc* desc, const void* x, const void* w_router,
  * MOE_EWORKSPACE if ws is not a decode workspace (< 8 KB or unaligned). */
 int moe_decode_status(void* ws, size_t ws_bytes, int32_t* status, int32_t clear, void* stream);
 
+/* moe_route_decode_noalloc: moe_route_decode for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same arguments and results as
+ * moe_route_decode, without a workspace: the decode workspace is a
+ * file-scope device array of MOE_NOALLOC_SCRATCH_BYTES that each GPU holds
+ * until the process ends (its address is looked up once per device; the
+ * first call on a device clears it with a kernel on `stream`).  A batch
+ * whose moe_workspace_bytes(.., T, MOE_MODE_DECODE) exceeds the array is
+ * rejected with MOE_EWORKSPACE.  No call allocates or frees anything.  Every
+ * call on one GPU shares its array: calls that can overlap on one GPU (other
+ * streams, other host threads) race.  wait_status: device int32 that
+ * receives the wait-expired word of this call's launches (0 = every wait
+ * finished in time; see moe_decode_status), or NULL. */
+#define MOE_NOALLOC_SCRATCH_BYTES (8u << 20)
+int moe_route_decode_noalloc(const moe_desc* desc, const void* x, const void* w_router,
+                             int32_t T, int32_t* ids, float* w,
+                             const int32_t* slot_of_expert, const void* slot_pool,
+                             const void* shared_expert, float* y, int32_t* wait_status,
+                             void* stream);
+
 /* moe_prefill: the same layer for long token batches.  Pairs are
  * counting-sorted by expert and each expert's rows run as a grouped GEMM.
  * MXFP4 weights: x and h are quantised to MXFP4 on the fly (x along H, h

@@ -20,7 +20,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["api.cpp", "host.cpp", "host_expert.cpp", "planner.cpp", "cache.cpp", "stream.cpp", "route.hip",
            "decode.hip", "decode_bf16.hip", "decode_mxfp4.hip", "decode_nvfp4.hip", "prefill.hip",
-           "prefill_nvfp4.hip", "formats.hip"]
+           "prefill_nvfp4.hip", "formats.hip", "noalloc.hip"]
 
 FLAGS = ["--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17", "-Wall",
          "-Wno-unused-function", "-Xclang", "-target-feature", "-Xclang",

@@ -66,6 +66,16 @@ def route_decode(desc, x, w_router, ids, w, pool, y, ws, slot_of=None, shared=No
           "moe_route_decode")
 
 
+def route_decode_noalloc(desc, x, w_router, ids, w, pool, y, wait_status=None, slot_of=None,
+                         shared=None, stream=None):
+    """moe_route_decode_noalloc: route_decode without a workspace (the
+    library's static device scratch); wait_status: optional device int32[1]."""
+    check(lib().moe_route_decode_noalloc(ctypes.byref(desc), _ptr(x), _ptr(w_router),
+                                         x.shape[0], _ptr(ids), _ptr(w), _ptr(slot_of),
+                                         _ptr(pool), _ptr(shared), _ptr(y), _ptr(wait_status),
+                                         _stream(stream)), "moe_route_decode_noalloc")
+
+
 def decode_status(ws, clear=True, stream=None):
     """The decode workspace's wait-expired word (0: every wait inside the
     launches on ws since the last clear finished in time), read after
