@@ -53,6 +53,10 @@ SHAPES = {
     # K = I one (the wide scheme)
     "mixed_prefill": dict(hidden=640, inter=1024, n_experts=9, top_k=3, shared=True,
                           wtype="mxfp4", tokens=(150, 400), layers=1),
+    # prefill with both K (H = 2048, I = 1024) on the wide GEMM scheme and a
+    # shared expert spanning three 128-row tiles at T = 300
+    "deep_prefill": dict(hidden=2048, inter=1024, n_experts=10, top_k=3, shared=True,
+                         wtype="mxfp4", tokens=(50, 300), layers=1),
     "small_cache": dict(hidden=256, inter=128, n_experts=32, top_k=4,
                         shared=False, wtype="mxfp4", tokens=(1,), layers=2,
                         slots=8, steps=64, zipf=1.1, drift=16),
