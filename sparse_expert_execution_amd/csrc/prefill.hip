@@ -319,23 +319,35 @@ struct Tile {
   const uint8_t* base;              // the expert's block
 };
 
-// Workgroup ids go round-robin over the 8 XCDs, each with its own L2.  Ids
-// are grouped so that the nt column tiles of one row tile run together on
-// one XCD: the row tile's A operand is then fetched from HBM once and served
-// from that L2 to the other nt - 1 workgroups.
+// Workgroup ids go round-robin over the 8 XCDs, each with its own L2.  The
+// row tiles are cut into 8 contiguous runs, one per XCD, and an XCD's
+// workgroups walk its run tile by tile, the nt column tiles of a row tile
+// one after another: a row tile's A operand is fetched from HBM once and
+// served from that L2 to its other column tiles, and the row tiles of one
+// expert (consecutive in the sort) run on the same XCD at about the same
+// time, so a weight tile they share is fetched once as well.  The grid has
+// 8 * ceil(max_tiles / 8) * nt workgroups; those past the run exit.
+__device__ __forceinline__ bool xcd_tile(const int32_t* tiles, int nt, int& tile, int& col) {
+  const int x = blockIdx.x & 7, k = blockIdx.x >> 3;
+  const int n = tiles[0];
+  const int run = (n + 7) >> 3;
+  const int i = k / nt;
+  tile = x * run + i;
+  col = k - i * nt;
+  return i < run && tile < n;
+}
+
 template <int MODE>
 __device__ __forceinline__ bool gemm_tile(const GemmArgs& a, Tile& t) {
   const int nout = MODE == 1 ? a.I : a.H;      // output columns of the whole GEMM
   const int bn = MODE == 1 ? kBN / 2 : kBN;    // output columns of one workgroup
   const int nt = (nout + bn - 1) / bn;
-  const int gid = blockIdx.x, per_group = 8 * nt;
-  const int rem = gid % per_group;
-  const int tile = (gid / per_group) * 8 + (rem & 7);
-  if (tile >= a.tiles[0]) return false;
+  int tile, col;
+  if (!xcd_tile(a.tiles, nt, tile, col)) return false;
   const int bin = a.tiles[1 + 2 * tile];
   t.row0 = a.tiles[2 + 2 * tile];
   t.seg_end = a.seg_start[bin + 1];
-  t.col0 = (rem >> 3) * bn;
+  t.col0 = col * bn;
   t.base = bin_base(a, bin);
   return true;
 }

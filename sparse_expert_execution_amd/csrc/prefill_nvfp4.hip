@@ -75,17 +75,18 @@ __global__ __launch_bounds__(kNvThreads, 2) void nv_gemm_kernel(NvPrefillArgs a)
   const int nout = MODE == 1 ? a.I : a.H;
   const int bn = MODE == 1 ? kNvBN / 2 : kNvBN;   // output columns of a workgroup
   const int nt = nout / bn;
-  // tile ids grouped per XCD as in the MXFP4 GEMMs: the nt column tiles of
-  // one row tile run on one XCD, which then serves the rows' activations
-  // from its L2
-  const int gid = blockIdx.x, per_group = 8 * nt;
-  const int rem = gid % per_group;
-  const int tile = (gid / per_group) * 8 + (rem & 7);
-  if (tile >= a.tiles[0]) return;
+  // row tiles in 8 contiguous runs, one per XCD, and a row tile's column
+  // tiles one after another on its XCD, as in the MXFP4 GEMMs: activations
+  // and shared weight tiles are served from that XCD's L2
+  const int x = blockIdx.x & 7, kk = blockIdx.x >> 3;
+  const int run = (a.tiles[0] + 7) >> 3;
+  const int ti = kk / nt;
+  const int tile = x * run + ti;
+  if (ti >= run || tile >= a.tiles[0]) return;
   const int bin = a.tiles[1 + 2 * tile];
   const int row0 = a.tiles[2 + 2 * tile];
   const int seg_end = a.seg_start[bin + 1];
-  const int col0 = (rem >> 3) * bn;
+  const int col0 = (kk - ti * nt) * bn;
   const uint8_t* base = nv_bin_base(a, bin);
   const int K = MODE == 1 ? a.H : a.I;
   const int tid = threadIdx.x, lane = tid & 63;
