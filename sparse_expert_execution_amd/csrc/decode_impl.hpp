@@ -49,8 +49,8 @@ constexpr int kMaxK = 8;
 constexpr int kMaxPairs = kMaxT * kMaxK;
 constexpr int kMaxUnits = kMaxPairs + 1;
 constexpr int kMaxEntries = kMaxPairs + kMaxT;
-constexpr int kXStage16 = 7680;     // 16-byte words of staged x (120 KB)
-constexpr int kHStage4 = 1536;      // float4s of staged h (24 KB)
+constexpr int kXStage16 = 8192;     // 16-byte words of staged x (128 KB: 16 tokens at H 4096)
+constexpr int kHStage4 = 1024;      // float4s of the per-wave h lists (16 KB)
 constexpr int kYOut = 512;          // y results per wave list in the down phase
 constexpr int kDnH4 = kXStage16 + kHStage4 - kW * kYOut / 2;  // float4s of staged h (down)
 constexpr int kMaxCE = 2;           // entries per virtual unit of the down phase, at most
@@ -1417,8 +1417,9 @@ __global__ __launch_bounds__(kT) void decode_kernel(DecArgs a) {
 inline int lx_cap(int lx) { return lx <= 1 ? 1 : lx <= 2 ? 2 : lx <= 4 ? 4 : lx <= 8 ? 8 : -1; }
 inline int nv_cap(int nv) { return nv <= 1 ? 1 : nv <= 2 ? 2 : nv <= 4 ? 4 : nv <= 8 ? 8 : -1; }
 
-// largest I the staged h of one entry fits
-constexpr int kMaxI = 4 * kHStage4;
+// largest I a down pass takes (kMaxCE entries of I values fit its h stage)
+constexpr int kMaxI = 6144;
+static_assert(kMaxCE * kMaxI <= 4 * kDnH4, "a down pass must hold kMaxCE entries");
 
 // tokens one launch can take: x of all of them must fit the LDS stage
 inline int max_tokens(int H) {
