@@ -145,7 +145,7 @@ int moe_route(const moe_desc* desc, const void* x, const void* w_router,
  * contribute: y is the partial sum over the resident subset (the GPU side of
  * the pages' exact split); non-resident pairs are skipped.
  * One persistent kernel per launch of up to moe_decode's per-launch token
- * limit (16, fewer when x of all tokens does not fit 128 KB of LDS; a larger
+ * limit (16, fewer when x of all tokens does not fit 120 KB of LDS; a larger
  * T is split evenly into launches in stream order).  The gate/up rows of all
  * selected experts are split evenly over the grid, h is handed between
  * workgroups through the workspace tagged with the launch's generation, then

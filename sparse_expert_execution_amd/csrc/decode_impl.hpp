@@ -49,8 +49,8 @@ constexpr int kMaxK = 8;
 constexpr int kMaxPairs = kMaxT * kMaxK;
 constexpr int kMaxUnits = kMaxPairs + 1;
 constexpr int kMaxEntries = kMaxPairs + kMaxT;
-constexpr int kXStage16 = 8192;     // 16-byte words of staged x (128 KB: 16 tokens at H 4096)
-constexpr int kHStage4 = 1024;      // float4s of the per-wave h lists (16 KB)
+constexpr int kXStage16 = 7680;     // 16-byte words of staged x (120 KB)
+constexpr int kHStage4 = 1536;      // float4s of the per-wave h lists (24 KB)
 constexpr int kYOut = 512;          // y results per wave list in the down phase
 constexpr int kDnH4 = kXStage16 + kHStage4 - kW * kYOut / 2;  // float4s of staged h (down)
 constexpr int kMaxCE = 2;           // entries per virtual unit of the down phase, at most
@@ -584,6 +584,67 @@ __device__ void build_units_wave(const DecArgs& a, DecLds& S, bool route, bool f
   }
 }
 
+// One routed token: its k experts are distinct (the router's own top-k), so
+// the resident ones, in rank order, are the units, each with one entry, and
+// the list follows from a ballot alone.  Every write below is independent
+// (no LDS read back), which saves the chain of dependent LDS round trips of
+// the general list (about 1.2 us of the call).  Wave 0 only; the result is
+// the general list's for this case.
+__device__ void build_units_t1(const DecArgs& a, DecLds& S, bool from_zsel) {
+  PlanLds& L = S.p;
+  const int lane = threadIdx.x & 63;
+  const int k = a.k, E = a.E;
+  const bool live = lane < k;
+  const int e = live ? L.ids[lane] : -1;
+  float wp = 0.f;
+  if (live) wp = from_zsel ? expf(L.zsel[lane] - L.mx[0]) * L.inv[0] : L.w[lane];
+  if (from_zsel && a.renorm) {
+    float sum = wp;
+    sum += dpp_f<kDppXor1>(sum);       // k <= 8 lanes: a row-local sum is enough
+    sum += dpp_f<kDppXor2>(sum);
+    sum += dpp_f<kDppHalfMirror>(sum);
+    if (live) wp /= sum;
+  }
+  if (blockIdx.x == 0 && live) {
+    a.ids[lane] = e;
+    a.w[lane] = wp;
+  }
+  int slot = -1;
+  if (live && e >= 0 && e < E) slot = a.slot_of ? a.slot_of[e] : e;
+  const bool ok = slot >= 0;
+  const uint64_t m = __ballot(ok);
+  const int n_routed = __popcll(m);
+  const int u = __popcll(m & ((1ull << lane) - 1ull));
+  if (ok) {
+    L.unit_expert[u] = e;
+    L.unit_slot[u] = slot;
+    L.unit_start[u] = u;
+    L.ent_pair[u] = lane;
+    L.ent_tok[u] = 0;
+    L.ent_gw[u] = wp;
+    L.vu_unit[u] = u;
+    L.vu_e0[u] = u;
+    L.vu_n[u] = 1;
+  }
+  const int n_units = n_routed + (a.shared ? 1 : 0);
+  if (lane == 0) {
+    if (a.shared) {
+      L.unit_slot[n_routed] = -1;
+      L.unit_start[n_routed] = n_routed;
+      L.ent_pair[n_routed] = k;
+      L.ent_tok[n_routed] = 0;
+      L.ent_gw[n_routed] = 1.f;
+      L.vu_unit[n_routed] = n_routed;
+      L.vu_e0[n_routed] = n_routed;
+      L.vu_n[n_routed] = 1;
+    }
+    L.unit_start[n_units] = n_units;
+    L.n_routed = n_routed;
+    L.n_units = n_units;
+    L.n_vu = n_units;
+  }
+}
+
 // Expert list of this launch, built the same way in every workgroup: the
 // distinct resident experts in order of first appearance over the (token,
 // rank) pairs, each with its pairs, then the shared expert.
@@ -611,6 +672,11 @@ __device__ void build_units(const DecArgs& a, DecLds& S, bool route, bool timing
     __syncthreads();
   }
   stamp(timing, a, 9);
+  if (route && T == 1) {
+    if (wave == 0) build_units_t1(a, S, from_zsel);
+    __syncthreads();
+    return;
+  }
   if (P + (a.shared ? 1 : 0) <= 64) {
     if (wave == 0) build_units_wave<CE, DPP>(a, S, route, from_zsel);
     __syncthreads();

@@ -413,8 +413,8 @@ def _route_decode(ops, L, x, slot_of=None, ws=None):
 
 def _launches(L, T):
     """Kernel launches of one decode call: x of every token of a launch must
-    fit the 128 KB LDS stage, and a launch takes at most 16 tokens."""
-    per = min(65536 // L.s["hidden"], 16)
+    fit the 120 KB LDS stage, and a launch takes at most 16 tokens."""
+    per = min(61440 // L.s["hidden"], 16)
     return (T + per - 1) // per
 
 
