@@ -144,8 +144,12 @@ __device__ void signal_done(unsigned* count) {
                            __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// wave 0 only: wait until the lines of a spread count add up to target
-__device__ void wait_count(const DecArgs& a, unsigned* count, unsigned target) {
+// wave 0 only: wait until the lines of a spread count add up to target (the
+// header's error word is set when the wait gives up).  It takes the header
+// rather than the kernel's arguments: a call the compiler does not inline
+// would otherwise copy the whole argument block into scratch memory, and
+// every later argument read would go through it.
+__device__ void wait_count(unsigned* hdr, unsigned* count, unsigned target) {
   const int lane = threadIdx.x & 63;
   unsigned spins = 0;
   int nap = 1;
@@ -161,7 +165,7 @@ __device__ void wait_count(const DecArgs& a, unsigned* count, unsigned target) {
     if (nap < 8) nap <<= 1;
     if (++spins > kSpinLimit) {
       if (lane == 0)
-        __hip_atomic_store(a.hdr + kHError, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(hdr + kHError, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       break;
     }
   }
@@ -186,7 +190,7 @@ __device__ __forceinline__ const uint64_t* zcopy(const DecArgs& a) {
 
 // one wave: logits of expert lane + 64 i of row zt into v (-inf past E)
 template <int M>
-__device__ void z_load(const DecArgs& a, const uint64_t* zt, unsigned gen, float v[M]) {
+__device__ __forceinline__ void z_load(const DecArgs& a, const uint64_t* zt, unsigned gen, float v[M]) {
   const int lane = threadIdx.x & 63;
   bool have[M];
 #pragma unroll
@@ -355,7 +359,7 @@ __device__ __forceinline__ void router_dot(const DecArgs& a, const DecLds& S, in
 // this wave's router items from `item` on (its first round already loaded
 // into w), each z written with an agent-coherent store
 template <int WT>
-__device__ void router_items_run(const DecArgs& a, const DecLds& S, int item, RouterRow& w,
+__device__ __forceinline__ void router_items_run(const DecArgs& a, const DecLds& S, int item, RouterRow& w,
                                  unsigned gen) {
   const int lane = threadIdx.x & 63;
   const int n_items = router_items(a), nr = router_rounds(a);
@@ -407,7 +411,7 @@ __device__ __forceinline__ float group_sum(float v, int lr) {
 // softmax max and 1 / sum (mx, inv; max-subtracted, fp32).
 constexpr int kRankItems = 128;
 
-__device__ void rank_topk(const DecArgs& a, DecLds& S, unsigned gen) {
+__device__ __forceinline__ void rank_topk(const DecArgs& a, DecLds& S, unsigned gen) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int T = a.T, E = a.E, k = a.k, n = T * E;
   const int E4 = (E + 3) & ~3;             // rows padded to whole float4s with -inf
@@ -498,7 +502,7 @@ __device__ __forceinline__ int wave_scan(int v) {
 // the gate weights come from the selected logits and the softmax statistics
 // (renormalised here when asked), else they are in L.w.
 template <int CE, bool DPP>
-__device__ void build_units_wave(const DecArgs& a, DecLds& S, bool route, bool from_zsel) {
+__device__ __forceinline__ void build_units_wave(const DecArgs& a, DecLds& S, bool route, bool from_zsel) {
   PlanLds& L = S.p;
   const int lane = threadIdx.x & 63;
   const int T = a.T, k = a.k, E = a.E, P = T * k;
@@ -590,7 +594,7 @@ __device__ void build_units_wave(const DecArgs& a, DecLds& S, bool route, bool f
 // (no LDS read back), which saves the chain of dependent LDS round trips of
 // the general list (about 1.2 us of the call).  Wave 0 only; the result is
 // the general list's for this case.
-__device__ void build_units_t1(const DecArgs& a, DecLds& S, bool from_zsel) {
+__device__ __forceinline__ void build_units_t1(const DecArgs& a, DecLds& S, bool from_zsel) {
   PlanLds& L = S.p;
   const int lane = threadIdx.x & 63;
   const int k = a.k, E = a.E;
@@ -649,7 +653,7 @@ __device__ void build_units_t1(const DecArgs& a, DecLds& S, bool from_zsel) {
 // distinct resident experts in order of first appearance over the (token,
 // rank) pairs, each with its pairs, then the shared expert.
 template <int M, int CE, bool DPP>
-__device__ void build_units(const DecArgs& a, DecLds& S, bool route, bool timing, unsigned gen) {
+__device__ __forceinline__ void build_units(const DecArgs& a, DecLds& S, bool route, bool timing, unsigned gen) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int T = a.T, k = a.k, E = a.E, P = T * k;
   PlanLds& L = S.p;
@@ -795,7 +799,7 @@ __device__ __forceinline__ const uint8_t* unit_base(const DecArgs& a, int slot) 
 // ---------------------------------------------------------------------------
 // x of every token into LDS in the layout DecLds::xs describes
 template <int WT>
-__device__ void stage_x(const DecArgs& a, DecLds& S) {
+__device__ __forceinline__ void stage_x(const DecArgs& a, DecLds& S) {
   constexpr int CPV = WT == 1 ? 1 : 4;
   const int NV = a.H / (8 * CPV);
   const int n = a.T * a.H / 8;
@@ -920,21 +924,34 @@ __device__ __forceinline__ void flush_h(const DecArgs& a, WaveOut& o) {
 // a per-wave list in the h stage of LDS.  SHARED: the list is the shared
 // expert's I rows and its entries are all T tokens (known before routing).
 template <int WT, int LXC, int RG, bool SHARED, class After>
-__device__ void gateup_range(const DecArgs& a, DecLds& S, int64_t q0, int64_t q1,
+__device__ __forceinline__ void gateup_range(const DecArgs& a, DecLds& S, int64_t q0, int64_t q1,
                              After&& after) {
   const int lane = threadIdx.x & 63, wave = uni((int)(threadIdx.x >> 6));
   const int I = a.I;
   const int64_t first = q0 + wave;
   const int nq = first < q1 ? (int)((q1 - first + kW - 1) / kW) : 0;
-  auto row_of = [&](int m, int& u, int& i) {
-    const int64_t q = first + (int64_t)m * kW;
-    if (SHARED) { u = -1; i = (int)q; }
-    else { u = (int)(q / I); i = (int)(q - (int64_t)u * I); }
+  // (unit, row) cursors of the row computed next and of the row loaded next;
+  // both step by kW rows, so only the first position takes a division
+  int cu = -1, ci = 0;
+  if (nq > 0) {
+    if (SHARED) {
+      ci = (int)first;
+    } else {
+      cu = (int)(first / I);
+      ci = (int)(first - (int64_t)cu * I);
+    }
+  }
+  auto step = [&](int& u, int& i) {
+    i += kW;
+    if (!SHARED)
+      while (i >= I) {
+        i -= I;
+        ++u;
+      }
   };
-  auto load = [&](int m, GuBuf<LXC>& b) {
-    int u, i;
-    row_of(m, u, i);
-    gu_load<WT, LXC>(a, SHARED ? a.shared : unit_base(a, S.p.unit_slot[u]), i, lane, b);
+  int lu = cu, li = ci;
+  auto load = [&](GuBuf<LXC>& b) {
+    gu_load<WT, LXC>(a, SHARED ? a.shared : unit_base(a, S.p.unit_slot[lu]), li, lane, b);
   };
   WaveOut out;
   out.cap = kHStage4 / kW * 2;
@@ -943,30 +960,35 @@ __device__ void gateup_range(const DecArgs& a, DecLds& S, int64_t q0, int64_t q1
   GuBuf<LXC> buf[RG];
 #pragma unroll
   for (int r = 0; r < RG; ++r)
-    if (r < nq) load(r, buf[r]);
+    if (r < nq) {
+      load(buf[r]);
+      step(lu, li);
+    }
   after();                                 // more loads, behind the first rows
   for (int m0 = 0; m0 < nq; m0 += RG) {
 #pragma unroll
     for (int r = 0; r < RG; ++r) {
       const int m = m0 + r;
       if (m < nq) {
-        int u, i;
-        row_of(m, u, i);
-        const int e0 = SHARED ? 0 : S.p.unit_start[u];
-        const int ne = SHARED ? a.T : S.p.unit_start[u + 1] - e0;
+        const int e0 = SHARED ? 0 : S.p.unit_start[cu];
+        const int ne = SHARED ? a.T : S.p.unit_start[cu + 1] - e0;
         float mine = 0.f;        // lane q keeps entry q's h
         for (int q = 0; q < ne; ++q) {
           const int t = SHARED ? q : S.p.ent_tok[e0 + q];
           const float hv = gu_dot<WT, LXC>(a, S, buf[r], t, lane);
           if (lane == q) mine = hv;
         }
-        if (m + RG < nq) load(m + RG, buf[r]);
+        if (m + RG < nq) {
+          load(buf[r]);
+          step(lu, li);
+        }
         if (out.n + ne > out.cap) flush_h(a, out);
         if (lane < ne) {
           const int pair = SHARED ? a.T * a.k + lane : S.p.ent_pair[e0 + lane];
-          out.buf[out.n + lane] = make_int2(pair * I + i, __float_as_int(mine));
+          out.buf[out.n + lane] = make_int2(pair * I + ci, __float_as_int(mine));
         }
         out.n += ne;
+        step(cu, ci);
       }
     }
   }
@@ -1063,7 +1085,7 @@ __device__ __forceinline__ int dn_row(const DnLane& L, const DnCur<CE>& c, int w
 // segments as the h stage and the y lists hold (the last one may be cut at a
 // step); *steps = the pass's steps.  The first step always fits (kMaxCE
 // entries of I values fit the stage, kMaxCE * rpw results a list).
-__device__ int pass_end(const DecArgs& a, const DecLds& S, int p0, int d1, const DnLane& L,
+__device__ __forceinline__ int pass_end(const DecArgs& a, const DecLds& S, int p0, int d1, const DnLane& L,
                         int* steps) {
   const int E0 = uni(S.p.vu_e0[p0 / a.H]);
   const int hcap = kDnH4 * 4 / a.I;
@@ -1257,7 +1279,7 @@ __device__ __forceinline__ void dn_compute(const DecArgs& a, const DecLds& S, co
 // polled until it carries this launch's generation; a thread loads the four
 // values of up to four float4s before it checks any of them
 template <int WT>
-__device__ void stage_h(const DecArgs& a, DecLds& S, int c0, int c1) {
+__device__ __forceinline__ void stage_h(const DecArgs& a, DecLds& S, int c0, int c1) {
   constexpr int EPV = WT == 1 ? 8 : 32;
   constexpr int B = 4;
   const int I4 = a.I / 4, V = a.I / EPV;
@@ -1445,7 +1467,7 @@ __global__ __launch_bounds__(kT) void decode_kernel(DecArgs a) {
     }
     if (!y_clear) {
       if (__builtin_amdgcn_readfirstlane((unsigned)wave_sum_dpp((float)yz)) < (unsigned)G)
-        wait_count(a, a.hdr + kHYZero, (unsigned)G);
+        wait_count(a.hdr, a.hdr + kHYZero, (unsigned)G);
       y_clear = true;
     }
     flush_y(a, out);
