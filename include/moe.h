@@ -141,12 +141,17 @@ int moe_route(const moe_desc* desc, const void* x, const void* w_router,
 /* moe_decode: y[t] = sum over j of w[t][j] * FFN_{ids[t][j]}(x[t])
  *                    (+ FFN_shared(x[t]) when desc->has_shared),
  * FFN_e(x) = W_down (silu(W_gate x) * (W_up x)), silu(z) = z / (1 + e^-z),
- * fp32 accumulation, x as given (BF16), h in fp32.  Only experts with a slot
+ * fp32 accumulation, x as given (BF16), h in fp32.  MXFP4 launches of 2 to
+ * 8 tokens with H and I multiples of 256 run on the scaled FP4 matrix
+ * instruction, which takes its activations as e4m3: x enters as two e4m3
+ * parts per element under a power-of-two scale per 32 (exact for a BF16
+ * value unless it is 2^-15 or more below its block's largest) and h as
+ * three (about 12 significant bits); products and sums stay fp32.  Only experts with a slot
  * contribute: y is the partial sum over the resident subset (the GPU side of
  * the pages' exact split); non-resident pairs are skipped.
- * One persistent kernel per launch of up to moe_decode's per-launch token
- * limit (16, fewer when x of all tokens does not fit 120 KB of LDS; a larger
- * T is split evenly into launches in stream order).  The gate/up rows of all
+ * One persistent kernel per launch of up to moe_decode_launch_tokens(desc)
+ * tokens (a larger T is split evenly into launches in stream order).  The
+ * gate/up rows of all
  * selected experts are split evenly over the grid, h is handed between
  * workgroups through the workspace tagged with the launch's generation, then
  * the down rows are split evenly and each row's gate-weighted result is
@@ -191,6 +196,13 @@ int moe_route_decode(const moe_desc* desc, const void* x, const void* w_router,
                      const int32_t* slot_of_expert, const void* slot_pool,
                      const void* shared_expert, float* y, void* ws,
                      size_t ws_bytes, void* stream);
+
+/* moe_decode_launch_tokens: tokens one decode kernel launch takes for this
+ * layer shape (at most 16; fewer when the LDS stages of x, or of h on the
+ * matrix-core MXFP4 path, would not fit); moe_decode and moe_route_decode
+ * split a larger T evenly into ceil(T / this) launches.  Host only.  A
+ * negative MOE_E* code if the shape has no decode kernel. */
+int32_t moe_decode_launch_tokens(const moe_desc* desc);
 
 /* moe_decode_status: the decode workspace's wait-expired word (non-zero when
  * a bounded wait inside a moe_decode / moe_route_decode launch on this

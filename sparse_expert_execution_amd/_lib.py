@@ -33,7 +33,7 @@ PLAN_MAX = 256
 # every symbol include/moe.h declares
 EXPORTS = (
     "moe_expert_layout", "moe_workspace_bytes", "moe_route", "moe_decode",
-    "moe_route_decode", "moe_route_decode_noalloc", "moe_prefill", "moe_merge_partials", "moe_quantize_mxfp4",
+    "moe_route_decode", "moe_route_decode_noalloc", "moe_decode_launch_tokens", "moe_prefill", "moe_merge_partials", "moe_quantize_mxfp4",
     "moe_pack_expert", "moe_decode_status", "moe_debug_prefill_layout", "moe_debug_dot_fp4", "moe_debug_dequant_mxfp4", "moe_debug_mfma_fp4_tile", "moe_debug_read_probe", "moe_debug_wave_scan", "moe_qstar",
     "moe_planner_create", "moe_planner_destroy", "moe_planner_set_bandwidths",
     "moe_planner_plan", "moe_planner_rollback", "moe_planner_slot_table",
@@ -98,6 +98,7 @@ def lib():
         "moe_prefill": (ctypes.c_int, [DP, P, I32, P, P, P, P, P, P, P, SZ, P]),
         "moe_route_decode": (ctypes.c_int, [DP, P, P, I32, P, P, P, P, P, P, P, SZ, P]),
         "moe_route_decode_noalloc": (ctypes.c_int, [DP, P, P, I32, P, P, P, P, P, P, P, P]),
+        "moe_decode_launch_tokens": (I32, [DP]),
         "moe_merge_partials": (ctypes.c_int, [P, P, P, SZ, P]),
         "moe_quantize_mxfp4": (ctypes.c_int, [P, I32, I32, I64, P, P, P]),
         "moe_pack_expert": (ctypes.c_int, [DP, P, P, P, I32, P, P]),

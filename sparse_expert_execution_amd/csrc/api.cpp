@@ -185,10 +185,10 @@ static int decode_impl(const moe_desc* desc, const void* x, const void* w_router
                ? (int64_t)(off[5] + (size_t)desc->hidden * desc->inter / 16) : 0;
   f.H = desc->hidden; f.I = desc->inter; f.E = desc->n_experts; f.k = desc->top_k;
   f.wtype = desc->wtype;
-  // launches of at most decode_max_tokens(H) tokens, in stream order, the
+  // launches of at most decode_max_tokens tokens, in stream order, the
   // batch split evenly over them
   const int H = desc->hidden, k = desc->top_k;
-  const int cap = moe::decode_max_tokens(H);
+  const int cap = moe::decode_max_tokens(desc->wtype, H, desc->inter);
   const int n_launch = (T + cap - 1) / cap;
   const int per = (T + n_launch - 1) / n_launch;
   for (int t0 = 0; t0 < T; t0 += per) {
@@ -202,6 +202,15 @@ static int decode_impl(const moe_desc* desc, const void* x, const void* w_router
     if (st) return st;
   }
   return MOE_OK;
+}
+
+int32_t moe_decode_launch_tokens(const moe_desc* desc) {
+  const int st = check_desc(desc);
+  if (st) return st;
+  if (!moe::decode_shape_supported(desc->wtype, desc->hidden, desc->inter))
+    return set_error(MOE_EUNSUPPORTED, "decode shape H=%d I=%d not compiled", desc->hidden,
+                     desc->inter);
+  return moe::decode_max_tokens(desc->wtype, desc->hidden, desc->inter);
 }
 
 int moe_decode(const moe_desc* desc, const void* x, int32_t T, const int32_t* ids, const float* w,

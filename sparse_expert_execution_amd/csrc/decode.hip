@@ -35,10 +35,15 @@ hipError_t launch_route_small(const void* x, const void* w_router, int router_f3
   return router_f32 ? launch_route_r<true>(a, st) : launch_route_r<false>(a, st);
 }
 
-int decode_max_tokens(int H) { return max_tokens(H); }
+int decode_max_tokens(int wtype, int H, int I) {
+  const int t = max_tokens(H);
+  const int m = wtype == 2 ? mf_max_tokens(H, I) : 0;
+  return m > 0 && m < t ? m : t;
+}
 
 hipError_t launch_decode(const DecodeLaunch& f, hipStream_t st) {
-  if (f.T < 1 || f.T > max_tokens(f.H) || f.k > kMaxK || f.E > kMaxE) return hipErrorInvalidValue;
+  if (f.T < 1 || f.T > decode_max_tokens(f.wtype, f.H, f.I) || f.k > kMaxK || f.E > kMaxE)
+    return hipErrorInvalidValue;
   DecArgs a;
   a.x = static_cast<const uint16_t*>(f.x);
   a.wr = f.w_router;

@@ -54,6 +54,7 @@ constexpr int kHStage4 = 1536;      // float4s of the per-wave h lists (24 KB)
 constexpr int kYOut = 512;          // y results per wave list in the down phase
 constexpr int kDnH4 = kXStage16 + kHStage4 - kW * kYOut / 2;  // float4s of staged h (down)
 constexpr int kMaxCE = 2;           // entries per virtual unit of the down phase, at most
+constexpr int kMfTab = 64;          // row groups per batch of the matrix-core path, at most
 constexpr unsigned kSpinLimit = 1u << 21;
 
 // a value the same in every lane of the wave, kept in a scalar register
@@ -259,6 +260,12 @@ struct PlanLds {
   // down work: each unit's entries in chunks of at most CE (virtual units)
   int vu_unit[kMaxEntries], vu_e0[kMaxEntries], vu_n[kMaxEntries];
   int n_routed, n_units, n_vu;
+  // matrix-core path: the row groups of one batch (slot of the expert block,
+  // -1 the shared expert; first row; unit).  A slot, not a pointer: a
+  // pointer read back from LDS loses its address space and every load
+  // through it becomes a flat load, whose waits cannot be counted.
+  int mf_slot[kMfTab], mf_row[kMfTab], mf_unit[kMfTab];
+  int mf_hoff[kMfTab];     // down: byte offset of the group's unit's h stage
 };
 
 struct DecLds {
@@ -271,6 +278,8 @@ struct DecLds {
       uint4 xs[kXStage16];
       float4 hs[kHStage4];         // per-wave lists of gate/up h results
     } g;
+    // the matrix-core path lays out its own stages in the same bytes
+    uint8_t raw[(kXStage16 + kHStage4) * 16];
     struct {                       // down
       int2 yout[kW * kYOut];       // per-wave lists of y results
       // h of the entries of one down pass; an entry's I values as float4s at
@@ -411,11 +420,10 @@ __device__ __forceinline__ float group_sum(float v, int lr) {
 // softmax max and 1 / sum (mx, inv; max-subtracted, fp32).
 constexpr int kRankItems = 128;
 
-__device__ __forceinline__ void rank_topk(const DecArgs& a, DecLds& S, unsigned gen) {
+__device__ __forceinline__ void rank_topk(const DecArgs& a, DecLds& S, unsigned gen, float* zs) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int T = a.T, E = a.E, k = a.k, n = T * E;
   const int E4 = (E + 3) & ~3;             // rows padded to whole float4s with -inf
-  float* zs = reinterpret_cast<float*>(S.g.hs);
   for (int i = threadIdx.x; i < T * E4; i += kT) {
     const int t = i / E4, e = i - t * E4;
     float z = -INFINITY;
@@ -653,13 +661,14 @@ __device__ __forceinline__ void build_units_t1(const DecArgs& a, DecLds& S, bool
 // distinct resident experts in order of first appearance over the (token,
 // rank) pairs, each with its pairs, then the shared expert.
 template <int M, int CE, bool DPP>
-__device__ __forceinline__ void build_units(const DecArgs& a, DecLds& S, bool route, bool timing, unsigned gen) {
+__device__ __forceinline__ void build_units(const DecArgs& a, DecLds& S, bool route, bool timing, unsigned gen,
+                                            float* zs) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int T = a.T, k = a.k, E = a.E, P = T * k;
   PlanLds& L = S.p;
   const bool from_zsel = route && T * E <= kRankItems;
   if (from_zsel) {
-    rank_topk(a, S, gen);
+    rank_topk(a, S, gen, zs);
   } else if (route) {
     for (int t = wave; t < T; t += kW) {
       float v[M];
@@ -1329,6 +1338,35 @@ __device__ __forceinline__ void stage_h(const DecArgs& a, DecLds& S, int c0, int
   }
 }
 
+// Exit of a launch: workgroups are counted per group (b % kNCtr), then the
+// groups; the last workgroup out clears the counts and advances the
+// generation, so the next launch on this workspace starts from zero.
+__device__ __forceinline__ void finish_launch(const DecArgs& a, unsigned gen) {
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int bid = blockIdx.x, G = a.G;
+    const int grp = bid % kNCtr;
+    const unsigned gsize = (unsigned)((G - grp + kNCtr - 1) / kNCtr);
+    const unsigned ngrp = (unsigned)(G < kNCtr ? G : kNCtr);
+    const unsigned old = __hip_atomic_fetch_add(a.hdr + kHExit + grp * kLine, 1u,
+                                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (old == gsize - 1 &&
+        __hip_atomic_fetch_add(a.hdr + kHExitTop, 1u, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT) == ngrp - 1) {
+      for (int j = 0; j < kNCtr; ++j) {
+        __hip_atomic_store(a.hdr + kHYZero + j * kLine, 0u, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(a.hdr + kHExit + j * kLine, 0u, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+      }
+      __hip_atomic_store(a.hdr + kHExitTop, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(a.hdr + kHGen, gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (a.hdr[kHTiming])
+        reinterpret_cast<unsigned long long*>(a.hdr + kHStamps)[4] = wall_clock64();
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // the kernel.  WT: 1 BF16, 2 MXFP4.  LXC, NVC: register capacity (vectors per
 // lane) of a gate/up row and of a down row.  M: logits per lane in the wave
@@ -1380,7 +1418,7 @@ __global__ __launch_bounds__(kT) void decode_kernel(DecArgs a) {
   stamp(timing, a, 8);
 
   // 2. the expert list
-  build_units<M, CE, WT != 1>(a, S, route, timing, gen);
+  build_units<M, CE, WT != 1>(a, S, route, timing, gen, reinterpret_cast<float*>(S.g.hs));
   stamp(timing, a, 1);
   const int n_routed = S.p.n_routed;
 
@@ -1477,28 +1515,7 @@ __global__ __launch_bounds__(kT) void decode_kernel(DecArgs a) {
   // exit: counted per group of workgroups (b % kNCtr), then per group; the
   // last workgroup out clears the counts and advances the generation
   stamp(timing, a, 3);
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const int grp = bid % kNCtr;
-    const unsigned gsize = (unsigned)((G - grp + kNCtr - 1) / kNCtr);
-    const unsigned ngrp = (unsigned)(G < kNCtr ? G : kNCtr);
-    const unsigned old = __hip_atomic_fetch_add(a.hdr + kHExit + grp * kLine, 1u,
-                                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (old == gsize - 1 &&
-        __hip_atomic_fetch_add(a.hdr + kHExitTop, 1u, __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT) == ngrp - 1) {
-      for (int j = 0; j < kNCtr; ++j) {
-        __hip_atomic_store(a.hdr + kHYZero + j * kLine, 0u, __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(a.hdr + kHExit + j * kLine, 0u, __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
-      }
-      __hip_atomic_store(a.hdr + kHExitTop, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(a.hdr + kHGen, gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (a.hdr[kHTiming])
-        reinterpret_cast<unsigned long long*>(a.hdr + kHStamps)[4] = wall_clock64();
-    }
-  }
+  finish_launch(a, gen);
 }
 
 // capacities compiled per weight format
@@ -1625,3 +1642,5 @@ hipError_t launch_route_r(const RouteArgs& a, hipStream_t st) {
 
 }  // namespace dec
 }  // namespace moe
+
+#include "decode_mfma.hpp"

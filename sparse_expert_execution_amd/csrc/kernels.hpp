@@ -94,7 +94,7 @@ inline size_t decode_z_copy_bytes(int T, int E) {
 // decode: router (optional) + experts + combine in one kernel, at most
 // decode_max_tokens(H) tokens per launch
 bool decode_shape_supported(int wtype, int H, int I);
-int decode_max_tokens(int H);
+int decode_max_tokens(int wtype, int H, int I);
 hipError_t launch_decode(const DecodeLaunch& f, hipStream_t st);
 
 // prefill

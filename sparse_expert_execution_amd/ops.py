@@ -76,6 +76,13 @@ def route_decode_noalloc(desc, x, w_router, ids, w, pool, y, wait_status=None, s
                                          _stream(stream)), "moe_route_decode_noalloc")
 
 
+def decode_launch_tokens(desc):
+    """moe_decode_launch_tokens: tokens one decode launch takes for this shape."""
+    n = lib().moe_decode_launch_tokens(ctypes.byref(desc))
+    check(n if n < 0 else 0, "moe_decode_launch_tokens")
+    return n
+
+
 def decode_status(ws, clear=True, stream=None):
     """The decode workspace's wait-expired word (0: every wait inside the
     launches on ws since the last clear finished in time), read after

@@ -57,6 +57,10 @@ SHAPES = {
     # shared expert spanning three 128-row tiles at T = 300
     "deep_prefill": dict(hidden=2048, inter=1024, n_experts=10, top_k=3, shared=True,
                          wtype="mxfp4", tokens=(50, 300), layers=1),
+    # decode on the matrix-core MXFP4 path (H, I multiples of 256) at sizes
+    # the oracle takes whole: 8 tokens per launch, 11 split into two
+    "mfma_decode": dict(hidden=512, inter=256, n_experts=12, top_k=3, shared=True,
+                        wtype="mxfp4", tokens=(1, 3, 8, 11), layers=1),
     "small_cache": dict(hidden=256, inter=128, n_experts=32, top_k=4,
                         shared=False, wtype="mxfp4", tokens=(1,), layers=2,
                         slots=8, steps=64, zipf=1.1, drift=16),

@@ -115,6 +115,25 @@ def test_workspace_sizes(L):
     assert L.moe_workspace_bytes(ctypes.byref(d), 4, 9) == 0
 
 
+@pytest.mark.parametrize("shape,wtype,want", [
+    ((2048, 768), 1, 16),      # BF16: 16, x of 16 tokens fits the 120 KB stage
+    ((4096, 1024), 1, 15),     # BF16: 120 KB / (2 H) tokens
+    ((800, 96), 2, 16),        # MXFP4, H not a multiple of 128: the vector kernel
+    ((4096, 2048), 2, 8),      # MXFP4 on the matrix core: BF16 x, its two
+    ((6144, 2048), 2, 5),      #   e4m3 parts and scales in 144 KB of LDS
+    ((4096, 128), 2, 15),      # MXFP4 with I not a multiple of 256: the vector kernel
+    ((512, 256), 2, 8),
+    ((4096, 2048), 3, 15),     # NVFP4: the vector kernel
+])
+def test_decode_launch_tokens(L, shape, wtype, want):
+    """Per-launch token cap of the decode (the split of a larger batch)."""
+    H, I = shape
+    d = _desc(hidden=H, inter=I, n_experts=256, top_k=6, has_shared=1, wtype=wtype)
+    assert L.moe_decode_launch_tokens(ctypes.byref(d)) == want
+    bad = _desc(hidden=H, inter=I + 1, n_experts=256, top_k=6, has_shared=1, wtype=wtype)
+    assert L.moe_decode_launch_tokens(ctypes.byref(bad)) < 0
+
+
 def test_qstar_matches_oracle(L):
     for m in range(0, 20):
         for bp, bh in [(51.5, 178.0), (11.8, 90.0), (50, 50), (64, 8), (1, 1000), (3, 7)]:

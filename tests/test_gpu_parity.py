@@ -347,10 +347,11 @@ def test_decode_ragged_shapes(ops, T):
     assert olayer.row_rel_error(y, ref) < TOL
 
 
-def test_decode_partial_over_resident_subset(ops):
+@pytest.mark.parametrize("name", ["ragged_decode", "mfma_decode"])
+def test_decode_partial_over_resident_subset(ops, name):
     """Non-resident experts are skipped; the two partial sums merge exactly."""
-    _say("decode partial + merge")
-    L = GpuLayer("ragged_decode")
+    _say("decode partial + merge", name)
+    L = GpuLayer(name)
     T, E = 9, L.s["n_experts"]
     x = L.tokens(T)
     ids, w = _route_gpu(ops, L, x)
@@ -412,9 +413,11 @@ def _route_decode(ops, L, x, slot_of=None, ws=None):
 
 
 def _launches(L, T):
-    """Kernel launches of one decode call: x of every token of a launch must
-    fit the 120 KB LDS stage, and a launch takes at most 16 tokens."""
-    per = min(61440 // L.s["hidden"], 16)
+    """Kernel launches of one decode call: T split evenly into launches of at
+    most moe_decode_launch_tokens tokens (its values are pinned on the host
+    in test_abi_host)."""
+    from sparse_expert_execution_amd import ops as _ops
+    per = _ops.decode_launch_tokens(L.desc)
     return (T + per - 1) // per
 
 
@@ -444,7 +447,11 @@ def _check_ids(L, x, gi, gw, renorm=False):
                                           ("qwen_bf16_decode", 4, "nvfp4"),
                                           ("many_experts", 1, None),
                                           ("many_experts", 5, None),
-                                          ("many_experts", 16, None)])
+                                          ("many_experts", 16, None),
+                                          ("mfma_decode", 1, None),
+                                          ("mfma_decode", 3, None),
+                                          ("mfma_decode", 8, None),
+                                          ("mfma_decode", 11, None)])
 def test_route_decode(ops, name, T, wtype):
     """Router + experts + combine in one call (one persistent kernel for T <= 4)."""
     _say("route_decode", name, T, wtype)
@@ -474,7 +481,8 @@ def test_route_decode(ops, name, T, wtype):
 
 @pytest.mark.parametrize("name,T,wtype", [("tiny", 4, "bf16"), ("qwen_bf16_decode", 1, None),
                                           ("qwen_bf16_decode", 16, None),
-                                          ("ragged_decode", 9, None)])
+                                          ("ragged_decode", 9, None),
+                                          ("mfma_decode", 5, None)])
 def test_route_decode_renorm(ops, name, T, wtype):
     """Renormalised top-k weights in the one-kernel path: the rank and the
     wave-arg-max top-k, the one-wave and the workgroup expert list."""
