@@ -35,8 +35,8 @@ import os
 import sys
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-DECODE_SOURCES = ["decode_impl.hpp", "decode_launch.hpp", "decode.hip", "decode_bf16.hip",
-                  "decode_mxfp4.hip", "device.hpp", "kernels.hpp"]
+DECODE_SOURCES = ["decode_impl.hpp", "decode_mfma.hpp", "decode_launch.hpp", "decode.hip",
+                  "decode_bf16.hip", "decode_mxfp4.hip", "device.hpp", "kernels.hpp"]
 PREFILL_SOURCES = ["prefill.hip", "device.hpp", "kernels.hpp"]
 PROBE_BYTES = 256 << 20
 SIMDS = 256 * 4                     # MI355X: 256 compute units x 4 SIMDs
