@@ -46,7 +46,9 @@ def build(verbose=True):
     with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
         objs = list(ex.map(_compile, SOURCES))
     tmp = OUT + ".tmp"
-    cmd = [HIPCC, "-shared", "-fPIC", "--offload-arch=gfx950", "-o", tmp] + objs
+    # librocprofiler-sdk-roctx: the roctx ranges around the C-ABI calls
+    cmd = [HIPCC, "-shared", "-fPIC", "--offload-arch=gfx950", "-o", tmp] + objs + [
+        "-L/opt/rocm/lib", "-lrocprofiler-sdk-roctx"]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stderr)

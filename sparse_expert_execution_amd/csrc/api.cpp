@@ -109,6 +109,7 @@ size_t moe_workspace_bytes(const moe_desc* desc, int32_t T, int32_t mode) {
 
 int moe_route(const moe_desc* desc, const void* x, const void* w_router, int32_t T,
               int32_t* ids, float* w, void* ws, size_t ws_bytes, void* stream) {
+  moe::ApiRange range_("moe_route");
   int st = check_desc(desc);
   if (st) return st;
   if (T == 0) return MOE_OK;
@@ -216,6 +217,7 @@ int32_t moe_decode_launch_tokens(const moe_desc* desc) {
 int moe_decode(const moe_desc* desc, const void* x, int32_t T, const int32_t* ids, const float* w,
                const int32_t* slot_of_expert, const void* slot_pool, const void* shared_expert,
                float* y, void* ws, size_t ws_bytes, void* stream) {
+  moe::ApiRange range_("moe_decode");
   if (T == 0) return check_desc(desc);
   int st = check_ffn_args(desc, x, T, ids, w, slot_pool, shared_expert, y);
   if (st) return st;
@@ -227,6 +229,7 @@ int moe_route_decode(const moe_desc* desc, const void* x, const void* w_router, 
                      int32_t* ids, float* w, const int32_t* slot_of_expert,
                      const void* slot_pool, const void* shared_expert, float* y, void* ws,
                      size_t ws_bytes, void* stream) {
+  moe::ApiRange range_("moe_route_decode");
   if (T == 0) return check_desc(desc);
   int st = check_ffn_args(desc, x, T, ids, w, slot_pool, shared_expert, y);
   if (st) return st;
@@ -241,6 +244,7 @@ int moe_route_decode(const moe_desc* desc, const void* x, const void* w_router, 
 int moe_prefill(const moe_desc* desc, const void* x, int32_t T, const int32_t* ids, const float* w,
                 const int32_t* slot_of_expert, const void* slot_pool, const void* shared_expert,
                 float* y, void* ws, size_t ws_bytes, void* stream) {
+  moe::ApiRange range_("moe_prefill");
   if (T == 0) return check_desc(desc);
   int st = check_ffn_args(desc, x, T, ids, w, slot_pool, shared_expert, y);
   if (st) return st;
@@ -290,6 +294,7 @@ int moe_debug_prefill_layout(const moe_desc* desc, int32_t T, int64_t out[5]) {
 }
 
 int moe_merge_partials(const float* a, const float* b, float* y, size_t n, void* stream) {
+  moe::ApiRange range_("moe_merge_partials");
   if (n == 0) return MOE_OK;
   if (!a || !b || !y) return set_error(MOE_EINVAL, "null pointer");
   return hip_status(moe::launch_merge(a, b, y, n, as_stream(stream)), "moe_merge_partials");
@@ -297,6 +302,7 @@ int moe_merge_partials(const float* a, const float* b, float* y, size_t n, void*
 
 int moe_quantize_mxfp4(const float* src, int32_t rows, int32_t K, int64_t src_ld, uint8_t* codes,
                        uint8_t* scales, void* stream) {
+  moe::ApiRange range_("moe_quantize_mxfp4");
   if (rows == 0) return MOE_OK;
   if (!src || !codes || !scales) return set_error(MOE_EINVAL, "null pointer");
   if (rows < 0 || K <= 0 || K % 32 || src_ld < K || src_ld % 4)
@@ -310,6 +316,7 @@ int moe_quantize_mxfp4(const float* src, int32_t rows, int32_t K, int64_t src_ld
 
 int moe_pack_expert(const moe_desc* desc, const void* gate, const void* up, const void* down,
                     int32_t src_type, void* dst, void* stream) {
+  moe::ApiRange range_("moe_pack_expert");
   int st = check_desc(desc);
   if (st) return st;
   if (!gate || !up || !down || !dst) return set_error(MOE_EINVAL, "null pointer");

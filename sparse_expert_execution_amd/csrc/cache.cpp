@@ -136,6 +136,7 @@ const moe_planner* moe_cache_planner(const moe_cache* c) { return c ? c->planner
 
 int moe_cache_plan(moe_cache* c, int32_t layer, const int32_t* ids_host, const float* w_host,
                    int32_t n, int32_t q, moe_plan* plan) {
+  moe::ApiRange range_("moe_cache_plan");
   if (!c) return set_error(MOE_EINVAL, "null cache");
   return moe::planner_plan(c->planner, layer, ids_host, w_host, n, q, plan);
 }
@@ -147,6 +148,7 @@ int moe_cache_debug_fail_fills(moe_cache* c, int32_t n) {
 }
 
 int cache_fill(moe_cache* c, const moe_plan* plan, void* side_stream, void* compute_stream) {
+  moe::ApiRange range_("cache_fill");
   if (!c || !plan) return set_error(MOE_EINVAL, "null pointer");
   hipStream_t side = static_cast<hipStream_t>(side_stream);
   hipStream_t comp = static_cast<hipStream_t>(compute_stream);
@@ -211,6 +213,7 @@ int cache_fill(moe_cache* c, const moe_plan* plan, void* side_stream, void* comp
 }
 
 int moe_cache_resize(moe_cache* c, void* dev_slot_pool, int32_t n_slots, void* compute_stream) {
+  moe::ApiRange range_("moe_cache_resize");
   if (!c || !dev_slot_pool) return set_error(MOE_EINVAL, "null pointer");
   if (n_slots < 1) return set_error(MOE_EINVAL, "slot budget %d < 1", n_slots);
   uint8_t* np = static_cast<uint8_t*>(dev_slot_pool);
@@ -281,6 +284,7 @@ int moe_cache_resize(moe_cache* c, void* dev_slot_pool, int32_t n_slots, void* c
 }
 
 int moe_cache_release(moe_cache* c, const moe_plan* plan, void* compute_stream) {
+  moe::ApiRange range_("moe_cache_release");
   if (!c || !plan) return set_error(MOE_EINVAL, "null pointer");
   hipStream_t comp = static_cast<hipStream_t>(compute_stream);
   auto rec = [&](int s) -> int {

@@ -75,6 +75,7 @@ extern "C" int moe_route_decode_noalloc(const moe_desc* desc, const void* x,
                                         const int32_t* slot_of_expert, const void* slot_pool,
                                         const void* shared_expert, float* y,
                                         int32_t* wait_status, void* stream) {
+  moe::ApiRange range_("moe_route_decode_noalloc");
   if (T == 0) return moe_workspace_bytes(desc, 1, MOE_MODE_DECODE) ? MOE_OK : MOE_EINVAL;
   const size_t need = moe_workspace_bytes(desc, T, MOE_MODE_DECODE);
   if (need == 0) return MOE_EINVAL;   // bad descriptor or T: the text is set

@@ -102,6 +102,7 @@ void moe_layer_stream_destroy(moe_layer_stream* s) {
 
 int moe_layer_stream_acquire(moe_layer_stream* s, int32_t layer, void* copy_stream,
                              void* compute_stream, void** dev_layer) {
+  moe::ApiRange range_("moe_layer_stream_acquire");
   if (!s || !dev_layer) return set_error(MOE_EINVAL, "null pointer");
   if (layer < 0 || layer >= s->n_layers)
     return set_error(MOE_EINVAL, "layer %d out of range", layer);
@@ -129,6 +130,7 @@ int moe_layer_stream_acquire(moe_layer_stream* s, int32_t layer, void* copy_stre
 }
 
 int moe_layer_stream_release(moe_layer_stream* s, int32_t layer, void* compute_stream) {
+  moe::ApiRange range_("moe_layer_stream_release");
   if (!s) return set_error(MOE_EINVAL, "null stream object");
   if (layer < 0 || layer >= s->n_layers)
     return set_error(MOE_EINVAL, "layer %d out of range", layer);

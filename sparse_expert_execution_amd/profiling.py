@@ -261,6 +261,32 @@ def cmd_counters(args):
     print(text)
 
 
+def cmd_markers(args):
+    """Per-range summary of the roctx ranges around the library's C-ABI calls
+    from a rocprofv3 --marker-trace run (its marker_api_trace.csv)."""
+    per = {}
+    with open(args.csv) as f:
+        for r in csv.DictReader(f):
+            name = r.get("Function") or r.get("Message") or r.get("Name") or ""
+            try:
+                dt = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+            except (KeyError, ValueError):
+                continue
+            per.setdefault(name, []).append(dt)
+    lines = [f"# {args.name}", "", "roctx ranges around the C-ABI calls (host time of each call, "
+             "rocprofv3 --marker-trace):", "", f"    {args.command}", "",
+             "| range | calls | mean us | min us | max us |", "|---|---|---|---|---|"]
+    for name, v in sorted(per.items(), key=lambda kv: -len(kv[1])):
+        lines.append(f"| {name} | {len(v)} | {sum(v) / len(v):.2f} | {min(v):.2f} | {max(v):.2f} |")
+    if args.note:
+        lines += ["", args.note]
+    text = "\n".join(lines) + "\n"
+    os.makedirs(args.out_dir, exist_ok=True)
+    with open(os.path.join(args.out_dir, f"{args.name}.md"), "w") as f:
+        f.write(text)
+    print(text)
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -292,9 +318,18 @@ def main(argv=None):
     c.add_argument("--csv", nargs="+", required=True)
     c.add_argument("--match", default="")
     c.add_argument("--out", default=None)
+    mk = sub.add_parser("markers")
+    mk.add_argument("--csv", required=True)
+    mk.add_argument("--name", required=True)
+    mk.add_argument("--command", default="", help="the rocprofv3 command, for the record")
+    mk.add_argument("--note", default="")
+    mk.add_argument("--out-dir", default=os.path.join(ROOT, "profiles"))
     a = ap.parse_args(argv)
     if a.cmd == "counters":
         cmd_counters(a)
+        return
+    if a.cmd == "markers":
+        cmd_markers(a)
         return
     if a.cmd == "run":
         cmd_run(a)

@@ -453,7 +453,8 @@ def _check_ids(L, x, gi, gw, renorm=False):
                                           ("mfma_decode", 8, None),
                                           ("mfma_decode", 11, None)])
 def test_route_decode(ops, name, T, wtype):
-    """Router + experts + combine in one call (one persistent kernel for T <= 4)."""
+    """Router + experts + combine in one call (one persistent kernel per
+    launch of up to moe_decode_launch_tokens tokens)."""
     _say("route_decode", name, T, wtype)
     L = GpuLayer(name, wtype=wtype)
     x = L.tokens(T)
