@@ -1170,15 +1170,16 @@ __device__ __forceinline__ void flush_y(const DecArgs& a, WaveOut& o) {
 template <int WT>
 __device__ __forceinline__ float wdot_h(const uint4 q, uint32_t sc, const float4* h4) {
   if (WT == 1) {
-    const float4 h0 = h4[0], h1 = h4[1];
-    float s = bf16_lo(q.x) * h0.x;
-    s = fmaf(bf16_hi(q.x), h0.y, s);
-    s = fmaf(bf16_lo(q.y), h0.z, s);
-    s = fmaf(bf16_hi(q.y), h0.w, s);
-    s = fmaf(bf16_lo(q.z), h1.x, s);
-    s = fmaf(bf16_hi(q.z), h1.y, s);
-    s = fmaf(bf16_lo(q.w), h1.z, s);
-    return fmaf(bf16_hi(q.w), h1.w, s);
+    // h as BF16 hi parts (h4[0]) and lo parts (h4[1]): exact products, fp32 sums
+    const float4 hf = h4[0], lf = h4[1];
+    float s = dot2_bf16(q.x, __float_as_uint(hf.x), 0.f);
+    s = dot2_bf16(q.y, __float_as_uint(hf.y), s);
+    s = dot2_bf16(q.z, __float_as_uint(hf.z), s);
+    s = dot2_bf16(q.w, __float_as_uint(hf.w), s);
+    s = dot2_bf16(q.x, __float_as_uint(lf.x), s);
+    s = dot2_bf16(q.y, __float_as_uint(lf.y), s);
+    s = dot2_bf16(q.z, __float_as_uint(lf.z), s);
+    return dot2_bf16(q.w, __float_as_uint(lf.w), s);
   } else {
     // MXFP4: one sum times the e8m0 scale; NVFP4: the two 16-element halves
     // (words 0-1, 2-3) each times its E4M3 scale
@@ -1330,9 +1331,20 @@ __device__ __forceinline__ void stage_h(const DecArgs& a, DecLds& S, int c0, int
           }
         }
         const int v = c4 / (EPV / 4), cc = c4 - v * (EPV / 4);
-        S.d.hst[e * I4 + cc * V + v] =
-            make_float4(__uint_as_float((uint32_t)w[b][0]), __uint_as_float((uint32_t)w[b][1]),
-                        __uint_as_float((uint32_t)w[b][2]), __uint_as_float((uint32_t)w[b][3]));
+        const float h0 = __uint_as_float((uint32_t)w[b][0]), h1 = __uint_as_float((uint32_t)w[b][1]);
+        const float h2 = __uint_as_float((uint32_t)w[b][2]), h3 = __uint_as_float((uint32_t)w[b][3]);
+        if (WT == 1) {
+          // BF16 weights: the vector's 8 h values as BF16 hi parts (first
+          // float4) and lo parts (second), so a row takes two dot2 per pair
+          uint32_t hi0, lo0, hi1, lo1;
+          bf16_split2(h0, h1, hi0, lo0);
+          bf16_split2(h2, h3, hi1, lo1);
+          uint2* dst = reinterpret_cast<uint2*>(S.d.hst + e * I4 + v);
+          dst[cc] = make_uint2(hi0, hi1);
+          reinterpret_cast<uint2*>(S.d.hst + e * I4 + V + v)[cc] = make_uint2(lo0, lo1);
+        } else {
+          S.d.hst[e * I4 + cc * V + v] = make_float4(h0, h1, h2, h3);
+        }
       }
     }
   }

@@ -23,6 +23,16 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float acc) {
   return __builtin_amdgcn_fdot2_f32_bf16(as_v2bf(a), as_v2bf(b), acc, false);
 }
 
+// Two fp32 values as BF16 parts: hi = RNE(v), lo = RNE(v - hi) (the
+// difference is exact in fp32), packed low element first.  hi + lo is v to
+// within about 2^-17 of |v|.
+__device__ __forceinline__ void bf16_split2(float a, float b, uint32_t& hi, uint32_t& lo) {
+  const v2bf h = {(__bf16)a, (__bf16)b};
+  hi = __builtin_bit_cast(uint32_t, h);
+  const v2bf l = {(__bf16)(a - bf16_lo(hi)), (__bf16)(b - bf16_hi(hi))};
+  lo = __builtin_bit_cast(uint32_t, l);
+}
+
 // ---- e2m1 (MXFP4 element) decode ------------------------------------------
 // Two e2m1 codes held in byte SEL of `word` -> two bf16 values (exact: every
 // e2m1 value is a bf16), packed low element first.  Uses the gfx950 scaled
