@@ -202,6 +202,10 @@ __global__ __launch_bounds__(256) void sort_scatter_kernel(SortArgs a) {
   if (b < 0) return;
   int rank = 0;
   for (int q = 0; q < (int)threadIdx.x; ++q) rank += (sbin[q] == b);
+  // count and scatter read the same ids and slot table in stream order, so
+  // every position is in range and written once; the guard (and the range
+  // checks where the GEMMs read sorted_pair) keep a caller's concurrent
+  // change of those inputs from turning into stores or loads out of bounds
   const int pos = a.chunk_counts[(int64_t)blockIdx.x * nb + b] + rank;
   if ((unsigned)pos < (unsigned)a.n_pairs) a.sorted_pair[pos] = p;
 }
@@ -229,8 +233,10 @@ __device__ __forceinline__ const uint8_t* bin_base(const GemmArgs& a, int bin) {
   return a.pool + (int64_t)slot * a.expert_bytes;
 }
 
+// token of pair p (a pair id outside [0, T (k + 1)) reads token 0)
 __device__ __forceinline__ int pair_token(const GemmArgs& a, int p) {
   const int nr = a.T * a.k;
+  if ((unsigned)p >= (unsigned)(nr + a.T)) return 0;
   return p < nr ? p / a.k : p - nr;
 }
 
@@ -472,6 +478,7 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& a, const Tile& t,
         const int r = t.row0 + wm * 64 + ms * 16 + d_row(lane, i);
         if (r >= t.seg_end) continue;
         const int p = a.sorted_pair[r];
+        if ((unsigned)p >= (unsigned)(nr + a.T)) continue;
         int prow;
         if (p < nr) prow = (p / a.k) * (a.k + 1) + (p % a.k);
         else prow = (p - nr) * (a.k + 1) + a.k;

@@ -37,8 +37,10 @@ constexpr int kNvBN = 64;            // weight rows (output columns) of a tile
 constexpr int kNvKC = 128;           // K per chunk
 constexpr int kNvLdsRow = kNvKC * 2 + 16;   // bytes of one expanded weight row in LDS
 
+// token of pair p (a pair id outside [0, T (k + 1)) reads token 0)
 __device__ __forceinline__ int nv_pair_token(const NvPrefillArgs& a, int p) {
   const int nr = a.T * a.k;
+  if ((unsigned)p >= (unsigned)(nr + a.T)) return 0;
   return p < nr ? p / a.k : p - nr;
 }
 
@@ -213,6 +215,7 @@ __global__ __launch_bounds__(kNvThreads, 2) void nv_gemm_kernel(NvPrefillArgs a)
         const int r = row0 + 32 * wv + 16 * ms + 4 * fg + i;
         if (r >= seg_end) continue;
         const int p = a.sorted_pair[r];
+        if ((unsigned)p >= (unsigned)(nr + a.T)) continue;
         const int prow = p < nr ? (p / a.k) * (a.k + 1) + (p % a.k) : (p - nr) * (a.k + 1) + a.k;
         float* dst = a.partial + (int64_t)prow * a.H + col0 + fr;
 #pragma unroll
