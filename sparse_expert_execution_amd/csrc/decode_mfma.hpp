@@ -661,6 +661,42 @@ __device__ __forceinline__ void mf_down(const DecArgs& a, DecLds& S, uint8_t* U,
   stamp(timing, a, 12);
 }
 
+// Down work split by cost.  A row group of a unit with ne entries costs
+// about kDnA + kDnB * ne: its MFMA steps are the same for any ne (the B
+// columns hold the entries), but its h stage, its B fragment reads (distinct
+// columns instead of one broadcast column) and its y results grow with ne.
+// On the DeepSeek-shaped layer at four tokens the shared expert's groups
+// (ne = 4) took 1.31 times as long as single-entry ones; kDnA = 17, kDnB = 2
+// gives 25 / 19.  Group weights are linear in ne, so the cost ahead of unit
+// u is (kDnA u + kDnB unit_start[u]) (H / 8), and boundary b of the grid's
+// split is the group where the cost passes b / G of the total; adjacent
+// workgroups compute the same boundary, so the ranges tile the groups.
+// Boundaries are rounded to whole multiples of 8 groups: a batch of a
+// multiple of 8 groups gives each wave whole groups (mf_split), anything
+// else slices every group's K over the waves.  Against the even split of
+// row groups: DeepSeek-shaped layer, 4 tokens 104 -> 99 us, 8 tokens 213 ->
+// 192 us per launch.
+constexpr int kDnA = 17, kDnB = 2;
+
+__device__ __forceinline__ int mf_dn_bound(const DecArgs& a, const DecLds& S, int b, int G) {
+  const int HG = a.H / 8, nu = uni(S.p.n_units);
+  auto cost = [&](int u) -> int64_t {
+    return ((int64_t)kDnA * u + (int64_t)kDnB * uni(S.p.unit_start[u])) * HG;
+  };
+  const int64_t target = cost(nu) * b / G;
+  int lo = 0, hi = nu;                    // the last unit u with cost(u) <= target
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (cost(mid) <= target) lo = mid;
+    else hi = mid - 1;
+  }
+  if (lo >= nu) return nu * HG;
+  const int64_t wu = (int64_t)kDnA + (int64_t)kDnB * (uni(S.p.unit_start[lo + 1]) -
+                                                       uni(S.p.unit_start[lo]));
+  const int g = (int)(lo * HG + (target - cost(lo)) / wu);
+  return uni((g + 4) & ~7);
+}
+
 // ---- the kernel ---------------------------------------------------------------
 template <int M>
 __global__ __launch_bounds__(kT) void decode_mfma_kernel(DecArgs a) {
@@ -707,20 +743,23 @@ __global__ __launch_bounds__(kT) void decode_mfma_kernel(DecArgs a) {
   stamp(timing, a, 1);
 
   // 3. gate/up of every unit (the shared expert is the last one; in the
-  // first phase its row groups would not spread evenly over the grid)
+  // first phase its row groups would not spread evenly over the grid), in
+  // whole multiples of 8 groups per workgroup (I / 8 is a multiple of 8):
+  // each wave then takes whole groups, where any other count slices every
+  // group's K over the waves and meets the slices in LDS atomics.  On the
+  // DeepSeek-shaped layer this took 8 tokens from 192 to 160 us per launch
+  // (at 4 tokens no change, at 2 tokens 66.8 -> 68.4 us: shares of 8 or 16
+  // groups where the even split gave 13)
   {
     int64_t lo, hi;
-    split((int64_t)S.p.n_units * (a.I / 8), G, bid, lo, hi);
-    mf_gateup<false>(a, S, U, (int)lo, (int)hi);
+    split((int64_t)S.p.n_units * (a.I / 64), G, bid, lo, hi);
+    mf_gateup<false>(a, S, U, (int)lo * 8, (int)hi * 8);
   }
   stamp(timing, a, 7);
 
-  // 4. down of every unit (h polled per value, no grid-wide wait)
-  {
-    int64_t lo, hi;
-    split((int64_t)S.p.n_units * (a.H / 8), G, bid, lo, hi);
-    mf_down(a, S, U, (int)lo, (int)hi, timing);
-  }
+  // 4. down of every unit (h polled per value, no grid-wide wait), split
+  // by cost rather than by row groups
+  mf_down(a, S, U, mf_dn_bound(a, S, bid, G), mf_dn_bound(a, S, bid + 1, G), timing);
   stamp(timing, a, 3);
   finish_launch(a, gen);
 }
