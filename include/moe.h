@@ -151,12 +151,14 @@ int moe_route(const moe_desc* desc, const void* x, const void* w_router,
  * the pages' exact split); non-resident pairs are skipped.
  * One persistent kernel per launch of up to moe_decode_launch_tokens(desc)
  * tokens (a larger T is split evenly into launches in stream order).  The
- * gate/up rows of all
- * selected experts are split evenly over the grid, h is handed between
- * workgroups through the workspace tagged with the launch's generation, then
- * the down rows are split evenly and each row's gate-weighted result is
- * added into y with an fp32 atomic, so the summation order (and the last bits
- * of y) can differ between runs.
+ * gate/up rows of all selected experts are split evenly over the grid (on
+ * the matrix core in whole multiples of 8 groups of 8 rows), h is handed
+ * between workgroups through the workspace tagged with the launch's
+ * generation, then the down rows are split over the grid (evenly, or on the
+ * matrix core by cost: an expert's rows weigh more the more tokens chose
+ * it) and each row's gate-weighted result is added into y with an fp32
+ * atomic, so the summation order (and the last bits of y) can differ
+ * between runs.
  *   x              device [T][H] BF16;   1 <= T <= MOE_DECODE_MAX_T
  *   ids, w         device [T][k] (from moe_route or the caller)
  *   slot_of_expert device [E] int32: slot holding expert e, -1 = not

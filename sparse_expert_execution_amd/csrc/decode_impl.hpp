@@ -290,6 +290,30 @@ struct DecLds {
   };
 };
 
+// Boundary b of a split of the rows of units [0, nu) (R rows each) over G
+// parts by cost, where a row of unit u weighs A + B * (its entries): the cost
+// ahead of unit u is (A u + B unit_start[u]) R, and boundary b is the row
+// where the cost passes b / G of the total (a binary search over the units).
+// Adjacent parts compute the same boundary, so the ranges tile the rows;
+// with B = 0 it is the even split.
+__device__ __forceinline__ int cost_bound(const PlanLds& P, int nu, int R, int A, int B, int b,
+                                          int G) {
+  auto cost = [&](int u) -> int64_t {
+    return ((int64_t)A * u + (int64_t)B * uni(P.unit_start[u])) * R;
+  };
+  const int64_t target = cost(nu) * b / G;
+  int lo = 0, hi = nu;                    // the last unit u with cost(u) <= target
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (cost(mid) <= target) lo = mid;
+    else hi = mid - 1;
+  }
+  if (lo >= nu) return nu * R;
+  const int64_t wu =
+      (int64_t)A + (int64_t)B * (uni(P.unit_start[lo + 1]) - uni(P.unit_start[lo]));
+  return uni((int)(lo * R + (target - cost(lo)) / wu));
+}
+
 // ---------------------------------------------------------------------------
 // routing: z rows (router workgroups) and the per-workgroup expert list
 // ---------------------------------------------------------------------------

@@ -667,33 +667,16 @@ __device__ __forceinline__ void mf_down(const DecArgs& a, DecLds& S, uint8_t* U,
 // columns instead of one broadcast column) and its y results grow with ne.
 // On the DeepSeek-shaped layer at four tokens the shared expert's groups
 // (ne = 4) took 1.31 times as long as single-entry ones; kDnA = 17, kDnB = 2
-// gives 25 / 19.  Group weights are linear in ne, so the cost ahead of unit
-// u is (kDnA u + kDnB unit_start[u]) (H / 8), and boundary b of the grid's
-// split is the group where the cost passes b / G of the total; adjacent
-// workgroups compute the same boundary, so the ranges tile the groups.
-// Boundaries are rounded to whole multiples of 8 groups: a batch of a
-// multiple of 8 groups gives each wave whole groups (mf_split), anything
-// else slices every group's K over the waves.  Against the even split of
+// gives 25 / 19 (cost_bound over the units' H / 8 groups).  Boundaries
+// are rounded to whole multiples of 8 groups: a batch of a multiple of 8
+// groups gives each wave whole groups (mf_split), anything else slices
+// every group's K over the waves.  Against the even split of
 // row groups: DeepSeek-shaped layer, 4 tokens 104 -> 99 us, 8 tokens 213 ->
 // 192 us per launch.
 constexpr int kDnA = 17, kDnB = 2;
 
 __device__ __forceinline__ int mf_dn_bound(const DecArgs& a, const DecLds& S, int b, int G) {
-  const int HG = a.H / 8, nu = uni(S.p.n_units);
-  auto cost = [&](int u) -> int64_t {
-    return ((int64_t)kDnA * u + (int64_t)kDnB * uni(S.p.unit_start[u])) * HG;
-  };
-  const int64_t target = cost(nu) * b / G;
-  int lo = 0, hi = nu;                    // the last unit u with cost(u) <= target
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (cost(mid) <= target) lo = mid;
-    else hi = mid - 1;
-  }
-  if (lo >= nu) return nu * HG;
-  const int64_t wu = (int64_t)kDnA + (int64_t)kDnB * (uni(S.p.unit_start[lo + 1]) -
-                                                       uni(S.p.unit_start[lo]));
-  const int g = (int)(lo * HG + (target - cost(lo)) / wu);
+  const int g = cost_bound(S.p, uni(S.p.n_units), a.H / 8, kDnA, kDnB, b, G);
   return uni((g + 4) & ~7);
 }
 
