@@ -341,6 +341,112 @@ __device__ __forceinline__ MfGuPtr gu_ptr(const DecArgs& a, const DecLds& S, int
 // Every step issues the same loads (past the end they repeat the last), so
 // that the waits for a step's data are counted, not a drain of every load
 // in flight.
+// Gate/up with the A scales of a row group loaded once per pass of kMfRing
+// steps instead of one dword per step (the step's scale load cost as much as
+// its code load: a timing variant without scale loads was 7 us faster per
+// DeepSeek-shaped call at four tokens).  Lane l loads 16 scale bytes of row
+// l % 8 at byte 16 (l / 8) (NS loads per row: H / 32 bytes), so a row's
+// line comes whole; the dword a lane needs at step cp (2 cp + h of its row,
+// h = (l / 8) % 2) sits in lane row + 8 ((cp / 2) % 8), register 2 (cp % 2)
+// + h of load cp / 16, and ds_bpermute hands it over.  Needs each wave's
+// groups to run whole passes (nc a multiple of kMfRing): a pass then lies in
+// one group, and the loads of pass p + 1 go out at the first reload of pass
+// p into the set pass p - 1 used (two sets, passes unrolled in pairs).
+struct MfGuCode {
+  uint4 g, u;
+};
+
+template <int NS>
+struct MfGuScales {
+  uint4 g[NS], u[NS];
+};
+
+template <int NS>
+__device__ __forceinline__ void gu_batch_gs(const DecArgs& a, DecLds& S, uint8_t* U,
+                                            const MfSplit& m, int nsteps, float* acc) {
+  const int lane = threadIdx.x & 63, col = lane & 7;
+  const int T = a.T, SB = a.H / 32;
+  const uint8_t* xq = U + mf_xq(a);
+  const uint8_t* xsc = U + mf_xsc(a);
+  const ALane L = a_lane(a.H);
+  const BLane BL = b_lane(2, T);
+  uint32_t so[NS];                        // this lane's scale bytes (past the row: its start)
+#pragma unroll
+  for (int j = 0; j < NS; ++j) {
+    const int b = 128 * j + 16 * (lane >> 3);
+    so[j] = (uint32_t)((lane & 7) * SB + (b < SB ? b : 0));
+  }
+  const int hb = (lane >> 3) & 1;
+  MfCur lc{0, m.cl}, cc{0, m.cl};
+  MfGuPtr lp = gu_ptr(a, S, cur_group(m, lc));
+  auto load_scales = [&](MfGuScales<NS>& z) {
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+      z.g[j] = ldg16(lp.g.scale + so[j]);
+      z.u[j] = ldg16(lp.u.scale + so[j]);
+    }
+  };
+  auto load_codes = [&](MfGuCode& c) {
+    c.g = ldg16(lp.g.code + lc.c * 128 + L.code);
+    c.u = ldg16(lp.u.code + lc.c * 128 + L.code);
+    if (cur_next(m, lc)) lp = gu_ptr(a, S, cur_group(m, lc));
+  };
+  // the lane's scale byte at chunk pair cp from a set
+  auto pick = [&](const uint4 (&w)[NS], int cp) -> uint32_t {
+    const uint4 v = NS > 1 && cp >= 16 ? w[NS - 1] : w[0];
+    const int src = ((lane & 7) + 8 * ((cp >> 1) & 7)) * 4;
+    const uint32_t lo = (cp & 1) ? v.z : v.x, hi = (cp & 1) ? v.w : v.y;
+    const uint32_t d0 = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)lo);
+    const uint32_t d1 = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)hi);
+    return a_scale(hb ? d1 : d0);
+  };
+  MfGuScales<NS> z0, z1;
+  load_scales(z0);
+  MfGuCode ring[kMfRing];
+#pragma unroll
+  for (int i = 0; i < kMfRing; ++i) load_codes(ring[i]);
+  v4f ag = {0.f, 0.f, 0.f, 0.f}, au = {0.f, 0.f, 0.f, 0.f};
+  const bool mine = d_diag() && col < T;
+  // one pass: steps p0 .. p0 + kMfRing - 1 with scale set z, the next
+  // pass's set loaded into zn at its first reload
+  auto pass = [&](int p0, const MfGuScales<NS>& z, MfGuScales<NS>& zn) {
+#pragma unroll
+    for (int i = 0; i < kMfRing; ++i) {
+      if (p0 + i < nsteps) {
+        v8i b0, b1;
+        uint32_t s0b, s1b;
+        b_frag(xq, xsc, BL, cc.c, 0, 2, b0, s0b);
+        b_frag(xq, xsc, BL, cc.c, 1, 2, b1, s1b);
+        const uint32_t sg = pick(z.g, cc.c), su = pick(z.u, cc.c);
+        ag = mfma_fp4_fp8(ring[i].g, sg, b0, s0b, ag);
+        ag = mfma_fp4_fp8(ring[i].g, sg, b1, s1b, ag);
+        au = mfma_fp4_fp8(ring[i].u, su, b0, s0b, au);
+        au = mfma_fp4_fp8(ring[i].u, su, b1, s1b, au);
+        if (cc.c == m.cl + m.nc - 1) {      // the group's last step: add its sums
+          const int q = cur_group(m, cc);
+          if (mine) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int row = d_row8(r);
+              atomicAdd(acc + ((q * 2 + 0) * 8 + row) * T + col, ag[r]);
+              atomicAdd(acc + ((q * 2 + 1) * 8 + row) * T + col, au[r]);
+            }
+          }
+          ag = au = v4f{0.f, 0.f, 0.f, 0.f};
+        }
+        cur_next(m, cc);
+      }
+      if (i == 0) load_scales(zn);           // pass p0 + kMfRing: the cursor is there
+      load_codes(ring[i]);                   // step p0 + i + kMfRing
+    }
+  };
+  for (int s0 = 0; s0 < nsteps; s0 += 2 * kMfRing) {
+    pass(s0, z0, z1);
+    if (s0 + kMfRing >= nsteps) break;
+    pass(s0 + kMfRing, z1, z0);
+  }
+}
+
 __device__ __forceinline__ void gu_batch(const DecArgs& a, DecLds& S, uint8_t* U, int n,
                                          float* acc) {
   const int lane = threadIdx.x & 63, col = lane & 7;
@@ -350,6 +456,8 @@ __device__ __forceinline__ void gu_batch(const DecArgs& a, DecLds& S, uint8_t* U
   const MfSplit m = mf_split(n, C2);
   const int nsteps = m.cnt * m.nc;
   if (nsteps == 0) return;
+  if (m.nc % kMfRing == 0 && a.H <= 4096) return gu_batch_gs<1>(a, S, U, m, nsteps, acc);
+  if (m.nc % kMfRing == 0 && a.H <= 8192) return gu_batch_gs<2>(a, S, U, m, nsteps, acc);
   const ALane L = a_lane(a.H);
   const BLane BL = b_lane(2, T);
   MfCur lc{0, m.cl}, cc{0, m.cl};

@@ -398,6 +398,32 @@ def test_decode_dsv4_full_layer_sampled(ops, T, sample):
     assert olayer.row_rel_error(y[sample], ref) < TOL
 
 
+@pytest.mark.parametrize("name,sample", [("mfma_decode", None),
+                                         ("dsv4_mxfp4_decode", [0, 5, 7])])
+def test_decode_mfma_crowded_experts(ops, name, sample):
+    """Matrix-core decode of 8 tokens whose experts are shared unevenly (units
+    of 8, 5, 3 and 1 entries besides the shared expert's 8): the down row
+    groups are split over the grid by cost, which these entry counts skew."""
+    _say("decode crowded experts", name)
+    L = GpuLayer(name, layer=2 if name == "dsv4_mxfp4_decode" else 0)
+    T, E, k = 8, L.s["n_experts"], L.s["top_k"]
+    x = L.tokens(T)
+    hi = np.zeros((T, k), dtype=np.int32)
+    for t in range(T):
+        row = [0, 1, 2 if t < 5 else 3]              # 8, 8, 5 and 3 entries
+        row += [4 + (t * (k - 3) + j) % (E - 4) for j in range(k - 3)]
+        hi[t] = row[:k]
+    assert all(len(set(r)) == k for r in hi.tolist())
+    hw = np.random.default_rng(11).uniform(0.02, 0.3, size=(T, k)).astype(np.float32)
+    ids = torch.from_numpy(hi).cuda()
+    w = torch.from_numpy(hw).cuda()
+    y = _run_decode(ops, L, x, ids, w)
+    assert np.all(np.isfinite(y))
+    ref = _oracle_out(L, x, hi, hw.astype(np.float64), tokens=sample)
+    got = y if sample is None else y[sample]
+    assert olayer.row_rel_error(got, ref) < TOL
+
+
 def _route_decode(ops, L, x, slot_of=None, ws=None):
     T, k, H = x.shape[0], L.s["top_k"], L.s["hidden"]
     ids = torch.full((T, k), -7, dtype=torch.int32, device="cuda")
