@@ -626,6 +626,90 @@ __device__ __forceinline__ void stage_hq(const DecArgs& a, const DecLds& S, uint
   }
 }
 
+// Down with a row group's A scales once per pass of kMfRing steps, as in
+// gu_batch_gs (a ring of kMfRing steps, two scale sets; each wave's groups
+// run whole passes).
+template <int NS>
+__device__ __forceinline__ void dn_batch_gs(const DecArgs& a, DecLds& S, uint8_t* U,
+                                            const MfSplit& m, int nsteps, float* yacc) {
+  const int lane = threadIdx.x & 63, col = lane & 7;
+  const int T = a.T, SB = a.I / 32;
+  const ALane L = a_lane(a.I);
+  uint32_t so[NS];
+#pragma unroll
+  for (int j = 0; j < NS; ++j) {
+    const int b = 128 * j + 16 * (lane >> 3);
+    so[j] = (uint32_t)((lane & 7) * SB + (b < SB ? b : 0));
+  }
+  const int hb = (lane >> 3) & 1;
+  MfCur lc{0, m.cl}, cc{0, m.cl};
+  MPtr lp = dn_ptr(a, S, cur_group(m, lc));
+  auto load_scales = [&](uint4 (&z)[NS]) {
+#pragma unroll
+    for (int j = 0; j < NS; ++j) z[j] = ldg16(lp.scale + so[j]);
+  };
+  auto load_codes = [&](uint4& q) {
+    q = ldg16(lp.code + lc.c * 128 + L.code);
+    if (cur_next(m, lc)) lp = dn_ptr(a, S, cur_group(m, lc));
+  };
+  auto pick = [&](const uint4 (&w)[NS], int cp) -> uint32_t {
+    const uint4 v = NS > 1 && cp >= 16 ? w[NS - 1] : w[0];
+    const int src = ((lane & 7) + 8 * ((cp >> 1) & 7)) * 4;
+    const uint32_t lo = (cp & 1) ? v.z : v.x, hi = (cp & 1) ? v.w : v.y;
+    const uint32_t d0 = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)lo);
+    const uint32_t d1 = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)hi);
+    return a_scale(hb ? d1 : d0);
+  };
+  uint4 z0[NS], z1[NS];
+  load_scales(z0);
+  uint4 ring[kMfRing];
+#pragma unroll
+  for (int i = 0; i < kMfRing; ++i) load_codes(ring[i]);
+  auto enter = [&](int q, const uint8_t*& hq, const uint8_t*& hsc, BLane& BL, int& ne) {
+    ne = uni(S.p.unit_start[S.p.mf_unit[q] + 1] - S.p.unit_start[S.p.mf_unit[q]]);
+    hq = U + uni(S.p.mf_hoff[q]);
+    hsc = hq + mf_hsc(a, ne);
+    BL = b_lane(kHParts, ne);
+  };
+  const uint8_t *hq, *hsc;
+  BLane BL;
+  int ne;
+  enter(cur_group(m, cc), hq, hsc, BL, ne);
+  v4f acc = {0.f, 0.f, 0.f, 0.f};
+  const bool diag = d_diag();
+  auto pass = [&](int p0, const uint4 (&z)[NS], uint4 (&zn)[NS]) {
+#pragma unroll
+    for (int i = 0; i < kMfRing; ++i) {
+      if (p0 + i < nsteps) {
+        const uint32_t sa = pick(z, cc.c);
+#pragma unroll
+        for (int p = 0; p < kHParts; ++p) {
+          v8i b;
+          uint32_t sb;
+          b_frag(hq, hsc, BL, cc.c, p, kHParts, b, sb);
+          acc = mfma_fp4_fp8(ring[i], sa, b, sb, acc);
+        }
+        if (cc.c == m.cl + m.nc - 1) {
+          const int q = cur_group(m, cc);
+          if (diag && col < ne) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) atomicAdd(yacc + (q * 8 + d_row8(r)) * T + col, acc[r]);
+          }
+          acc = v4f{0.f, 0.f, 0.f, 0.f};
+        }
+        if (cur_next(m, cc)) enter(cur_group(m, cc), hq, hsc, BL, ne);
+      }
+      if (i == 0) load_scales(zn);
+      load_codes(ring[i]);
+    }
+  };
+  for (int s0 = 0; s0 < nsteps; s0 += 2 * kMfRing) {
+    pass(s0, z0, z1);
+    if (s0 + kMfRing >= nsteps) break;
+    pass(s0 + kMfRing, z1, z0);
+  }
+}
+
 // one batch of n down row groups (table S.p.mf_*: each group's unit, its h
 // stage, its entry count): sums into yacc[(j * 8 + row) * T + e]; loads as
 // in gu_batch
@@ -636,6 +720,8 @@ __device__ __forceinline__ void dn_batch(const DecArgs& a, DecLds& S, uint8_t* U
   const MfSplit m = mf_split(n, CI2);
   const int nsteps = m.cnt * m.nc;
   if (nsteps == 0) return;
+  if (m.nc % kMfRing == 0 && a.I <= 4096) return dn_batch_gs<1>(a, S, U, m, nsteps, yacc);
+  if (m.nc % kMfRing == 0 && a.I <= 8192) return dn_batch_gs<2>(a, S, U, m, nsteps, yacc);
   const ALane L = a_lane(a.I);
   MfCur lc{0, m.cl}, cc{0, m.cl};
   MPtr lp = dn_ptr(a, S, cur_group(m, lc));
