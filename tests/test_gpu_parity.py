@@ -537,6 +537,21 @@ def test_route_decode_dsv4_full_sampled(ops, T, sample):
     assert _counters_clear(ws, _launches(L, T))
 
 
+@pytest.mark.parametrize("T,sample", [(2, [0, 1]), (5, [0, 4])])
+def test_route_decode_glm_matrix_core_sampled(ops, T, sample):
+    """GLM-shaped layer (H 6144: two 16-byte scale loads per row in the
+    matrix-core gate/up) on the matrix-core decode, sampled tokens."""
+    _say("route_decode glm matrix core", T)
+    L = GpuLayer("glm_cache_decode", layer=0)
+    x = L.tokens(T)
+    ids, w, y, ws = _route_decode(ops, L, x)
+    gi, gw = ids.cpu().numpy(), w.cpu().numpy()
+    _check_ids(L, x, gi, gw)
+    ref = _oracle_out(L, x, gi, gw, tokens=sample)
+    assert olayer.row_rel_error(y.cpu().numpy()[sample], ref) < TOL
+    assert _counters_clear(ws, _launches(L, T))
+
+
 def test_route_decode_dsv4_nvfp4_sampled(ops):
     """DeepSeek-shaped layer with NVFP4 experts (and the shared expert), one
     token: router + experts + combine against the oracle."""
