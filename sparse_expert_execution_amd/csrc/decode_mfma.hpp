@@ -38,18 +38,20 @@
 // two blocks are discarded.  Up to 8 tokens per launch.
 //
 // Work: a layer's row groups (8 rows of a matrix of one expert) are split
-// evenly over the workgroups; a workgroup's groups are spread over its
-// eight waves by slices of K when there are fewer than eight of them (each
-// wave takes one slice of every group), and the per-slice sums meet in LDS
-// through LDS float atomics.  A wave keeps kMfRing steps of weight loads in
-// flight (one row group, two chunks, each).
+// over the workgroups, gate/up in whole multiples of 8 groups and down by
+// cost (a unit's groups weigh more the more entries it has); a workgroup's
+// groups go to its eight waves whole when it has a multiple of 8 of them,
+// else by slices of K (each wave takes one slice of every group) whose sums
+// meet in LDS through LDS float atomics.  A wave keeps kMfRing steps of
+// weight loads in flight (one row group, two chunks, each; down 2 kMfRing
+// where it loads a scale dword per step).
 #pragma once
 
 namespace moe {
 namespace dec {
 
 constexpr int kUnionBytes = (kXStage16 + kHStage4) * 16;
-constexpr int kMfRing = 8;     // steps of loads in flight per wave (gate/up; down 2x)
+constexpr int kMfRing = 8;     // steps of loads in flight per wave
 constexpr int kHParts = 3;     // e4m3 parts of h
 constexpr int kZsBytes = 1024; // logits of the rank top-k (T * E <= 128, rows padded to 4)
 
