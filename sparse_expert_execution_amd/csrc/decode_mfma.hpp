@@ -851,6 +851,9 @@ __device__ __forceinline__ void mf_down(const DecArgs& a, DecLds& S, uint8_t* U,
                           S.p.ent_gw[e0 + e] * yacc[q]);
         yacc[q] = 0.f;
       }
+      // every thread is done with this batch's table (mf_unit, mf_row) before
+      // the next batch's is written
+      lds_barrier();
     }
     s0 = s1;
   }
