@@ -548,14 +548,21 @@ def test_route_decode_glm_matrix_core_sampled(ops, T, sample):
     gi, gw = ids.cpu().numpy(), w.cpu().numpy()
     _check_ids(L, x, gi, gw)
     ref = _oracle_out(L, x, gi, gw, tokens=sample)
-    got = y.cpu().numpy()[sample]
-    err = olayer.row_rel_error(got, ref)
-    if err >= TOL:
-        bad = np.argwhere(np.abs(got - ref) > TOL * np.abs(ref).max(axis=1, keepdims=True))
-        _say("glm mismatch: ids", gi.tolist(), "bad (token, column) count", len(bad),
-             "first", bad[:24].tolist())
-    assert err < TOL
-    assert _counters_clear(ws, _launches(L, T))
+    # repeated calls: the down phase runs two batches per pass here, whose
+    # table hand-over between batches once let y results land on wrong rows
+    # in about one call in sixty
+    for rep in range(20):
+        if rep:
+            ids, w, y, ws = _route_decode(ops, L, x)
+            assert np.array_equal(ids.cpu().numpy(), gi)
+        got = y.cpu().numpy()[sample]
+        err = olayer.row_rel_error(got, ref)
+        if err >= TOL:
+            bad = np.argwhere(np.abs(got - ref) > TOL * np.abs(ref).max(axis=1, keepdims=True))
+            _say("glm mismatch: call", rep, "bad (token, column) count", len(bad),
+                 "first", bad[:24].tolist())
+        assert err < TOL
+        assert _counters_clear(ws, _launches(L, T))
 
 
 def test_route_decode_dsv4_nvfp4_sampled(ops):
